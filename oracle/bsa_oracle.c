@@ -1,0 +1,333 @@
+/*
+ * bsa_oracle.c -- plain, slow CPU oracle for block-sparse attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY (see bsa_oracle.h): used by the tests, the smoke
+ * check and the CPU-baseline leg of the benchmark; never by the product path.
+ *
+ * Every step is the plain definition written out in double precision:
+ * decode the selected key set of a work unit, list its attended keys in
+ * ascending order, then for each query row take the dot products, the
+ * base-2 softmax over the attended keys (two passes: max, then weights) and
+ * the weighted sum of values.  No blocking, fusion or online rescaling.
+ * OpenMP only spreads independent work units over cores.
+ */
+#include "bsa_oracle.h"
+
+#include <float.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- element decoders ----------------------------------------------- */
+
+/* bf16 is the upper half of an IEEE binary32: the value is exact. */
+double bsa_oracle_bf16_value(uint16_t bits) {
+  uint32_t w = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+/* OCP 8-bit floating point, E4M3 "fn" encoding: 1 sign bit, 4 exponent bits
+ * (bias 7), 3 mantissa bits; exponent field 0 is subnormal
+ * (2^-6 * m/8); no infinities; S.1111.111 is NaN; largest finite 448.
+ * The K/V quantisation recipe (scale = amax/448) fixes this encoding. */
+double bsa_oracle_fp8e4m3_value(uint8_t byte) {
+  int sign = (byte >> 7) & 1;
+  int e = (byte >> 3) & 0xF;
+  int m = byte & 0x7;
+  double mag;
+  if (e == 0xF && m == 0x7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* ---- selected set of one work unit ----------------------------------- */
+
+static int32_t clamp_i32(int32_t x, int32_t lo, int32_t hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+/* LUT form: sel[kb] = 1 for every idx[row, j], j < clamp(num,0,max_kv),
+ * with 0 <= idx < NK.  Entries at j >= count are never read; order and
+ * repetitions do not matter (a set). */
+static void select_lut(const int32_t* q2k_idx, const int32_t* q2k_num,
+                       int32_t max_kv, int64_t row, int32_t NK,
+                       unsigned char* sel) {
+  int32_t n = clamp_i32(q2k_num[row], 0, max_kv);
+  memset(sel, 0, (size_t)NK);
+  for (int32_t j = 0; j < n; ++j) {
+    int32_t kb = q2k_idx[row * (int64_t)max_kv + j];
+    if (kb >= 0 && kb < NK) sel[kb] = 1;
+  }
+}
+
+/* Bitmap form: nonzero byte = attend. */
+static void select_bitmap(const int8_t* mask, int64_t row, int32_t NK,
+                          unsigned char* sel) {
+  for (int32_t kb = 0; kb < NK; ++kb)
+    sel[kb] = mask[row * (int64_t)NK + kb] != 0;
+}
+
+/* Number of valid keys of key block kb. */
+static int32_t block_valid(const int32_t* vbs, int32_t kb, int32_t block) {
+  return vbs ? clamp_i32(vbs[kb], 0, block) : block;
+}
+
+/* ---- attention over the attended set of one unit --------------------- */
+
+typedef struct {
+  const uint16_t* q;
+  const void* k;
+  const void* v;
+  int kv_dtype;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* vbs;
+  double sm_scale;
+  int32_t H, S, D, block;
+} attn_args;
+
+static double kv_value(const attn_args* a, const void* base, const float* scale,
+                       int64_t elem, int64_t scale_idx) {
+  if (a->kv_dtype == ORACLE_KV_BF16)
+    return bsa_oracle_bf16_value(((const uint16_t*)base)[elem]);
+  return bsa_oracle_fp8e4m3_value(((const uint8_t*)base)[elem]) *
+         (double)scale[scale_idx];
+}
+
+/* Computes the `block` output rows of unit (b, h, qb) given its selected set.
+ * keys and t are scratch arrays of length S, qd of length D. */
+static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
+                        const unsigned char* sel, int64_t* keys, double* t,
+                        double* qd, double* out, double* lse) {
+  const int32_t D = a->D, S = a->S, block = a->block, NK = S / block;
+  const int64_t head = (int64_t)b * a->H + h; /* (b, h) plane index */
+  const int64_t plane = head * (int64_t)S * D;
+  const double c = a->sm_scale / log(2.0); /* sm_scale * log2(e) */
+
+  /* attended keys, ascending */
+  int64_t n_att = 0;
+  for (int32_t kb = 0; kb < NK; ++kb) {
+    if (!sel[kb]) continue;
+    int32_t nv = block_valid(a->vbs, kb, block);
+    for (int32_t tt = 0; tt < nv; ++tt) keys[n_att++] = (int64_t)kb * block + tt;
+  }
+
+  for (int32_t r = 0; r < block; ++r) {
+    double* o = out + (int64_t)r * D;
+    const int64_t qrow = plane + ((int64_t)qb * block + r) * D;
+    if (n_att == 0) {
+      for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+      lse[r] = -(double)FLT_MAX;
+      continue;
+    }
+    for (int32_t d = 0; d < D; ++d) qd[d] = bsa_oracle_bf16_value(a->q[qrow + d]);
+    /* pass 1: scaled scores and their maximum */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n_att; ++j) {
+      const int64_t key = keys[j];
+      const int64_t srow = head * (S / block) + key / block;
+      double s = 0.0;
+      for (int32_t d = 0; d < D; ++d)
+        s += qd[d] * kv_value(a, a->k, a->k_scale, plane + key * D + d, srow);
+      t[j] = s * c;
+      if (t[j] > m) m = t[j];
+    }
+    /* pass 2: weights, their sum, and the weighted sum of values */
+    double l = 0.0;
+    for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+    for (int64_t j = 0; j < n_att; ++j) {
+      const int64_t key = keys[j];
+      const int64_t srow = head * (S / block) + key / block;
+      const double w = exp2(t[j] - m);
+      l += w;
+      for (int32_t d = 0; d < D; ++d)
+        o[d] += w * kv_value(a, a->v, a->v_scale, plane + key * D + d, srow);
+    }
+    for (int32_t d = 0; d < D; ++d) o[d] /= l;
+    lse[r] = m + log2(l);
+  }
+}
+
+/* ---- argument checks shared by the entry points ---------------------- */
+
+static int check_dims(int32_t B, int32_t H, int32_t S, int32_t D,
+                      int32_t block) {
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || block <= 0) return 1;
+  if (S % block != 0) return 1;
+  return 0;
+}
+
+static int check_units(const int64_t* units, int64_t n_units, int64_t total) {
+  if (!units) return n_units == total ? 0 : 1;
+  for (int64_t i = 0; i < n_units; ++i)
+    if (units[i] < 0 || units[i] >= total) return 1;
+  return 0;
+}
+
+enum { FORM_LUT = 0, FORM_BITMAP = 1 };
+
+typedef struct {
+  int form;
+  const int32_t* q2k_idx;
+  const int32_t* q2k_num;
+  int32_t max_kv;
+  int64_t sb, sh; /* metadata row strides (in rows) */
+  const int8_t* mask;
+} sel_args;
+
+static void unit_select(const sel_args* s, int32_t b, int32_t h, int32_t qb,
+                        int32_t NK, unsigned char* sel) {
+  const int64_t row = (int64_t)b * s->sb + (int64_t)h * s->sh + qb;
+  if (s->form == FORM_LUT)
+    select_lut(s->q2k_idx, s->q2k_num, s->max_kv, row, NK, sel);
+  else
+    select_bitmap(s->mask, row, NK, sel);
+}
+
+static int run_fwd(const attn_args* a, const sel_args* s, int32_t B,
+                   const int64_t* units, int64_t n_units, double* out,
+                   double* lse) {
+  const int32_t NQ = a->S / a->block, NK = NQ;
+  int failed = 0;
+#pragma omp parallel
+  {
+    unsigned char* sel = (unsigned char*)malloc((size_t)NK);
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)a->S);
+    double* t = (double*)malloc(sizeof(double) * (size_t)a->S);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)a->D);
+    const int ok = sel && keys && t && qd;
+    if (!ok) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_units; ++i) {
+      if (!ok) continue;
+      const int64_t u = units ? units[i] : i;
+      const int32_t qb = (int32_t)(u % NQ);
+      const int32_t h = (int32_t)((u / NQ) % a->H);
+      const int32_t b = (int32_t)(u / ((int64_t)NQ * a->H));
+      unit_select(s, b, h, qb, NK, sel);
+      attend_unit(a, b, h, qb, sel, keys, t, qd,
+                  out + i * (int64_t)a->block * a->D,
+                  lse + i * (int64_t)a->block);
+    }
+    free(sel);
+    free(keys);
+    free(t);
+    free(qd);
+  }
+  (void)B;
+  return failed ? 3 : 0;
+}
+
+/* ---- entry points ---------------------------------------------------- */
+
+int bsa_oracle_fwd_lut(const uint16_t* q, const void* k, const void* v,
+                       int kv_dtype, const float* k_scale, const float* v_scale,
+                       const int32_t* q2k_idx, const int32_t* q2k_num,
+                       int32_t max_kv, int64_t meta_stride_b,
+                       int64_t meta_stride_h, const int32_t* vbs,
+                       double sm_scale, int32_t B, int32_t H, int32_t S,
+                       int32_t D, int32_t block, const int64_t* units,
+                       int64_t n_units, double* out, double* lse) {
+  if (!q || !k || !v || !q2k_idx || !q2k_num || !out || !lse) return 1;
+  if (check_dims(B, H, S, D, block) || max_kv < 1) return 1;
+  if (kv_dtype != ORACLE_KV_BF16 && kv_dtype != ORACLE_KV_FP8E4M3) return 1;
+  if (kv_dtype == ORACLE_KV_FP8E4M3 && (!k_scale || !v_scale)) return 1;
+  if (check_units(units, n_units, (int64_t)B * H * (S / block))) return 1;
+  attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, vbs, sm_scale, H, S, D,
+                 block};
+  sel_args s = {FORM_LUT, q2k_idx, q2k_num, max_kv, meta_stride_b,
+                meta_stride_h, NULL};
+  return run_fwd(&a, &s, B, units, n_units, out, lse);
+}
+
+int bsa_oracle_fwd_bitmap(const uint16_t* q, const void* k, const void* v,
+                          int kv_dtype, const float* k_scale,
+                          const float* v_scale, const int8_t* mask,
+                          int64_t mask_stride_b, int64_t mask_stride_h,
+                          const int32_t* vbs, double sm_scale, int32_t B,
+                          int32_t H, int32_t S, int32_t D, int32_t block,
+                          const int64_t* units, int64_t n_units, double* out,
+                          double* lse) {
+  if (!q || !k || !v || !mask || !out || !lse) return 1;
+  if (check_dims(B, H, S, D, block)) return 1;
+  if (kv_dtype != ORACLE_KV_BF16 && kv_dtype != ORACLE_KV_FP8E4M3) return 1;
+  if (kv_dtype == ORACLE_KV_FP8E4M3 && (!k_scale || !v_scale)) return 1;
+  if (check_units(units, n_units, (int64_t)B * H * (S / block))) return 1;
+  attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, vbs, sm_scale, H, S, D,
+                 block};
+  sel_args s = {FORM_BITMAP, NULL, NULL, 0, mask_stride_b, mask_stride_h,
+                mask};
+  return run_fwd(&a, &s, B, units, n_units, out, lse);
+}
+
+int bsa_oracle_key_counts(int form, const int32_t* q2k_idx,
+                          const int32_t* q2k_num, int32_t max_kv,
+                          int64_t meta_stride_b, int64_t meta_stride_h,
+                          const int8_t* mask, int64_t mask_stride_b,
+                          int64_t mask_stride_h, const int32_t* vbs, int32_t B,
+                          int32_t H, int32_t S, int32_t block,
+                          const int64_t* units, int64_t n_units,
+                          int32_t* counts) {
+  if (!counts || check_dims(B, H, S, 1, block)) return 1;
+  if (form == FORM_LUT && (!q2k_idx || !q2k_num || max_kv < 1)) return 1;
+  if (form == FORM_BITMAP && !mask) return 1;
+  if (form != FORM_LUT && form != FORM_BITMAP) return 1;
+  const int32_t NQ = S / block, NK = NQ;
+  if (check_units(units, n_units, (int64_t)B * H * NQ)) return 1;
+  sel_args s;
+  if (form == FORM_LUT) {
+    sel_args t = {FORM_LUT, q2k_idx, q2k_num, max_kv, meta_stride_b,
+                  meta_stride_h, NULL};
+    s = t;
+  } else {
+    sel_args t = {FORM_BITMAP, NULL, NULL, 0, mask_stride_b, mask_stride_h,
+                  mask};
+    s = t;
+  }
+  unsigned char* sel = (unsigned char*)malloc((size_t)NK);
+  if (!sel) return 3;
+  for (int64_t i = 0; i < n_units; ++i) {
+    const int64_t u = units ? units[i] : i;
+    const int32_t qb = (int32_t)(u % NQ);
+    const int32_t h = (int32_t)((u / NQ) % H);
+    const int32_t b = (int32_t)(u / ((int64_t)NQ * H));
+    unit_select(&s, b, h, qb, NK, sel);
+    for (int32_t kb = 0; kb < NK; ++kb)
+      counts[i * (int64_t)NK + kb] = sel[kb] ? block_valid(vbs, kb, block) : 0;
+  }
+  free(sel);
+  return 0;
+}
+
+int bsa_oracle_mask_to_lut(const int8_t* mask, int64_t rows, int32_t NK,
+                           int32_t* idx, int32_t* num) {
+  if (!mask || !idx || !num || rows < 0 || NK <= 0) return 1;
+  for (int64_t r = 0; r < rows; ++r) {
+    int32_t n = 0;
+    for (int32_t kb = 0; kb < NK; ++kb)
+      if (mask[r * (int64_t)NK + kb] != 0) idx[r * (int64_t)NK + n++] = kb;
+    for (int32_t j = n; j < NK; ++j) idx[r * (int64_t)NK + j] = -1;
+    num[r] = n;
+  }
+  return 0;
+}
+
+int bsa_oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

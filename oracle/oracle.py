@@ -1,0 +1,221 @@
+"""ctypes wrapper around the C oracle (``libbsa_oracle.so``).
+
+TEST INFRASTRUCTURE ONLY: used by ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py``.  Inputs are CPU torch tensors; outputs
+are float64 numpy arrays.  Work units are numbered ``u = (b*H + h)*NQ + qb``;
+with ``units=None`` every unit is computed and the outputs have the shapes
+``[B, H, S, D]`` and ``[B, H, S]``, otherwise ``[n, block, D]`` and
+``[n, block]`` for the n requested units.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+KV_BF16 = 0
+KV_FP8E4M3 = 1
+# Finite LSE sentinel of a query row that attends to no key: the lowest finite
+# binary32 value (a stand-in for log(0) that merges with weight 0).
+LSE_EMPTY = float(np.finfo(np.float32).min)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libbsa_oracle.so")
+
+
+def build() -> None:
+    """Compile the oracle with gcc (``oracle/build.sh``)."""
+    subprocess.run(["sh", os.path.join(_HERE, "build.sh")], check=True)
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(lib_path()):
+            build()
+        lib = ctypes.CDLL(lib_path())
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.bsa_oracle_bf16_value.restype = f64
+        lib.bsa_oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        lib.bsa_oracle_fp8e4m3_value.restype = f64
+        lib.bsa_oracle_fp8e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.bsa_oracle_fwd_lut.restype = ctypes.c_int
+        lib.bsa_oracle_fwd_lut.argtypes = [
+            P, P, P, ctypes.c_int, P, P, P, P, i32, i64, i64, P, f64,
+            i32, i32, i32, i32, i32, P, i64, P, P]
+        lib.bsa_oracle_fwd_bitmap.restype = ctypes.c_int
+        lib.bsa_oracle_fwd_bitmap.argtypes = [
+            P, P, P, ctypes.c_int, P, P, P, i64, i64, P, f64,
+            i32, i32, i32, i32, i32, P, i64, P, P]
+        lib.bsa_oracle_key_counts.restype = ctypes.c_int
+        lib.bsa_oracle_key_counts.argtypes = [
+            ctypes.c_int, P, P, i32, i64, i64, P, i64, i64, P,
+            i32, i32, i32, i32, P, i64, P]
+        lib.bsa_oracle_mask_to_lut.restype = ctypes.c_int
+        lib.bsa_oracle_mask_to_lut.argtypes = [P, i64, i32, P, P]
+        lib.bsa_oracle_num_threads.restype = ctypes.c_int
+        lib.bsa_oracle_num_threads.argtypes = []
+        _LIB = lib
+    return _LIB
+
+
+def num_threads() -> int:
+    return int(_lib().bsa_oracle_num_threads())
+
+
+def bf16_value(bits: int) -> float:
+    return float(_lib().bsa_oracle_bf16_value(int(bits) & 0xFFFF))
+
+
+def fp8e4m3_value(byte: int) -> float:
+    return float(_lib().bsa_oracle_fp8e4m3_value(int(byte) & 0xFF))
+
+
+def _cpu(t: torch.Tensor) -> torch.Tensor:
+    assert t.device.type == "cpu", "oracle inputs must be CPU tensors"
+    return t.contiguous()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _kv_bits(t: torch.Tensor):
+    t = _cpu(t)
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16), KV_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8), KV_FP8E4M3
+    raise TypeError(f"unsupported K/V dtype {t.dtype}")
+
+
+def _units_arg(units, total):
+    if units is None:
+        return None, total
+    u = torch.as_tensor(units, dtype=torch.int64).contiguous()
+    return u, int(u.numel())
+
+
+def _outputs(units, n, B, H, S, D, block):
+    if units is None:
+        return np.empty((B, H, S, D)), np.empty((B, H, S))
+    return np.empty((n, block, D)), np.empty((n, block))
+
+
+def _common(q, k, v, k_scale, v_scale):
+    q = _cpu(q)
+    assert q.dtype == torch.bfloat16 and q.dim() == 4
+    kb, kdt = _kv_bits(k)
+    vb, vdt = _kv_bits(v)
+    assert kdt == vdt, "K and V must share a dtype"
+    if kdt == KV_FP8E4M3:
+        k_scale = _cpu(k_scale.to(torch.float32))
+        v_scale = _cpu(v_scale.to(torch.float32))
+    else:
+        k_scale = v_scale = None
+    return q.view(torch.int16), kb, vb, kdt, k_scale, v_scale
+
+
+def fwd_lut(q, k, v, q2k_idx, q2k_num, vbs=None, *, block, sm_scale=None,
+            k_scale=None, v_scale=None, meta_strides=None, units=None):
+    """Oracle forward, LUT form.  ``q2k_idx`` is ``[..., max_kv]`` int32 and
+    ``q2k_num`` the matching per-row counts; ``meta_strides=(sb, sh)`` gives
+    the row of (b, h, qb) as ``b*sb + h*sh + qb`` (default: one row per
+    (b, h, qb), i.e. ``(H*NQ, NQ)``)."""
+    B, H, S, D = q.shape
+    NQ = S // block
+    qb_, kb_, vb_, kdt, ks, vs = _common(q, k, v, k_scale, v_scale)
+    idx = _cpu(q2k_idx.to(torch.int32))
+    num = _cpu(q2k_num.to(torch.int32))
+    max_kv = int(idx.shape[-1])
+    sb, sh = meta_strides if meta_strides is not None else (H * NQ, NQ)
+    vbs_t = None if vbs is None else _cpu(vbs.to(torch.int32))
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    u, n = _units_arg(units, B * H * NQ)
+    out, lse = _outputs(units, n, B, H, S, D, block)
+    rc = _lib().bsa_oracle_fwd_lut(
+        _ptr(qb_), _ptr(kb_), _ptr(vb_), kdt, _ptr(ks), _ptr(vs),
+        _ptr(idx), _ptr(num), max_kv, sb, sh, _ptr(vbs_t), float(sm_scale),
+        B, H, S, D, block, _ptr(u), n,
+        out.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError(f"bsa_oracle_fwd_lut failed (rc={rc})")
+    return out, lse
+
+
+def fwd_bitmap(q, k, v, mask, vbs=None, *, block, sm_scale=None,
+               k_scale=None, v_scale=None, mask_strides=None, units=None):
+    """Oracle forward, bitmap form.  ``mask`` is i8 rows of NK bytes;
+    ``mask_strides=(sb, sh)`` as for the LUT (``(0, 0)`` = one shared
+    ``[NQ, NK]`` mask)."""
+    B, H, S, D = q.shape
+    NQ = S // block
+    qb_, kb_, vb_, kdt, ks, vs = _common(q, k, v, k_scale, v_scale)
+    m = _cpu(mask.to(torch.int8))
+    sb, sh = mask_strides if mask_strides is not None else (H * NQ, NQ)
+    vbs_t = None if vbs is None else _cpu(vbs.to(torch.int32))
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    u, n = _units_arg(units, B * H * NQ)
+    out, lse = _outputs(units, n, B, H, S, D, block)
+    rc = _lib().bsa_oracle_fwd_bitmap(
+        _ptr(qb_), _ptr(kb_), _ptr(vb_), kdt, _ptr(ks), _ptr(vs),
+        _ptr(m), sb, sh, _ptr(vbs_t), float(sm_scale),
+        B, H, S, D, block, _ptr(u), n,
+        out.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError(f"bsa_oracle_fwd_bitmap failed (rc={rc})")
+    return out, lse
+
+
+def key_counts(*, B, H, S, block, q2k_idx=None, q2k_num=None, mask=None,
+               vbs=None, meta_strides=None, mask_strides=None, units=None):
+    """Integer decode: ``[n_units, NK]`` int32 attended-key counts per key
+    block (LUT form if ``q2k_idx`` is given, else bitmap form)."""
+    NQ = S // block
+    vbs_t = None if vbs is None else _cpu(vbs.to(torch.int32))
+    u, n = _units_arg(units, B * H * NQ)
+    counts = np.empty((n, NQ), dtype=np.int32)
+    lib = _lib()
+    if q2k_idx is not None:
+        idx = _cpu(q2k_idx.to(torch.int32))
+        num = _cpu(q2k_num.to(torch.int32))
+        sb, sh = meta_strides if meta_strides is not None else (H * NQ, NQ)
+        rc = lib.bsa_oracle_key_counts(
+            0, _ptr(idx), _ptr(num), int(idx.shape[-1]), sb, sh, None, 0, 0,
+            _ptr(vbs_t), B, H, S, block, _ptr(u), n,
+            counts.ctypes.data_as(ctypes.c_void_p))
+    else:
+        m = _cpu(mask.to(torch.int8))
+        sb, sh = mask_strides if mask_strides is not None else (H * NQ, NQ)
+        rc = lib.bsa_oracle_key_counts(
+            1, None, None, 0, 0, 0, _ptr(m), sb, sh,
+            _ptr(vbs_t), B, H, S, block, _ptr(u), n,
+            counts.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError(f"bsa_oracle_key_counts failed (rc={rc})")
+    return counts
+
+
+def mask_to_lut(mask):
+    """Compaction of an i8 ``[..., NK]`` bitmap into ``(idx [..., NK],
+    num [...])`` with ascending indices and -1 padding."""
+    m = _cpu(mask.to(torch.int8))
+    NK = int(m.shape[-1])
+    rows = m.numel() // NK
+    idx = torch.empty(m.shape, dtype=torch.int32)
+    num = torch.empty(m.shape[:-1], dtype=torch.int32)
+    rc = _lib().bsa_oracle_mask_to_lut(_ptr(m), rows, NK, _ptr(idx), _ptr(num))
+    if rc != 0:
+        raise ValueError(f"bsa_oracle_mask_to_lut failed (rc={rc})")
+    return idx, num

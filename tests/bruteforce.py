@@ -1,0 +1,89 @@
+"""Independent dense float64 brute force for tiny inputs (test helper).
+
+Builds the full [S, S] boolean attend mask key by key (key c of query row r
+is attended iff c's block is in r's selected set and c % block < vbs), then
+takes an ordinary natural-exp masked softmax with numpy.  It shares nothing
+with the C oracle: other language, other formulation (dense mask, natural
+exponent, library logsumexp).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+from scipy.special import logsumexp
+
+LSE_EMPTY = float(np.finfo(np.float32).min)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.to(torch.float64).numpy()
+
+
+def selected_sets(w) -> list:
+    """Python sets of selected key blocks, indexed by unit u=(b*H+h)*NQ+qb."""
+    NQ = w.NQ
+    out = []
+    for b in range(w.B):
+        for h in range(w.H):
+            for qb in range(NQ):
+                if w.form == "lut":
+                    sb, sh = w.meta_strides
+                    row = b * sb + h * sh + qb
+                    n = int(w.q2k_num[row])
+                    n = max(0, min(n, w.q2k_idx.shape[-1]))
+                    s = {int(x) for x in w.q2k_idx[row, :n].tolist()
+                         if 0 <= int(x) < NQ}
+                else:
+                    sb, sh = w.mask_strides
+                    row = b * sb + h * sh + qb
+                    s = {kb for kb in range(NQ) if int(w.mask[row, kb]) != 0}
+                out.append(s)
+    return out
+
+
+def dense_mask(w) -> np.ndarray:
+    """[B, H, S, S] bool attend mask."""
+    S, blk, NQ = w.S, w.block, w.NQ
+    vbs = [blk] * NQ if w.vbs is None else [
+        max(0, min(blk, int(x))) for x in w.vbs.tolist()]
+    sets = selected_sets(w)
+    m = np.zeros((w.B, w.H, S, S), dtype=bool)
+    for u, sel in enumerate(sets):
+        qb = u % NQ
+        h = (u // NQ) % w.H
+        b = u // (NQ * w.H)
+        for c in range(S):
+            if c // blk in sel and c % blk < vbs[c // blk]:
+                m[b, h, qb * blk:(qb + 1) * blk, c] = True
+    return m
+
+
+def kv_f64(w):
+    """Decoded K and V as float64 [B,H,S,D] (fp8: code value x block scale,
+    decoded by torch's float8_e4m3fn)."""
+    if w.kv_fp8:
+        k = to_f64(w.k.to(torch.float32))
+        v = to_f64(w.v.to(torch.float32))
+        ks = np.repeat(to_f64(w.k_scale), w.block, axis=-1)[..., None]
+        vs = np.repeat(to_f64(w.v_scale), w.block, axis=-1)[..., None]
+        return k * ks, v * vs
+    return to_f64(w.k), to_f64(w.v)
+
+
+def attention(w, mask=None):
+    """(O [B,H,S,D], LSE base 2 [B,H,S]) by dense masked softmax."""
+    if mask is None:
+        mask = dense_mask(w)
+    q = to_f64(w.q)
+    k, v = kv_f64(w)
+    logits = np.einsum("bhsd,bhtd->bhst", q, k) * w.sm_scale
+    logits = np.where(mask, logits, -np.inf)
+    any_key = mask.any(axis=-1)
+    safe = np.where(any_key[..., None], logits, 0.0)
+    lse_e = logsumexp(safe, axis=-1)
+    p = np.where(mask, np.exp(safe - lse_e[..., None]), 0.0)
+    o = np.einsum("bhst,bhtd->bhsd", p, v)
+    o = np.where(any_key[..., None], o, 0.0)
+    lse2 = np.where(any_key, lse_e / np.log(2.0), LSE_EMPTY)
+    return o, lse2

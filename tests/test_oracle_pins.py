@@ -1,0 +1,408 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test checks the oracle against something it does not share code with:
+library routines (torch's bf16/fp8 casts, torch SDPA, scipy logsumexp), an
+independent dense brute force, closed forms and invariants of the definition
+of sparse softmax attention (FastVideo "block_sparse_attn_sm100a.py",
+`is_supported` docstring; rocke "sparse_attention.py", module docstring and
+`_stage_vsa_bitmap_to_lds`; rocke "sage_attention.py", module docstring).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import bruteforce as bf
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+def run_oracle(w, **kw):
+    args = dict(block=w.block, sm_scale=w.sm_scale, k_scale=w.k_scale,
+                v_scale=w.v_scale)
+    args.update(kw)
+    if w.form == "lut":
+        return oracle.fwd_lut(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs,
+                              meta_strides=w.meta_strides, **args)
+    return oracle.fwd_bitmap(w.q, w.k, w.v, w.mask, w.vbs,
+                             mask_strides=w.mask_strides, **args)
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_bf16_decode_matches_torch_for_every_pattern():
+    bits = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16)
+    ref = bits.view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_value(int(b) & 0xFFFF) for b in bits.tolist()])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def test_fp8e4m3_decode_matches_torch_for_every_code():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.fp8e4m3_value(c) for c in range(256)])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+    assert oracle.fp8e4m3_value(0x7E) == 448.0  # largest finite
+    assert oracle.fp8e4m3_value(0x01) == 2.0 ** -9  # smallest subnormal
+    assert math.isnan(oracle.fp8e4m3_value(0x7F))
+
+
+# ------------------------------------------------- dense reduction (SDPA)
+
+@pytest.mark.parametrize("block,B,H,S", [(64, 2, 2, 256), (128, 1, 3, 512)])
+def test_full_lut_equals_dense_sdpa(block, B, H, S):
+    w = workloads.make_random(11 + block, B=B, H=H, S=S, block=block,
+                              density=1.0)
+    NQ = S // block
+    assert int(w.q2k_num.min()) == NQ  # every block selected, vbs full
+    o, lse = run_oracle(w)
+    q = w.q.to(torch.float64)
+    k = w.k.to(torch.float64)
+    v = w.v.to(torch.float64)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, scale=w.sm_scale).numpy()
+    lse_ref = (torch.logsumexp(q @ k.transpose(-1, -2) * w.sm_scale, dim=-1)
+               * LOG2E).numpy()
+    np.testing.assert_allclose(o, ref, atol=1e-10, rtol=1e-9)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-10, rtol=1e-10)
+
+
+def test_full_bitmap_equals_dense_sdpa_custom_scale():
+    w = workloads.make_random(5, B=1, H=2, S=256, block=64, form="bitmap",
+                              density=1.1)
+    w.sm_scale = 0.37
+    o, lse = run_oracle(w)
+    q, k, v = (t.to(torch.float64) for t in (w.q, w.k, w.v))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, scale=0.37).numpy()
+    lse_ref = (torch.logsumexp(q @ k.transpose(-1, -2) * 0.37, dim=-1)
+               * LOG2E).numpy()
+    np.testing.assert_allclose(o, ref, atol=1e-10, rtol=1e-9)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-10, rtol=1e-10)
+
+
+# ------------------------------------------------------ dense brute force
+
+BRUTE_CASES = [
+    dict(seed=1, block=64, S=256, density=0.5, vbs_mode="random"),
+    dict(seed=2, block=64, S=512, count_mode="uniform", vbs_mode="zero_some"),
+    dict(seed=3, block=128, S=512, count_mode="uniform", vbs_mode="partial",
+         max_kv=3),
+    dict(seed=4, block=64, S=256, form="bitmap", density=0.4,
+         vbs_mode="random"),
+    dict(seed=5, block=64, S=256, shared_meta=True, density=0.5,
+         vbs_mode="partial"),
+    dict(seed=6, block=64, S=256, form="bitmap", shared_meta=True,
+         density=0.6),
+    dict(seed=7, block=64, S=256, kv="fp8", density=0.5, vbs_mode="random"),
+    dict(seed=8, block=128, S=256, kv="fp8", form="bitmap", density=0.7,
+         std=3.0),
+]
+
+
+@pytest.mark.parametrize("case", BRUTE_CASES)
+def test_oracle_matches_dense_bruteforce(case):
+    case = dict(case)
+    seed = case.pop("seed")
+    w = workloads.make_random(seed, B=2, H=2, **case)
+    o, lse = run_oracle(w)
+    o_ref, lse_ref = bf.attention(w)
+    np.testing.assert_allclose(o, o_ref, atol=1e-10, rtol=1e-9)
+    empty = lse_ref == bf.LSE_EMPTY
+    assert (lse[empty] == bf.LSE_EMPTY).all()
+    assert (o[empty] == 0).all()
+    np.testing.assert_allclose(lse[~empty], lse_ref[~empty], atol=1e-10,
+                               rtol=1e-10)
+
+
+def test_units_subset_matches_full_run():
+    w = workloads.make_random(9, B=2, H=3, S=512, block=64,
+                              count_mode="uniform", vbs_mode="random")
+    o, lse = run_oracle(w)
+    units = [0, 5, 17, 47, 30]
+    os_, ls_ = run_oracle(w, units=units)
+    of = o.reshape(-1, w.block, w.D)
+    lf = lse.reshape(-1, w.block)
+    for i, u in enumerate(units):
+        assert np.array_equal(os_[i], of[u])
+        assert np.array_equal(ls_[i], lf[u])
+
+
+# ------------------------------------------------------------ closed forms
+
+def _single_row_lut(B, H, S, block, row_sets, vbs=None):
+    """LUT workload with explicit per-unit sets (list of lists)."""
+    NQ = S // block
+    rows = B * H * NQ
+    max_kv = max(1, max(len(s) for s in row_sets))
+    idx = torch.full((rows, max_kv), -1, dtype=torch.int32)
+    num = torch.zeros((rows,), dtype=torch.int32)
+    for r, s in enumerate(row_sets):
+        idx[r, :len(s)] = torch.tensor(s, dtype=torch.int32)
+        num[r] = len(s)
+    return idx, num
+
+
+def test_zero_query_gives_mean_of_attended_values():
+    w = workloads.make_random(21, B=1, H=2, S=256, block=64, density=0.5,
+                              vbs_mode="partial")
+    w.q = torch.zeros_like(w.q)
+    o, lse = run_oracle(w)
+    mask = bf.dense_mask(w)
+    v = bf.to_f64(w.v)
+    for h in range(w.H):
+        for r in range(w.S):
+            keys = np.nonzero(mask[0, h, r])[0]
+            assert len(keys) > 0
+            np.testing.assert_allclose(o[0, h, r], v[0, h, keys].mean(axis=0),
+                                       atol=1e-12)
+            assert abs(lse[0, h, r] - math.log2(len(keys))) < 1e-12
+
+
+def test_single_attended_key_gives_its_value_and_score_lse():
+    B, H, S, blk = 1, 1, 256, 64
+    w = workloads.make_random(22, B=B, H=H, S=S, block=blk)
+    # every q-block selects block 2 only; block 2 has exactly one valid key
+    idx, num = _single_row_lut(B, H, S, blk, [[2]] * 4)
+    w.q2k_idx, w.q2k_num = idx, num
+    w.vbs = torch.tensor([64, 64, 1, 64], dtype=torch.int32)
+    o, lse = run_oracle(w)
+    q = bf.to_f64(w.q)[0, 0]
+    k = bf.to_f64(w.k)[0, 0, 128]
+    v = bf.to_f64(w.v)[0, 0, 128]
+    for r in range(S):
+        np.testing.assert_array_equal(o[0, 0, r], v)
+        t = float(q[r] @ k) * w.sm_scale * LOG2E
+        assert abs(lse[0, 0, r] - t) < 1e-11
+
+
+def test_two_keys_give_sigmoid_weights():
+    B, H, S, blk = 1, 1, 128, 64
+    w = workloads.make_random(23, B=B, H=H, S=S, block=blk)
+    idx, num = _single_row_lut(B, H, S, blk, [[1], [0]])
+    w.q2k_idx, w.q2k_num = idx, num
+    w.vbs = torch.tensor([2, 2], dtype=torch.int32)
+    o, lse = run_oracle(w)
+    q = bf.to_f64(w.q)[0, 0]
+    k = bf.to_f64(w.k)[0, 0]
+    v = bf.to_f64(w.v)[0, 0]
+    for r in range(S):
+        kb = 1 if r < 64 else 0
+        k0, k1 = k[kb * 64], k[kb * 64 + 1]
+        a = q[r] @ k0 * w.sm_scale
+        b = q[r] @ k1 * w.sm_scale
+        w0 = 1.0 / (1.0 + math.exp(b - a))
+        np.testing.assert_allclose(
+            o[0, 0, r], w0 * v[kb * 64] + (1 - w0) * v[kb * 64 + 1],
+            atol=1e-12, rtol=1e-12)
+        ref = (max(a, b) + math.log1p(math.exp(-abs(a - b)))) * LOG2E
+        assert abs(lse[0, 0, r] - ref) < 1e-12
+
+
+def test_count_zero_rows_give_exact_zero_and_sentinel():
+    w = workloads.make_random(24, B=1, H=2, S=256, block=64,
+                              count_mode="zero")
+    o, lse = run_oracle(w)
+    assert (o == 0).all() and not np.signbit(o).any()
+    assert (lse == oracle.LSE_EMPTY).all()
+    assert oracle.LSE_EMPTY == -3.4028234663852886e38
+
+
+def test_all_selected_blocks_empty_by_vbs_is_an_empty_row():
+    w = workloads.make_random(25, B=1, H=1, S=256, block=64, density=0.5)
+    w.vbs = torch.zeros((4,), dtype=torch.int32)
+    o, lse = run_oracle(w)
+    assert (o == 0).all() and (lse == oracle.LSE_EMPTY).all()
+
+
+# -------------------------------------------------------------- invariants
+
+def _lut_copy(w, idx=None, num=None):
+    import copy
+    w2 = copy.copy(w)
+    if idx is not None:
+        w2.q2k_idx = idx
+    if num is not None:
+        w2.q2k_num = num
+    return w2
+
+
+def test_lut_order_padding_and_duplicates_do_not_matter():
+    w = workloads.make_random(31, B=2, H=2, S=512, block=64, max_kv=6,
+                              count_mode="uniform", vbs_mode="random")
+    o, lse = run_oracle(w)
+    g = torch.Generator().manual_seed(0)
+    idx = w.q2k_idx.clone()
+    num = w.q2k_num
+    for r in range(idx.shape[0]):
+        n = int(num[r])
+        idx[r, :n] = idx[r, :n][torch.randperm(n, generator=g)]
+        pads = torch.tensor([-2**31, w.NQ + 5, 10**6, -1, w.NQ, 7],
+                            dtype=torch.int32)
+        idx[r, n:] = pads[:idx.shape[1] - n]
+    o2, l2 = run_oracle(_lut_copy(w, idx=idx))
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+    # duplicates: append each row's first entry again in a wider LUT
+    wide = torch.full((idx.shape[0], idx.shape[1] + 1), -1, dtype=torch.int32)
+    num2 = num.clone()
+    for r in range(idx.shape[0]):
+        n = int(num[r])
+        wide[r, :n] = idx[r, :n]
+        if n > 0:
+            wide[r, n] = idx[r, 0]
+            num2[r] = n + 1
+    o3, l3 = run_oracle(_lut_copy(w, idx=wide, num=num2))
+    assert np.array_equal(o, o3) and np.array_equal(lse, l3)
+
+
+def test_out_of_range_entries_and_counts_are_skipped_and_clamped():
+    w = workloads.make_random(32, B=1, H=2, S=256, block=64, max_kv=4,
+                              count_mode="uniform")
+    o, lse = run_oracle(w)
+    idx = w.q2k_idx.clone()
+    num = w.q2k_num.clone()
+    # insert an out-of-range entry below the count (skipped) by widening
+    wide = torch.full((idx.shape[0], 6), 3, dtype=torch.int32)
+    num2 = num.clone()
+    for r in range(idx.shape[0]):
+        n = int(num[r])
+        row = idx[r, :n].tolist() + [w.NQ + 3]
+        wide[r, :len(row)] = torch.tensor(row, dtype=torch.int32)
+        num2[r] = len(row)
+    o2, l2 = run_oracle(_lut_copy(w, idx=wide, num=num2))
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+    # count above max_kv is clamped to max_kv; negative count means 0
+    full = _lut_copy(w, num=torch.full_like(num, 4))
+    o3, l3 = run_oracle(full)
+    o4, l4 = run_oracle(_lut_copy(w, num=torch.full_like(num, 99)))
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
+    o5, l5 = run_oracle(_lut_copy(w, num=torch.full_like(num, -7)))
+    assert (o5 == 0).all() and (l5 == oracle.LSE_EMPTY).all()
+
+
+def test_vbs_is_clamped_to_block():
+    w = workloads.make_random(33, B=1, H=1, S=256, block=64, density=0.5)
+    o, lse = run_oracle(w)
+    w.vbs = torch.tensor([64, 1000, 64, 65], dtype=torch.int32)
+    o2, l2 = run_oracle(w)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+def test_bitmap_equals_compacted_lut():
+    w = workloads.make_random(34, B=2, H=2, S=512, block=64, form="bitmap",
+                              density=0.4, vbs_mode="random")
+    o, lse = run_oracle(w)
+    # compaction by numpy (independent of the oracle's own compaction)
+    m = w.mask.numpy()
+    idx = np.full(m.shape, -1, dtype=np.int32)
+    num = np.zeros(m.shape[0], dtype=np.int32)
+    for r in range(m.shape[0]):
+        nz = np.nonzero(m[r])[0]
+        idx[r, :len(nz)] = nz
+        num[r] = len(nz)
+    o2, l2 = oracle.fwd_lut(w.q, w.k, w.v, torch.from_numpy(idx),
+                            torch.from_numpy(num), w.vbs, block=w.block,
+                            meta_strides=w.mask_strides)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+    i3, n3 = oracle.mask_to_lut(w.mask)
+    assert np.array_equal(i3.numpy(), idx) and np.array_equal(n3.numpy(), num)
+
+
+def test_output_is_linear_in_v():
+    w = workloads.make_random(35, B=1, H=2, S=256, block=64, density=0.5,
+                              vbs_mode="partial")
+    o, lse = run_oracle(w)
+    w.v = (-2.0 * w.v.float()).to(torch.bfloat16)  # exact in bf16
+    o2, l2 = run_oracle(w)
+    np.testing.assert_allclose(o2, -2.0 * o, atol=1e-12, rtol=1e-12)
+    assert np.array_equal(lse, l2)
+
+
+def test_common_key_shift_moves_lse_only():
+    """Adding one vector u to every key multiplies every weight of a row by
+    2^(c q.u): O is unchanged and LSE shifts by c*q.u (integer data so that
+    K + u is exact in bf16)."""
+    g = torch.Generator().manual_seed(36)
+    w = workloads.make_random(36, B=1, H=1, S=256, block=64, density=0.5,
+                              vbs_mode="partial")
+    w.q = torch.randint(-3, 4, w.q.shape, generator=g).to(torch.bfloat16)
+    w.k = torch.randint(-3, 4, w.k.shape, generator=g).to(torch.bfloat16)
+    o, lse = run_oracle(w)
+    u = torch.randint(-2, 3, (w.D,), generator=g)
+    w2 = _lut_copy(w)
+    w2.k = (w.k.float() + u.float()).to(torch.bfloat16)
+    o2, l2 = run_oracle(w2)
+    np.testing.assert_allclose(o2, o, atol=1e-12, rtol=1e-10)
+    shift = (w.q.double() @ u.double()).numpy() * w.sm_scale * LOG2E
+    np.testing.assert_allclose(l2, lse + shift, atol=1e-10)
+
+
+def test_heads_and_batches_are_independent():
+    w = workloads.make_random(37, B=2, H=3, S=256, block=64,
+                              count_mode="uniform", vbs_mode="random")
+    o, lse = run_oracle(w)
+    NQ = w.NQ
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = slice((b * w.H + h) * NQ, (b * w.H + h + 1) * NQ)
+            o1, l1 = oracle.fwd_lut(
+                w.q[b:b + 1, h:h + 1], w.k[b:b + 1, h:h + 1],
+                w.v[b:b + 1, h:h + 1], w.q2k_idx[rows], w.q2k_num[rows],
+                w.vbs, block=w.block, meta_strides=(NQ, NQ))
+            assert np.array_equal(o1[0, 0], o[b, h])
+            assert np.array_equal(l1[0, 0], lse[b, h])
+
+
+def test_fp8_scales_fold_linearly():
+    """Doubling V's block scales doubles O; doubling K's scale doubles every
+    logit (checked against the brute force)."""
+    w = workloads.make_random(38, B=1, H=2, S=256, block=64, kv="fp8",
+                              density=0.5)
+    o, lse = run_oracle(w)
+    w.v_scale = w.v_scale * 2
+    o2, l2 = run_oracle(w)
+    np.testing.assert_allclose(o2, 2 * o, atol=1e-12, rtol=1e-12)
+    assert np.array_equal(l2, lse)
+    w.k_scale = w.k_scale * 2
+    o3, l3 = run_oracle(w)
+    o_ref, l_ref = bf.attention(w)
+    np.testing.assert_allclose(o3, o_ref, atol=1e-10, rtol=1e-9)
+    np.testing.assert_allclose(l3, l_ref, atol=1e-10)
+
+
+# ---------------------------------------------------- integer decode only
+
+@pytest.mark.parametrize("form", ["lut", "bitmap"])
+def test_key_counts_match_python_sets(form):
+    w = workloads.make_random(41, B=2, H=2, S=512, block=64, form=form,
+                              count_mode="uniform", density=0.3,
+                              vbs_mode="random")
+    kw = dict(B=w.B, H=w.H, S=w.S, block=w.block, vbs=w.vbs)
+    if form == "lut":
+        c = oracle.key_counts(q2k_idx=w.q2k_idx, q2k_num=w.q2k_num,
+                              meta_strides=w.meta_strides, **kw)
+    else:
+        c = oracle.key_counts(mask=w.mask, mask_strides=w.mask_strides, **kw)
+    sets = bf.selected_sets(w)
+    vbs = w.vbs.tolist()
+    for u, s in enumerate(sets):
+        want = [min(max(vbs[kb], 0), w.block) if kb in s else 0
+                for kb in range(w.NQ)]
+        assert c[u].tolist() == want
+
+
+def test_tiny_named_workload_runs_and_has_expected_structure():
+    w = workloads.make_config(0)
+    assert (w.B, w.H, w.S, w.block) == (1, 1, 512, 64)
+    assert w.vbs.tolist() == [64] * 7 + [40]
+    assert (w.q2k_num == 4).all()
+    o, lse = run_oracle(w)
+    o_ref, l_ref = bf.attention(w)
+    np.testing.assert_allclose(o, o_ref, atol=1e-10, rtol=1e-9)
+    np.testing.assert_allclose(lse, l_ref, atol=1e-10)
