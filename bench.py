@@ -1,0 +1,243 @@
+"""Benchmark of the block-sparse attention forward on one MI355X.
+
+A step is one forward pass (one kernel launch: decode, gather, QK^T, softmax,
+PV, epilogue) over the video-shaped VSA workload: B=1, H=24, S=49152
+(768 blocks of 64 tokens), D=128, bf16 N(0,1), 96 of 768 key blocks per query
+block (sorted LUT), variable_block_sizes uniform in [16, 64].  Inputs are
+resident in HBM before the timed region starts.
+
+Metric: effective TFLOP/s = 4*D*P / kernel time, with P the exact number of
+attended (query, key) pairs of the seeded metadata, against the MI355X bf16
+dense MFMA peak (2.5 PFLOP/s).  Prints ONE JSON line on stdout; progress goes
+to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import block_sparse_attention_tile_amd as bsa  # noqa: E402
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_attention_tile_amd", "csrc",
+                             "bsa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsa_fwd_traffic.json")
+
+
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def selected_matrix(w) -> torch.Tensor:
+    """[n_units, NK] bool: key block kb is selected by unit u (set semantics:
+    LUT entries below the clamped count, inside [0, NK))."""
+    NQ = w.NQ
+    u = torch.arange(w.n_units)
+    qb, h, b = u % NQ, (u // NQ) % w.H, u // (NQ * w.H)
+    if w.form == "lut":
+        sb, sh = w.meta_strides
+        rows = b * sb + h * sh + qb
+        idx = w.q2k_idx.long()[rows]
+        n = w.q2k_num.long()[rows].clamp(0, idx.shape[-1])
+        ok = (torch.arange(idx.shape[-1])[None, :] < n[:, None]) & \
+             (idx >= 0) & (idx < NQ)
+        sel = torch.zeros((w.n_units, NQ + 1), dtype=torch.bool)
+        sel.scatter_(1, torch.where(ok, idx, torch.full_like(idx, NQ)),
+                     torch.ones_like(ok))
+        return sel[:, :NQ]
+    sb, sh = w.mask_strides
+    rows = b * sb + h * sh + qb
+    return w.mask[rows] != 0
+
+
+def attended_pairs(w, units=None) -> int:
+    """Exact number of attended (query, key) pairs (per unit: block query
+    rows times the valid keys of its selected blocks)."""
+    sel = selected_matrix(w)
+    if units is not None:
+        sel = sel[torch.as_tensor(units, dtype=torch.long)]
+    nv = torch.full((w.NQ,), w.block, dtype=torch.long) if w.vbs is None \
+        else w.vbs.long().clamp(0, w.block)
+    return int((sel.long() * nv[None, :]).sum()) * w.block
+
+
+def launch(w, d, out, lse):
+    if w.form == "lut":
+        bsa.bsa_fwd_lut(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"],
+                        d["vbs"], block=w.block, sm_scale=w.sm_scale,
+                        k_scale=d["k_scale"], v_scale=d["v_scale"],
+                        meta_strides=w.meta_strides, out=out, lse=lse)
+    else:
+        bsa.bsa_fwd_bitmap(d["q"], d["k"], d["v"], d["mask"], d["vbs"],
+                           block=w.block, sm_scale=w.sm_scale,
+                           k_scale=d["k_scale"], v_scale=d["v_scale"],
+                           mask_strides=w.mask_strides, out=out, lse=lse)
+
+
+def stored_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload_name)
+    if not e or e.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float):
+    """The oracle (as it stands) on a bounded sample of the same workload's
+    work units; throughput in the same unit as the GPU metric."""
+    import numpy as np
+
+    import oracle
+    g = np.random.default_rng(1234)
+    order = g.permutation(w.n_units)
+    kw = dict(block=w.block, sm_scale=w.sm_scale, k_scale=w.k_scale,
+              v_scale=w.v_scale)
+
+    def run(units):
+        t0 = time.perf_counter()
+        if w.form == "lut":
+            oracle.fwd_lut(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs,
+                           meta_strides=w.meta_strides, units=units, **kw)
+        else:
+            oracle.fwd_bitmap(w.q, w.k, w.v, w.mask, w.vbs,
+                              mask_strides=w.mask_strides, units=units, **kw)
+        return time.perf_counter() - t0
+
+    threads = oracle.num_threads()
+    probe = order[:max(1, threads)].tolist()
+    t_probe = run(probe)
+    per_unit = t_probe / len(probe)
+    n = int(min(w.n_units, max(len(probe), target_s / max(per_unit, 1e-6))))
+    units = order[:n].tolist()
+    progress(f"cpu baseline: oracle on {n} of {w.n_units} units "
+             f"({threads} threads, ~{per_unit * n:.1f} s)")
+    dt = run(units)
+    pairs = attended_pairs(w, units)
+    return {
+        "value": 4.0 * w.D * pairs / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{n} of {w.n_units} work units (b,h,q-block) of "
+                   f"{w.name}, drawn at random (seed 1234); {pairs} attended "
+                   f"pairs in {dt:.2f} s, fp64 C oracle with OpenMP"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="named workload index (default 2: video-shaped VSA)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the forward "
+              "pass on a single MI355X (each GPU would take its own share of "
+              "heads with no communication); --gpus must be 1.",
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    progress(f"generating workload {args.workload}")
+    w = workloads.make_config(args.workload)
+    pairs = attended_pairs(w)
+    flop = 4.0 * w.D * pairs
+    dev = torch.device("cuda:0")
+    d = {n: (None if getattr(w, n) is None else getattr(w, n).to(dev))
+         for n in ("q", "k", "v", "k_scale", "v_scale", "q2k_idx", "q2k_num",
+                   "mask", "vbs")}
+    out = torch.empty(tuple(w.q.shape), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    progress(f"warmup {args.warmup} steps on {w.name}")
+    for _ in range(args.warmup):
+        launch(w, d, out, lse)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        launch(w, d, out, lse)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    progress(f"timed {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)")
+
+    tflops = flop / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "effective TFLOP/s (4*D*attended pairs) + % bf16 MFMA peak, "
+                  "VSA fwd",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-kv/bf16" if w.kv_fp8 else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "B": w.B, "H": w.H, "S": w.S, "D": w.D, "block": w.block,
+            "form": w.form,
+            "attended_pairs": pairs,
+            "effective_flop_per_step": flop,
+            "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": stored_traffic(w.name),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,21 @@
+"""MI355X (gfx950) block-sparse attention forward.
+
+The compute runs in the HIP library ``libbsa.so`` (C ABI in
+``include/bsa.h``); this package only marshals torch tensors into it.
+"""
+
+from .api import (  # noqa: F401
+    BSA_ERR_ALIGN,
+    BSA_ERR_HIP,
+    BSA_ERR_NULL,
+    BSA_ERR_SHAPE,
+    BSA_ERR_UNSUPPORTED,
+    BSA_KV_BF16,
+    BSA_KV_FP8E4M3,
+    BSA_OK,
+    LSE_EMPTY,
+    BsaError,
+    bsa_fwd_bitmap,
+    bsa_fwd_lut,
+    bsa_status_str,
+)

@@ -1,0 +1,42 @@
+"""ctypes loader for the HIP library ``libbsa.so`` (built in-tree by
+``block_sparse_attention_tile_amd.build``).  There is no fallback: if the
+library is missing or does not load, every call raises."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsa.so")
+
+# The exported C symbols, as declared in include/bsa.h.
+EXPORTS = ("bsa_fwd_lut", "bsa_fwd_bitmap", "bsa_status_str")
+
+_lib = None
+
+
+def load():
+    """Loads (once) and returns the ctypes handle of libbsa.so."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m block_sparse_attention_tile_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.bsa_fwd_lut.restype = ctypes.c_int32
+    lib.bsa_fwd_lut.argtypes = [
+        P, P, P, i32, P, P, P, P, i32, i64, i64, P, f32, P, P,
+        i32, i32, i32, i32, i32, P]
+    lib.bsa_fwd_bitmap.restype = ctypes.c_int32
+    lib.bsa_fwd_bitmap.argtypes = [
+        P, P, P, i32, P, P, P, i64, i64, P, f32, P, P,
+        i32, i32, i32, i32, i32, P]
+    lib.bsa_status_str.restype = ctypes.c_char_p
+    lib.bsa_status_str.argtypes = [i32]
+    _lib = lib
+    return lib

@@ -1,0 +1,145 @@
+"""Thin Python binding of the C ABI in ``include/bsa.h``.
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels of ``libbsa.so``.  PyTorch supplies device memory and the stream
+(``torch.cuda.current_stream()``); outputs are allocated here with
+``torch.empty`` when not passed in.  Integer metadata is cast to contiguous
+int32 as the FastVideo wrapper does (``block_sparse_attn_sm100a``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+BSA_OK = 0
+BSA_ERR_NULL = 1
+BSA_ERR_SHAPE = 2
+BSA_ERR_UNSUPPORTED = 3
+BSA_ERR_ALIGN = 4
+BSA_ERR_HIP = 5
+BSA_KV_BF16 = 0
+BSA_KV_FP8E4M3 = 1
+LSE_EMPTY = -3.4028234663852886e38  # BSA_LSE_EMPTY = -FLT_MAX
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = int(status)
+        super().__init__(f"bsa status {status}: {bsa_status_str(status)}")
+
+
+def bsa_status_str(status: int) -> str:
+    return _lib.load().bsa_status_str(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _kv_dtype(k: torch.Tensor, v: torch.Tensor) -> int:
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must have the same dtype")
+    if k.dtype == torch.bfloat16:
+        return BSA_KV_BF16
+    if k.dtype == torch.float8_e4m3fn:
+        return BSA_KV_FP8E4M3
+    raise TypeError(f"unsupported k/v dtype {k.dtype}")
+
+
+def _i32(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    return None if t is None else t.to(torch.int32).contiguous()
+
+
+def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block):
+    if q.dtype != torch.bfloat16 or q.dim() != 4:
+        raise TypeError("q must be a 4-D bf16 [B, H, S, D] tensor")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same [B, H, S, D] shape")
+    kvd = _kv_dtype(k, v)
+    if kvd == BSA_KV_FP8E4M3:
+        if k_scale is None or v_scale is None:
+            raise ValueError("fp8 k/v need k_scale and v_scale")
+        k_scale = k_scale.to(torch.float32).contiguous()
+        v_scale = v_scale.to(torch.float32).contiguous()
+    else:
+        k_scale = v_scale = None
+    B, H, S, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if need_lse and lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if not need_lse:
+        lse = None
+    return q, k, v, kvd, k_scale, v_scale, out, lse
+
+
+def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                q2k_idx: torch.Tensor, q2k_num: torch.Tensor,
+                variable_block_sizes: Optional[torch.Tensor] = None, *,
+                block: int, sm_scale: Optional[float] = None,
+                k_scale: Optional[torch.Tensor] = None,
+                v_scale: Optional[torch.Tensor] = None,
+                meta_strides: Optional[Tuple[int, int]] = None,
+                need_lse: bool = True, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None):
+    """VSA form.  Returns ``(out, lse)`` (``lse`` is None if not needed).
+    ``meta_strides=(sb, sh)``: the LUT row of (b, h, qb) is
+    ``b*sb + h*sh + qb``; default one row per unit."""
+    q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
+                                              lse, need_lse, block)
+    B, H, S, D = q.shape
+    NQ = S // block
+    idx = _i32(q2k_idx)
+    num = _i32(q2k_num)
+    vbs = _i32(variable_block_sizes)
+    sb, sh = meta_strides if meta_strides is not None else (H * NQ, NQ)
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    st = (stream or torch.cuda.current_stream(q.device)).cuda_stream
+    rc = _lib.load().bsa_fwd_lut(
+        _ptr(q), _ptr(k), _ptr(v), kvd, _ptr(ks), _ptr(vs), _ptr(idx),
+        _ptr(num), int(idx.shape[-1]), int(sb), int(sh), _ptr(vbs),
+        float(sm_scale), _ptr(out), _ptr(lse), B, H, S, D, int(block),
+        ctypes.c_void_p(st))
+    if rc != BSA_OK:
+        raise BsaError(rc)
+    return out, lse
+
+
+def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   mask: torch.Tensor,
+                   variable_block_sizes: Optional[torch.Tensor] = None, *,
+                   block: int, sm_scale: Optional[float] = None,
+                   k_scale: Optional[torch.Tensor] = None,
+                   v_scale: Optional[torch.Tensor] = None,
+                   mask_strides: Optional[Tuple[int, int]] = None,
+                   need_lse: bool = True, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None):
+    """Jenga form.  ``mask`` is an int8 (or bool) tensor of rows of S/block
+    bytes; ``mask_strides=(sb, sh)`` as in the LUT form ((0, 0) = one
+    [NQ, NK] mask shared by all batches and heads)."""
+    q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
+                                              lse, need_lse, block)
+    B, H, S, D = q.shape
+    NQ = S // block
+    m = mask.to(torch.int8).contiguous()
+    vbs = _i32(variable_block_sizes)
+    sb, sh = mask_strides if mask_strides is not None else (H * NQ, NQ)
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    st = (stream or torch.cuda.current_stream(q.device)).cuda_stream
+    rc = _lib.load().bsa_fwd_bitmap(
+        _ptr(q), _ptr(k), _ptr(v), kvd, _ptr(ks), _ptr(vs), _ptr(m),
+        int(sb), int(sh), _ptr(vbs), float(sm_scale), _ptr(out), _ptr(lse),
+        B, H, S, D, int(block), ctypes.c_void_p(st))
+    if rc != BSA_OK:
+        raise BsaError(rc)
+    return out, lse

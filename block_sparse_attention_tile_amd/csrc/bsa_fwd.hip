@@ -1,0 +1,588 @@
+// bsa_fwd.hip -- block-sparse attention forward for MI355X (gfx950 / CDNA4).
+//
+// One workgroup computes one work unit: the `BLK` query rows of query block
+// qb of head h of batch b.  The steps, in order:
+//
+//  A1  unit id -> (b, h, qb), with workgroups of consecutive ids spread so
+//      that each XCD (and its L2) serves a contiguous range of heads.
+//  A2  selected-set decode into LDS.  LUT form: the row's first
+//      clamp(num, 0, max_kv) entries are scattered into a byte bitmap
+//      (duplicate stores write the same 1, out-of-range entries are dropped),
+//      as in rocke "sparse_attention.py" `_stage_vsa_bitmap_to_lds`.  Bitmap
+//      form: the mask row is copied into the same LDS bitmap
+//      (`_stage_jenga_mask_to_lds` on the same page).  One wave then
+//      compacts the bitmap into an ascending list of selected key blocks that
+//      have at least one valid key (ballot + popcount), so the K loop runs
+//      over selected tiles only and never touches an unselected one (the
+//      tile-skipping form the page calls strictly stronger than forcing
+//      -inf).  Ascending order makes the result independent of LUT order,
+//      padding and repetitions.
+//  A3  Q: each wave keeps its 32 query rows in VGPRs as MFMA operands for
+//      the whole K loop (loaded once with 128-bit loads).
+//  A4  K/V gather: 32-key tiles of the selected blocks, only rows below the
+//      block's valid count are read (coalesced 128-bit loads); rows past it
+//      are written as zeros.  Tiles are double-buffered in LDS: the loads of
+//      tile i+1 are in flight while tile i is computed.  fp8 e4m3 K/V are
+//      widened to bf16 exactly on the way into LDS.
+//  A5  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (fp32 accumulate), scaled by
+//      sm_scale*log2(e) (times the block's K scale for fp8); keys at or past
+//      the block's valid count are set to -inf.
+//  A6  online softmax in exp2 form (vLLM "tq_decode" step F shows the same
+//      running-max / rescale scheme): per-row running max m and partial sums
+//      l kept per lane, the max reduced across the four lane groups that
+//      share a query.
+//  A7  O^T += V^T P^T on the same MFMA; P is the softmax tile rounded to
+//      bf16 (times the block's V scale for fp8), already in the operand
+//      layout; V^T comes from the hardware transposing LDS read
+//      ds_read_b64_tr_b16 (the gfx950 idiom of the "tq_decode" page).
+//  A8  epilogue: O = acc / l rounded to bf16 (RNE), LSE = m + log2(l); a
+//      unit with no attended key writes +0 and BSA_LSE_EMPTY (FastVideo
+//      "block_sparse_attn_sm100a.py", `is_supported` docstring).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bsa.h"
+
+namespace {
+
+constexpr int HD = 128;             // head dimension
+constexpr int KT = 32;              // keys per pipeline tile
+constexpr int KPITCH = HD + 8;      // K tile row pitch in bf16 (272 B)
+constexpr int VPITCH = HD + 16;     // V tile row pitch in bf16 (288 B)
+constexpr int K_TILE_BYTES = KT * KPITCH * 2;
+constexpr int V_TILE_BYTES = KT * VPITCH * 2;
+constexpr int STAGE_BYTES = K_TILE_BYTES + V_TILE_BYTES;
+constexpr int NSTAGE = 2;
+constexpr float LOG2E = 1.4426950408889634f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+struct FwdParams {
+  const uint16_t* q;
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* idx;   // LUT form
+  const int32_t* num;   // LUT form
+  const int8_t* mask;   // bitmap form
+  int64_t meta_sb;      // metadata row stride per batch (rows)
+  int64_t meta_sh;      // metadata row stride per head (rows)
+  const int32_t* vbs;   // [NK] or null
+  uint16_t* out;
+  float* lse;           // or null
+  float c;              // sm_scale * log2(e)
+  int32_t max_kv;
+  int32_t H, S, NK;
+  int32_t n_units;
+};
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+// Valid keys of key block kb.
+template <int BLK>
+__device__ __forceinline__ int block_valid(const int32_t* vbs, int kb) {
+  return vbs ? clampi(vbs[kb], 0, BLK) : BLK;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (id % 8).  Give XCD x the
+// contiguous unit range [x*n/8, (x+1)*n/8) so the units of one head, which
+// share K/V blocks, meet in the same L2.
+__device__ __forceinline__ int remap_unit(int bid, int n) {
+  if (n % 8 != 0) return bid;
+  return (bid % 8) * (n / 8) + bid / 8;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 f = {a, b};
+  bf16x2 r = __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, RNE
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// 4 fp8 e4m3 codes -> 4 bf16 (exact widening; scale 1).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  u32x2 r;
+  r.x = __builtin_bit_cast(uint32_t,
+                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t,
+                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  return r;
+}
+
+__device__ __forceinline__ float wave_max_groups(float x) {
+  // lanes l, l^16, l^32, l^48 hold the same query row
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Position of one pipeline tile: entry e of the selected-block list, first
+// key t0 within the block, valid keys nv of the block.
+struct Tile {
+  int e, kb, t0, nv;
+};
+
+template <int BLK>
+__device__ __forceinline__ Tile tile_at_entry(const uint16_t* list,
+                                              const int32_t* vbs, int e,
+                                              int nsel) {
+  Tile t;
+  t.e = e;
+  t.t0 = 0;
+  if (e < nsel) {
+    t.kb = __builtin_amdgcn_readfirstlane((int)list[e]);
+    t.nv = __builtin_amdgcn_readfirstlane(block_valid<BLK>(vbs, t.kb));
+  } else {
+    t.kb = 0;
+    t.nv = 0;
+  }
+  return t;
+}
+
+template <int BLK>
+__device__ __forceinline__ Tile next_tile(const Tile& cur, const uint16_t* list,
+                                          const int32_t* vbs, int nsel) {
+  if (cur.t0 + KT < cur.nv) {
+    Tile t = cur;
+    t.t0 += KT;
+    return t;
+  }
+  return tile_at_entry<BLK>(list, vbs, cur.e + 1, nsel);
+}
+
+// Per-thread staging registers for one K/V tile.
+template <bool FP8, int NT>
+struct Staging {
+  // bf16: 32 rows x 16 chunks of 16 B for each of K, V.
+  // fp8 : 32 rows x  8 chunks of 16 B for each of K, V.
+  static constexpr int CHUNKS_PER_ROW = FP8 ? 8 : 16;
+  static constexpr int CHUNKS = KT * CHUNKS_PER_ROW;
+  static constexpr int PER_THREAD = CHUNKS / NT;
+  static_assert(CHUNKS % NT == 0, "tile chunks must divide evenly");
+  u32x4 kr[PER_THREAD];
+  u32x4 vr[PER_THREAD];
+};
+
+template <bool FP8, int NT>
+__device__ __forceinline__ void load_tile(Staging<FP8, NT>& st, const void* kg,
+                                          const void* vg, int64_t plane_elems,
+                                          const Tile& t, int BLKv, int tid) {
+  constexpr int CPR = Staging<FP8, NT>::CHUNKS_PER_ROW;
+  constexpr int EB = FP8 ? 1 : 2;  // bytes per element
+  const int64_t key0 = (int64_t)t.kb * BLKv + t.t0;
+  const char* kb = (const char*)kg + (plane_elems + key0 * HD) * EB;
+  const char* vb = (const char*)vg + (plane_elems + key0 * HD) * EB;
+  const int nvt = t.nv - t.t0;  // valid rows in this tile (may exceed KT)
+#pragma unroll
+  for (int i = 0; i < Staging<FP8, NT>::PER_THREAD; ++i) {
+    const int c = tid + i * NT;
+    const int row = c / CPR;
+    const int col = c % CPR;
+    if (row < nvt) {
+      const int64_t off = (int64_t)row * HD * EB + col * 16;
+      st.kr[i] = *(const u32x4*)(kb + off);
+      st.vr[i] = *(const u32x4*)(vb + off);
+    } else {
+      st.kr[i] = u32x4{0, 0, 0, 0};
+      st.vr[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+template <bool FP8, int NT>
+__device__ __forceinline__ void store_tile(const Staging<FP8, NT>& st,
+                                           char* stage, int tid) {
+  constexpr int CPR = Staging<FP8, NT>::CHUNKS_PER_ROW;
+  char* ks = stage;
+  char* vs = stage + K_TILE_BYTES;
+#pragma unroll
+  for (int i = 0; i < Staging<FP8, NT>::PER_THREAD; ++i) {
+    const int c = tid + i * NT;
+    const int row = c / CPR;
+    const int col = c % CPR;
+    if constexpr (!FP8) {
+      *(u32x4*)(ks + row * KPITCH * 2 + col * 16) = st.kr[i];
+      *(u32x4*)(vs + row * VPITCH * 2 + col * 16) = st.vr[i];
+    } else {
+      // 16 fp8 codes -> 16 bf16 (32 B)
+      u32x2 k0 = fp8x4_to_bf16x4(st.kr[i].x), k1 = fp8x4_to_bf16x4(st.kr[i].y);
+      u32x2 k2 = fp8x4_to_bf16x4(st.kr[i].z), k3 = fp8x4_to_bf16x4(st.kr[i].w);
+      u32x2 v0 = fp8x4_to_bf16x4(st.vr[i].x), v1 = fp8x4_to_bf16x4(st.vr[i].y);
+      u32x2 v2 = fp8x4_to_bf16x4(st.vr[i].z), v3 = fp8x4_to_bf16x4(st.vr[i].w);
+      char* kd = ks + row * KPITCH * 2 + col * 32;
+      char* vd = vs + row * VPITCH * 2 + col * 32;
+      *(u32x4*)(kd) = u32x4{k0.x, k0.y, k1.x, k1.y};
+      *(u32x4*)(kd + 16) = u32x4{k2.x, k2.y, k3.x, k3.y};
+      *(u32x4*)(vd) = u32x4{v0.x, v0.y, v1.x, v1.y};
+      *(u32x4*)(vd + 16) = u32x4{v2.x, v2.y, v3.x, v3.y};
+    }
+  }
+}
+
+template <int BLK, bool FP8, bool BITMAP>
+__global__ __launch_bounds__(BLK * 2) void bsa_fwd_kernel(FwdParams p) {
+  constexpr int NW = BLK / 32;  // waves; each owns 32 query rows
+  constexpr int NT = NW * 64;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_nsel;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;    // lane group: 0..3
+  const int r16 = lane & 15;  // row within a 16-row MFMA tile
+
+  const int NK = p.NK;
+  uint8_t* bmp = (uint8_t*)(smem + NSTAGE * STAGE_BYTES);
+  uint16_t* list = (uint16_t*)(bmp + ((NK + 15) & ~15));
+
+  // ---- A1: work unit
+  const int u = remap_unit(blockIdx.x, p.n_units);
+  const int qb = u % NK;
+  const int bh = u / NK;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int64_t plane = (int64_t)bh * p.S * HD;  // element offset of (b, h)
+  const int64_t row = (int64_t)b * p.meta_sb + (int64_t)h * p.meta_sh + qb;
+
+  // ---- A2: selected set -> LDS bitmap
+  if constexpr (BITMAP) {
+    const int8_t* mrow = p.mask + row * NK;
+    for (int i = tid; i < NK; i += NT) bmp[i] = mrow[i] != 0;
+  } else {
+    for (int i = tid; i < NK; i += NT) bmp[i] = 0;
+    __syncthreads();
+    const int n = clampi(p.num[row], 0, p.max_kv);
+    const int32_t* irow = p.idx + row * p.max_kv;
+    for (int j = tid; j < n; j += NT) {
+      const int kb = irow[j];
+      if (kb >= 0 && kb < NK) bmp[kb] = 1;  // duplicates store the same 1
+    }
+  }
+  __syncthreads();
+  // bitmap -> ascending list of selected blocks with >= 1 valid key
+  if (wave == 0) {
+    int base = 0;
+    for (int c0 = 0; c0 < NK; c0 += 64) {
+      const int kb = c0 + lane;
+      const bool f = kb < NK && bmp[kb] != 0 && block_valid<BLK>(p.vbs, kb) > 0;
+      const uint64_t bal = __ballot(f);
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      if (f) list[pos] = (uint16_t)kb;
+      base += __popcll(bal);
+    }
+    if (lane == 0) s_nsel = base;
+  }
+  __syncthreads();
+  const int nsel = s_nsel;
+
+  const int qrow0 = qb * BLK + wave * 32;  // first query row of this wave
+
+  if (nsel == 0) {
+    // A8 for a unit with no attended key: exact zeros and the sentinel
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *(u32x2*)(p.out + r * HD + dt * 16 + g * 4) = u32x2{0u, 0u};
+      if (p.lse && g == 0) p.lse[r] = BSA_LSE_EMPTY;
+    }
+    return;
+  }
+
+  // ---- A3: Q operands (B operand of S^T = K Q^T): Q[row r16][d kk*32+g*8..]
+  bf16x8 qreg[2][4];
+  {
+    const uint16_t* qg = p.q + plane + (int64_t)qrow0 * HD;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qreg[qt][kk] = *(const bf16x8*)(qg + (qt * 16 + r16) * HD + kk * 32 + g * 8);
+  }
+
+  f32x4 oacc[8][2];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+  // ---- A4: prologue -- tile 0 into stage 0
+  Staging<FP8, NT> st;
+  Tile cur = tile_at_entry<BLK>(list, p.vbs, 0, nsel);
+  load_tile<FP8, NT>(st, p.k, p.v, plane, cur, BLK, tid);
+  store_tile<FP8, NT>(st, smem, tid);
+  __syncthreads();
+
+  const int64_t scale_row = (int64_t)bh * NK;
+
+  for (int it = 0;; ++it) {
+    const Tile nxt = next_tile<BLK>(cur, list, p.vbs, nsel);
+    const bool has_next = nxt.e < nsel;
+    if (has_next) load_tile<FP8, NT>(st, p.k, p.v, plane, nxt, BLK, tid);
+
+    const char* ks = smem + (it & 1) * STAGE_BYTES;
+    const char* vs = ks + K_TILE_BYTES;
+
+    // ---- A5: S^T[key][query] for the 32 keys x 32 queries of this wave
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) sacc[s2][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 kop =
+            *(const bf16x8*)(ks + ((s2 * 16 + r16) * KPITCH + kk * 32 + g * 8) * 2);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+          sacc[s2][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kop, qreg[qt][kk], sacc[s2][qt], 0, 0, 0);
+      }
+    }
+
+    // ---- A6: online softmax (exp2 form)
+    float cs = p.c;
+    float vsc = 1.f;
+    if constexpr (FP8) {
+      cs *= p.k_scale[scale_row + cur.kb];
+      vsc = p.v_scale[scale_row + cur.kb];
+    }
+    const int nvt = cur.nv - cur.t0;  // valid keys of this tile (>= 1)
+    bf16x8 pop[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float x[8];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[s2 * 4 + j] = sacc[s2][qt][j] * cs;
+      if (nvt < KT) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (s2 * 16 + g * 4 + j >= nvt) x[s2 * 4 + j] = -INFINITY;
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+      mx = wave_max_groups(mx);
+      const float mnew = fmaxf(m_run[qt], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mnew);
+      m_run[qt] = mnew;
+      float ps = 0.f;
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(x[i] - mnew);
+        ps += pv[i];
+      }
+      l_run[qt] = l_run[qt] * alpha + ps;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) oacc[dt][qt] *= alpha;
+      if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] *= vsc;
+      }
+      u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                  pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+      pop[qt] = __builtin_bit_cast(bf16x8, pk);
+    }
+
+    // ---- A7: O^T[d][query] += V^T P^T.  The MFMA K index 8g+i maps to tile
+    // key 4g+i (i<4) and 16+4g+(i-4) (i>=4), matching P's accumulator layout.
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const char* va = vs + ((lane >> 2) * VPITCH + dt * 16 + (lane & 3) * 4) * 2;
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)va);
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(va + 16 * VPITCH * 2));
+      const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            vop, pop[qt], oacc[dt][qt], 0, 0, 0);
+    }
+
+    if (!has_next) break;
+    store_tile<FP8, NT>(st, smem + ((it + 1) & 1) * STAGE_BYTES, tid);
+    __syncthreads();
+    cur = nxt;
+  }
+
+  // ---- A8: epilogue
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float l = wave_sum_groups(l_run[qt]);  // >= 1: the row max has weight 1
+    const float inv = 1.0f / l;
+    const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 o = oacc[dt][qt] * inv;
+      *(u32x2*)(p.out + r * HD + dt * 16 + g * 4) =
+          u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+    if (p.lse && g == 0) p.lse[r] = m_run[qt] + __builtin_amdgcn_logf(l);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// host side
+
+size_t lds_bytes(int NK) {
+  return (size_t)NSTAGE * STAGE_BYTES + (size_t)((NK + 15) & ~15) +
+         (size_t)NK * sizeof(uint16_t);
+}
+
+template <int BLK, bool FP8, bool BITMAP>
+bsa_status launch(const FwdParams& p, hipStream_t stream) {
+  auto kern = bsa_fwd_kernel<BLK, FP8, BITMAP>;
+  const size_t lds = lds_bytes(p.NK);
+  if (lds > 65536) {
+    if (hipFuncSetAttribute((const void*)kern,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+      return BSA_ERR_HIP;
+  }
+  hipLaunchKernelGGL(kern, dim3(p.n_units), dim3(BLK * 2), lds, stream, p);
+  return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+template <bool BITMAP>
+bsa_status dispatch(const FwdParams& p, int block, bool fp8, hipStream_t s) {
+  if (block == 64)
+    return fp8 ? launch<64, true, BITMAP>(p, s) : launch<64, false, BITMAP>(p, s);
+  return fp8 ? launch<128, true, BITMAP>(p, s) : launch<128, false, BITMAP>(p, s);
+}
+
+bool aligned16(const void* x) { return ((uintptr_t)x & 15u) == 0; }
+
+// Static checks shared by both forms.
+bsa_status check_common(const void* q, const void* k, const void* v,
+                        int32_t kv_dtype, const float* k_scale,
+                        const float* v_scale, const void* out, int32_t B,
+                        int32_t H, int32_t S, int32_t D, int32_t block) {
+  if (!q || !k || !v || !out) return BSA_ERR_NULL;
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || block <= 0) return BSA_ERR_SHAPE;
+  if (S % block != 0) return BSA_ERR_SHAPE;
+  if (D != HD) return BSA_ERR_UNSUPPORTED;
+  if (block != 64 && block != 128) return BSA_ERR_UNSUPPORTED;
+  if (kv_dtype != BSA_KV_BF16 && kv_dtype != BSA_KV_FP8E4M3)
+    return BSA_ERR_UNSUPPORTED;
+  if (kv_dtype == BSA_KV_FP8E4M3 && (!k_scale || !v_scale)) return BSA_ERR_NULL;
+  if (S / block > BSA_MAX_KEY_BLOCKS) return BSA_ERR_UNSUPPORTED;
+  const int64_t units = (int64_t)B * H * (S / block);
+  if (units > INT32_MAX || (int64_t)B * H * S > INT32_MAX)
+    return BSA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return BSA_ERR_ALIGN;
+  return BSA_OK;
+}
+
+FwdParams make_params(const void* q, const void* k, const void* v,
+                      const float* k_scale, const float* v_scale,
+                      const int32_t* vbs, float sm_scale, void* out, float* lse,
+                      int32_t B, int32_t H, int32_t S, int32_t block) {
+  FwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = k;
+  p.v = v;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.vbs = vbs;
+  p.out = (uint16_t*)out;
+  p.lse = lse;
+  p.c = sm_scale * LOG2E;
+  p.H = H;
+  p.S = S;
+  p.NK = S / block;
+  p.n_units = B * H * (S / block);
+  return p;
+}
+
+}  // namespace
+
+extern "C" bsa_status bsa_fwd_lut(const void* q, const void* k, const void* v,
+                                  int32_t kv_dtype, const float* k_scale,
+                                  const float* v_scale, const int32_t* q2k_idx,
+                                  const int32_t* q2k_num, int32_t max_kv,
+                                  int64_t meta_stride_b, int64_t meta_stride_h,
+                                  const int32_t* variable_block_sizes,
+                                  float sm_scale, void* out, float* lse,
+                                  int32_t B, int32_t H, int32_t S, int32_t D,
+                                  int32_t block, void* stream) {
+  bsa_status st =
+      check_common(q, k, v, kv_dtype, k_scale, v_scale, out, B, H, S, D, block);
+  if (st != BSA_OK) return st;
+  if (!q2k_idx || !q2k_num) return BSA_ERR_NULL;
+  if (max_kv < 1 || meta_stride_b < 0 || meta_stride_h < 0) return BSA_ERR_SHAPE;
+  FwdParams p = make_params(q, k, v, k_scale, v_scale, variable_block_sizes,
+                            sm_scale, out, lse, B, H, S, block);
+  p.idx = q2k_idx;
+  p.num = q2k_num;
+  p.max_kv = max_kv;
+  p.meta_sb = meta_stride_b;
+  p.meta_sh = meta_stride_h;
+  return dispatch<false>(p, block, kv_dtype == BSA_KV_FP8E4M3,
+                         (hipStream_t)stream);
+}
+
+extern "C" bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v,
+                                     int32_t kv_dtype, const float* k_scale,
+                                     const float* v_scale, const int8_t* mask,
+                                     int64_t mask_stride_b, int64_t mask_stride_h,
+                                     const int32_t* variable_block_sizes,
+                                     float sm_scale, void* out, float* lse,
+                                     int32_t B, int32_t H, int32_t S, int32_t D,
+                                     int32_t block, void* stream) {
+  bsa_status st =
+      check_common(q, k, v, kv_dtype, k_scale, v_scale, out, B, H, S, D, block);
+  if (st != BSA_OK) return st;
+  if (!mask) return BSA_ERR_NULL;
+  if (mask_stride_b < 0 || mask_stride_h < 0) return BSA_ERR_SHAPE;
+  FwdParams p = make_params(q, k, v, k_scale, v_scale, variable_block_sizes,
+                            sm_scale, out, lse, B, H, S, block);
+  p.mask = mask;
+  p.meta_sb = mask_stride_b;
+  p.meta_sh = mask_stride_h;
+  return dispatch<true>(p, block, kv_dtype == BSA_KV_FP8E4M3,
+                        (hipStream_t)stream);
+}
+
+extern "C" const char* bsa_status_str(int32_t status) {
+  switch (status) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_NULL: return "a required pointer is NULL";
+    case BSA_ERR_SHAPE: return "invalid size (<= 0, or S not a multiple of block)";
+    case BSA_ERR_UNSUPPORTED:
+      return "unsupported configuration (D != 128, block not 64/128, "
+             "too many key blocks, or unknown kv dtype)";
+    case BSA_ERR_ALIGN: return "q, k, v or out is not 16-byte aligned";
+    case BSA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}

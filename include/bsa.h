@@ -1,0 +1,140 @@
+/*
+ * bsa.h -- C ABI of the MI355X (gfx950) block-sparse attention forward.
+ *
+ * One work unit is the `block` query rows of query block qb of head h of
+ * batch b.  It attends only to the keys of its selected key blocks, given
+ * either as a per-row look-up table (`q2k_idx` with a per-row count
+ * `q2k_num`, the VSA form of FastVideo "block_sparse_attn_sm100a.py") or as
+ * an i8 bitmap `mask[q_block, k_block]` (the Jenga form of rocke
+ * "sparse_attention.py", module docstring: nonzero = attend).  Keys at or
+ * past a key block's `variable_block_sizes` entry are masked.  The pass
+ * returns O and a per-row base-2 log-sum-exp (FastVideo
+ * "block_sparse_attn_sm100a.py", module docstring: lse = max(qk*qk_scale) +
+ * log2(l), [B, H, S] fp32):
+ *
+ *   t_j   = (q . k_j) * sm_scale * log2(e)          over attended keys j
+ *   O     = sum_j 2^(t_j - m) v_j / sum_j 2^(t_j - m),   m = max_j t_j
+ *   LSE   = m + log2(sum_j 2^(t_j - m))
+ *
+ * A row with no attended key gets O = +0 exactly and LSE = BSA_LSE_EMPTY
+ * (`is_supported` docstring of the same page: count-0 rows give exactly-zero
+ * output and a finite LSE sentinel).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers.  The caller allocates and owns
+ *    every buffer and keeps it alive until the work on `stream` completes.
+ *    The library allocates no device memory, keeps no state between calls
+ *    and is re-entrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    The call only enqueues work; it never synchronises.
+ *  - Validation is static only (shapes, pointers, alignment); no device
+ *    memory is read on the host.  On any error the status is returned,
+ *    nothing is launched and `out`/`lse` are left untouched.
+ *  - Device-side metadata is not validated; out-of-range values have the
+ *    defined behaviour listed with each argument (no out-of-bounds access).
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <float.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* LSE of a query row that attends to no key: the lowest finite float, a
+ * finite stand-in for log2(0) that carries weight 0 when partial results are
+ * merged. */
+#define BSA_LSE_EMPTY (-FLT_MAX)
+
+/* Largest supported number of key blocks S/block (LDS holds one byte and
+ * one 16-bit list entry per key block per work unit). */
+#define BSA_MAX_KEY_BLOCKS 16384
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  BSA_ERR_SHAPE = 2,       /* a size is <= 0 or S is not a multiple of block  */
+  BSA_ERR_UNSUPPORTED = 3, /* valid but not built: D != 128, block not 64/128,
+                              too many key blocks, unknown kv dtype           */
+  BSA_ERR_ALIGN = 4,       /* q, k, v or out not 16-byte aligned              */
+  BSA_ERR_HIP = 5          /* the HIP launch reported an error                */
+} bsa_status;
+
+typedef enum {
+  BSA_KV_BF16 = 0,   /* K and V are bf16 [B, H, S, D]                          */
+  BSA_KV_FP8E4M3 = 1 /* K and V are OCP fp8 e4m3 ("fn") bytes [B, H, S, D],
+                        each key block dequantised as code value times its
+                        fp32 scale (rocke "sage_attention.py", module
+                        docstring: K/V dequantised per block before the score
+                        and the PV product)                                   */
+} bsa_kv_dtype;
+
+/*
+ * bsa_fwd_lut -- VSA (look-up-table) form.
+ *
+ *  q            bf16 [B, H, S, D], contiguous (BHSD), 16-byte aligned.
+ *  k, v         [B, H, S, D] contiguous, bf16 or fp8 e4m3 per kv_dtype,
+ *               16-byte aligned.
+ *  kv_dtype     a bsa_kv_dtype value.
+ *  k_scale,     fp32 [B, H, S/block]: per-(b, h, key block) scales; required
+ *  v_scale      for BSA_KV_FP8E4M3, ignored (may be NULL) for bf16.
+ *  q2k_idx      int32 rows x max_kv: selected key-block indices of a row.
+ *               Only entries below the row's count are read.  Entries
+ *               outside [0, S/block) are skipped; order and repetitions do
+ *               not matter (the row is a set).
+ *  q2k_num      int32 per row: the count, clamped to [0, max_kv].
+ *  max_kv       row length of q2k_idx (>= 1).
+ *  meta_stride_b, meta_stride_h
+ *               the metadata row of unit (b, h, qb) is
+ *               b*meta_stride_b + h*meta_stride_h + qb (in rows).
+ *               (H*S/block, S/block) = one row per unit; (0, 0) = one
+ *               [S/block, max_kv] table shared by every batch and head.
+ *  variable_block_sizes
+ *               int32 [S/block] shared by every batch and head: valid keys
+ *               of each key block, clamped to [0, block]; keys at or past it
+ *               are masked.  NULL = every block full.
+ *  sm_scale     natural-log softmax scale (1/sqrt(D) is the usual value).
+ *  out          bf16 [B, H, S, D] contiguous, 16-byte aligned; every element
+ *               is written.
+ *  lse          fp32 [B, H, S] base-2 LSE, or NULL to skip it.
+ *  B, H, S, D   sizes; D must be 128, S a multiple of block.
+ *  block        64 or 128: the query-block and key-block size.
+ *  stream       hipStream_t (void*), NULL = null stream.
+ */
+bsa_status bsa_fwd_lut(const void* q, const void* k, const void* v,
+                       int32_t kv_dtype, const float* k_scale,
+                       const float* v_scale, const int32_t* q2k_idx,
+                       const int32_t* q2k_num, int32_t max_kv,
+                       int64_t meta_stride_b, int64_t meta_stride_h,
+                       const int32_t* variable_block_sizes, float sm_scale,
+                       void* out, float* lse, int32_t B, int32_t H, int32_t S,
+                       int32_t D, int32_t block, void* stream);
+
+/*
+ * bsa_fwd_bitmap -- Jenga (bitmap) form.  Arguments as bsa_fwd_lut, except:
+ *
+ *  mask         int8 rows x (S/block): nonzero = the key block is attended
+ *               (rocke "sparse_attention.py", module docstring).
+ *  mask_stride_b, mask_stride_h
+ *               the mask row of unit (b, h, qb) is
+ *               b*mask_stride_b + h*mask_stride_h + qb (in rows);
+ *               (0, 0) = one [S/block, S/block] mask for every batch and head.
+ */
+bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v,
+                          int32_t kv_dtype, const float* k_scale,
+                          const float* v_scale, const int8_t* mask,
+                          int64_t mask_stride_b, int64_t mask_stride_h,
+                          const int32_t* variable_block_sizes, float sm_scale,
+                          void* out, float* lse, int32_t B, int32_t H,
+                          int32_t S, int32_t D, int32_t block, void* stream);
+
+/* Static text of a status code (never NULL). */
+const char* bsa_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

@@ -1,0 +1,107 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/bsa.h declares, and rejects invalid static arguments before any HIP
+call (no compute is launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_tile_amd import _lib, api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # dynamic symbol table, independent of ctypes
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    for s in range(6):
+        assert api.bsa_status_str(s)
+    assert api.bsa_status_str(99) == "unknown status"
+
+
+# Fake, 16-byte aligned device addresses: validation fails before anything
+# is dereferenced or launched.
+A = 0x10000
+
+
+def lut(**over):
+    args = dict(q=A, k=A, v=A, kv=0, ks=None, vs=None, idx=A, num=A, max_kv=4,
+                sb=8, sh=8, vbs=None, scale=0.1, out=A, lse=None, B=1, H=1,
+                S=512, D=128, block=64, stream=None)
+    args.update(over)
+    return _lib.load().bsa_fwd_lut(*args.values())
+
+
+def bitmap(**over):
+    args = dict(q=A, k=A, v=A, kv=0, ks=None, vs=None, mask=A, sb=8, sh=8,
+                vbs=None, scale=0.1, out=A, lse=None, B=1, H=1, S=512, D=128,
+                block=64, stream=None)
+    args.update(over)
+    return _lib.load().bsa_fwd_bitmap(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), api.BSA_ERR_NULL),
+    (dict(k=None), api.BSA_ERR_NULL),
+    (dict(v=None), api.BSA_ERR_NULL),
+    (dict(out=None), api.BSA_ERR_NULL),
+    (dict(idx=None), api.BSA_ERR_NULL),
+    (dict(num=None), api.BSA_ERR_NULL),
+    (dict(kv=1), api.BSA_ERR_NULL),             # fp8 without scales
+    (dict(kv=1, ks=A), api.BSA_ERR_NULL),
+    (dict(B=0), api.BSA_ERR_SHAPE),
+    (dict(H=-1), api.BSA_ERR_SHAPE),
+    (dict(S=500), api.BSA_ERR_SHAPE),           # not a multiple of block
+    (dict(max_kv=0), api.BSA_ERR_SHAPE),
+    (dict(sb=-1), api.BSA_ERR_SHAPE),
+    (dict(D=64), api.BSA_ERR_UNSUPPORTED),
+    (dict(block=32, S=512), api.BSA_ERR_UNSUPPORTED),
+    (dict(block=256, S=512), api.BSA_ERR_UNSUPPORTED),
+    (dict(kv=7), api.BSA_ERR_UNSUPPORTED),
+    (dict(S=64 * 16385), api.BSA_ERR_UNSUPPORTED),  # > BSA_MAX_KEY_BLOCKS
+    (dict(q=A + 8), api.BSA_ERR_ALIGN),
+    (dict(out=A + 2), api.BSA_ERR_ALIGN),
+])
+def test_lut_rejects_invalid_static_arguments(over, status):
+    assert lut(**over) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(mask=None), api.BSA_ERR_NULL),
+    (dict(q=None), api.BSA_ERR_NULL),
+    (dict(S=100), api.BSA_ERR_SHAPE),
+    (dict(sh=-3), api.BSA_ERR_SHAPE),
+    (dict(D=256), api.BSA_ERR_UNSUPPORTED),
+    (dict(v=A + 4), api.BSA_ERR_ALIGN),
+])
+def test_bitmap_rejects_invalid_static_arguments(over, status):
+    assert bitmap(**over) == status
+
+
+def test_python_binding_checks_dtypes_before_calling():
+    import torch
+    q = torch.zeros((1, 1, 64, 128), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        api.bsa_fwd_lut(q, q, q, torch.zeros((1, 1), dtype=torch.int32),
+                        torch.zeros((1,), dtype=torch.int32), block=64)

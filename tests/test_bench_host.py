@@ -1,0 +1,50 @@
+"""Host-side logic of bench.py (CPU): the exact attended-pair count that the
+effective-FLOP metric divides by agrees with the oracle's integer decode."""
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import workloads
+
+
+def _oracle_pairs(w, units=None):
+    kw = dict(B=w.B, H=w.H, S=w.S, block=w.block, vbs=w.vbs, units=units)
+    if w.form == "lut":
+        c = oracle.key_counts(q2k_idx=w.q2k_idx, q2k_num=w.q2k_num,
+                              meta_strides=w.meta_strides, **kw)
+    else:
+        c = oracle.key_counts(mask=w.mask, mask_strides=w.mask_strides, **kw)
+    return int(c.astype(np.int64).sum()) * w.block
+
+
+@pytest.mark.parametrize("kw", [
+    dict(seed=1, S=512, block=64, count_mode="uniform", vbs_mode="random"),
+    dict(seed=2, S=512, block=128, form="bitmap", density=0.4,
+         vbs_mode="zero_some"),
+    dict(seed=3, S=512, block=64, shared_meta=True, density=0.5),
+    dict(seed=4, S=512, block=64, max_kv=3, count_mode="uniform",
+         pad_value=99),
+])
+def test_attended_pairs_matches_oracle_decode(kw):
+    kw = dict(kw)
+    w = workloads.make_random(kw.pop("seed"), B=2, H=3, **kw)
+    assert bench.attended_pairs(w) == _oracle_pairs(w)
+    units = [0, 3, 7, w.n_units - 1]
+    assert bench.attended_pairs(w, units) == _oracle_pairs(w, units)
+
+
+def test_tiny_named_workload_pair_count_closed_form():
+    w = workloads.make_config(0)
+    # 8 q-blocks x 4 selected blocks; block 7 has 40 valid keys, others 64
+    sel = bench.selected_matrix(w).numpy()
+    want = sum(64 * (40 if kb == 7 else 64)
+               for u in range(8) for kb in range(8) if sel[u, kb])
+    assert bench.attended_pairs(w) == want == _oracle_pairs(w)
+
+
+def test_multi_gpu_request_exits_with_message(monkeypatch, capsys):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
+    assert bench.main() == 2
+    assert "one GPU" in capsys.readouterr().err

@@ -1,0 +1,213 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, element by element.  Tolerances: O max-abs 1e-2, LSE
+(base 2) 1e-3 absolute; rows with no attended key bit-exact (+0 and the
+sentinel).  Outputs are pre-filled with NaN so unwritten elements fail."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_tile_amd as bsa
+import workloads
+from tests.gpu_helpers import check, gather_units, log, run_gpu, run_oracle, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+SMALL = [
+    # (label, make_random kwargs)
+    ("lut64_half", dict(seed=101, B=1, H=2, S=512, block=64, density=0.5)),
+    ("lut64_full_dense", dict(seed=102, B=2, H=1, S=256, block=64, density=1.0)),
+    ("lut64_vbs_random", dict(seed=103, B=1, H=3, S=768, block=64,
+                              count_mode="uniform", vbs_mode="random")),
+    ("lut64_vbs_zero_some", dict(seed=104, B=2, H=2, S=512, block=64,
+                                 count_mode="uniform", vbs_mode="zero_some")),
+    ("lut128_uniform", dict(seed=105, B=1, H=2, S=1024, block=128,
+                            count_mode="uniform", vbs_mode="partial")),
+    ("lut128_dense", dict(seed=106, B=1, H=1, S=512, block=128, density=1.0)),
+    ("lut64_maxkv1", dict(seed=107, B=1, H=2, S=512, block=64, max_kv=1,
+                          count_mode="uniform")),
+    ("lut64_shared_meta", dict(seed=108, B=2, H=3, S=512, block=64,
+                               shared_meta=True, density=0.4,
+                               vbs_mode="partial")),
+    ("lut64_count_zero", dict(seed=109, B=1, H=2, S=256, block=64,
+                              count_mode="zero")),
+    ("lut64_one_block", dict(seed=110, B=1, H=2, S=64, block=64, density=1.0,
+                             vbs_mode="partial")),
+    ("lut64_std3", dict(seed=111, B=1, H=2, S=512, block=64, density=0.5,
+                        std=3.0, vbs_mode="partial")),
+    ("bitmap64", dict(seed=112, B=1, H=2, S=512, block=64, form="bitmap",
+                      density=0.5, vbs_mode="random")),
+    ("bitmap128_shared", dict(seed=113, B=2, H=2, S=1024, block=128,
+                              form="bitmap", shared_meta=True, density=0.3)),
+    ("fp8_lut64", dict(seed=114, B=1, H=2, S=512, block=64, kv="fp8",
+                       density=0.5, vbs_mode="partial")),
+    ("fp8_lut128", dict(seed=115, B=2, H=1, S=512, block=128, kv="fp8",
+                        count_mode="uniform", vbs_mode="random")),
+    ("fp8_bitmap64", dict(seed=116, B=1, H=2, S=512, block=64, kv="fp8",
+                          form="bitmap", density=0.6)),
+    ("lut64_long_nk1024", dict(seed=117, B=1, H=1, S=65536, block=64,
+                               max_kv=40, density=0.0006, count_mode="uniform",
+                               vbs_mode="partial")),
+]
+
+
+@pytest.mark.parametrize("label,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_random_parity(label, kw):
+    kw = dict(kw)
+    w = workloads.make_random(kw.pop("seed"), **kw)
+    log(f"[parity] {label} B{w.B} H{w.H} S{w.S} blk{w.block} form={w.form} "
+        f"fp8={w.kv_fp8}")
+    out, lse = run_gpu(w)
+    units = None
+    if w.n_units > 64:
+        units = sorted(set(np.linspace(0, w.n_units - 1, 48).astype(int).tolist()))
+    o_ref, l_ref = run_oracle(w, units=units)
+    if units is None:
+        o_gpu = out.float().cpu().numpy()
+        l_gpu = lse.cpu().numpy()
+    else:
+        o_gpu, l_gpu = gather_units(w, out, lse, units)
+    # inputs scaled by 3 give |O| up to ~7, where bf16 output rounding alone
+    # exceeds 1e-2: add the half-ulp of the output to the bound
+    check(o_gpu, l_gpu, o_ref, l_ref, label,
+          o_rel=2.0 ** -8 if kw.get("std", 1.0) > 1.0 else 0.0)
+
+
+def test_tiny_named_workload_full_parity():
+    w = workloads.make_config(0)
+    log(f"[parity] {w.name} (every element)")
+    out, lse = run_gpu(w)
+    o_ref, l_ref = run_oracle(w)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, w.name)
+
+
+def _sample_units(w, n=24, seed=0):
+    g = np.random.default_rng(seed)
+    units = set([0, w.n_units - 1, w.n_units // 2])
+    units.update(g.choice(w.n_units, size=n, replace=False).tolist())
+    if w.form == "lut":
+        # include rows with count 0 when the workload has them
+        sb, sh = w.meta_strides
+        zeros = []
+        for u in range(w.n_units):
+            qb = u % w.NQ
+            h = (u // w.NQ) % w.H
+            b = u // (w.NQ * w.H)
+            if int(w.q2k_num[b * sb + h * sh + qb]) == 0:
+                zeros.append(u)
+            if len(zeros) >= 3:
+                break
+        units.update(zeros)
+    return sorted(units)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_named_workload_sampled_parity(cfg):
+    """Full-size named workloads, launched exactly as the benchmark launches
+    them; the oracle computes a sample of work units one by one."""
+    w = workloads.make_config(cfg)
+    log(f"[parity] {w.name}: B{w.B} H{w.H} S{w.S} blk{w.block} "
+        f"units={w.n_units}")
+    out, lse = run_gpu(w)
+    units = _sample_units(w, seed=cfg)
+    log(f"  oracle on {len(units)} sampled units")
+    o_ref, l_ref = run_oracle(w, units=units)
+    o_gpu, l_gpu = gather_units(w, out, lse, units)
+    check(o_gpu, l_gpu, o_ref, l_ref, w.name)
+    # whole-output properties that hold at any size
+    assert not torch.isnan(out).any().item(), "unwritten or NaN output"
+    assert not torch.isnan(lse).any().item(), "unwritten or NaN lse"
+    assert torch.isfinite(lse).all().item()
+
+
+def test_need_lse_false_gives_same_output_and_leaves_lse_alone():
+    w = workloads.make_random(201, B=1, H=2, S=512, block=64,
+                              count_mode="uniform", vbs_mode="partial")
+    log("[parity] need_lse=False")
+    out1, _ = run_gpu(w)
+    out2, _ = run_gpu(w, need_lse=False)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+def test_gpu_result_is_bitwise_invariant_to_lut_order_padding_duplicates():
+    w = workloads.make_random(202, B=1, H=2, S=1024, block=64, max_kv=10,
+                              count_mode="uniform", vbs_mode="random")
+    log("[parity] LUT order / padding / duplicate invariance")
+    out1, lse1 = run_gpu(w)
+    idx = w.q2k_idx.clone()
+    num = w.q2k_num.clone()
+    g = torch.Generator().manual_seed(3)
+    wide = torch.full((idx.shape[0], idx.shape[1] + 2), -7, dtype=torch.int32)
+    for r in range(idx.shape[0]):
+        n = int(num[r])
+        row = idx[r, :n][torch.randperm(n, generator=g)]
+        extra = [int(row[0])] if n > 0 else []
+        extra.append(w.NQ + 11)  # out of range below the count: skipped
+        full = torch.cat([row, torch.tensor(extra, dtype=torch.int32)])
+        wide[r, :len(full)] = full
+        garbage = [2**31 - 1, -2**31, 5, w.NQ, -1]
+        npad = wide.shape[1] - len(full)
+        wide[r, len(full):] = torch.tensor(
+            [garbage[i % len(garbage)] for i in range(npad)], dtype=torch.int32)
+        num[r] = len(full)
+    w.q2k_idx, w.q2k_num = wide.contiguous(), num
+    out2, lse2 = run_gpu(w)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+
+
+def test_bitmap_form_is_bitwise_equal_to_compacted_lut():
+    w = workloads.make_random(203, B=2, H=2, S=1024, block=64, form="bitmap",
+                              density=0.35, vbs_mode="random")
+    log("[parity] bitmap == compacted LUT")
+    out1, lse1 = run_gpu(w)
+    m = w.mask.numpy()
+    idx = np.full(m.shape, -1, dtype=np.int32)
+    num = np.zeros(m.shape[0], dtype=np.int32)
+    for r in range(m.shape[0]):
+        nz = np.nonzero(m[r])[0]
+        idx[r, :len(nz)] = nz
+        num[r] = len(nz)
+    w.form = "lut"
+    w.q2k_idx = torch.from_numpy(idx)
+    w.q2k_num = torch.from_numpy(num)
+    w.meta_strides = w.mask_strides
+    out2, lse2 = run_gpu(w)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+
+
+def test_out_of_range_counts_and_vbs_are_clamped_like_the_oracle():
+    w = workloads.make_random(204, B=1, H=2, S=512, block=64, max_kv=5,
+                              count_mode="uniform")
+    num = w.q2k_num.clone()
+    num[::3] = 1000   # above max_kv: clamped
+    num[1::5] = -4    # negative: empty row
+    w.q2k_num = num
+    w.vbs = torch.tensor([64, 1000, -5, 65, 3, 0, 64, 200], dtype=torch.int32)
+    log("[parity] clamped counts and vbs")
+    out, lse = run_gpu(w)
+    o_ref, l_ref = run_oracle(w)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref,
+          "clamped")
+
+
+def test_invalid_static_arguments_raise_and_write_nothing():
+    w = workloads.make_random(205, B=1, H=1, S=256, block=64)
+    d = to_dev(w)
+    out = torch.full(tuple(w.q.shape), 7.0, dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.full((1, 1, 256), 7.0, device="cuda")
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_fwd_lut(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"],
+                        block=32, out=out, lse=lse)
+    assert e.value.status == bsa.BSA_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert (out.float() == 7.0).all().item() and (lse == 7.0).all().item()
