@@ -46,15 +46,18 @@
 
 namespace {
 
-constexpr int HD = 128;             // head dimension
-constexpr int KT = 32;              // keys per pipeline tile
-constexpr int KPITCH = HD + 8;      // K tile row pitch in bf16 (272 B)
-constexpr int VPITCH = HD + 16;     // V tile row pitch in bf16 (288 B)
-constexpr int K_TILE_BYTES = KT * KPITCH * 2;
-constexpr int V_TILE_BYTES = KT * VPITCH * 2;
-constexpr int STAGE_BYTES = K_TILE_BYTES + V_TILE_BYTES;
+constexpr int HD = 128;                 // head dimension
+constexpr int KT = 32;                  // keys per pipeline tile
+constexpr int ROWB = HD * 2;            // bytes of one bf16 row in LDS
+constexpr int TILE_BYTES = KT * ROWB;   // one K or V tile (8 KB)
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 constexpr int NSTAGE = 2;
 constexpr float LOG2E = 1.4426950408889634f;
+// Lazy rescaling: the running reference m of a row is only raised when a
+// tile's maximum exceeds it by more than TAU (log2 units), so weights stay
+// below 2^TAU and the accumulator is rescaled rarely.  Any reference gives
+// the same O and LSE in exact arithmetic.
+constexpr float TAU = 8.0f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -65,6 +68,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct FwdParams {
   const uint16_t* q;
@@ -104,6 +108,19 @@ __device__ __forceinline__ int remap_unit(int bid, int n) {
   return (bid % 8) * (n / 8) + bid / 8;
 }
 
+// LDS tile layout: 32 rows of 256 B, 16-byte chunks XOR-swizzled per row so
+// that the MFMA operand reads are free of bank conflicts without padding.
+// K tiles are read row-wise (16 rows x one chunk per 16 lanes): chunk c of
+// row r sits at position c ^ (r & 15).  V tiles are read through the
+// transposing LDS read (8 rows x 4 half-chunks per 32 lanes): position
+// c ^ ((r & 7) << 1).
+__device__ __forceinline__ int k_off(int r, int c) {
+  return r * ROWB + ((c ^ (r & 15)) << 4);
+}
+__device__ __forceinline__ int v_off(int r, int c) {
+  return r * ROWB + ((c ^ ((r & 7) << 1)) << 4);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2 f = {a, b};
   bf16x2 r = __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, RNE
@@ -120,17 +137,31 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
-__device__ __forceinline__ float wave_max_groups(float x) {
-  // lanes l, l^16, l^32, l^48 hold the same query row
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Reductions over the four lanes l, l^16, l^32, l^48 (the lanes that hold
+// one query row), with the gfx950 cross-row lane swaps (no LDS traffic).
+__device__ __forceinline__ float group_max(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-
-__device__ __forceinline__ float wave_sum_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+__device__ __forceinline__ float group_min(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  x = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Position of one pipeline tile: entry e of the selected-block list, first
@@ -139,16 +170,16 @@ struct Tile {
   int e, kb, t0, nv;
 };
 
-template <int BLK>
-__device__ __forceinline__ Tile tile_at_entry(const uint16_t* list,
-                                              const int32_t* vbs, int e,
+// The selected-block list holds (kb << 8) | nv per entry, nv = valid keys.
+__device__ __forceinline__ Tile tile_at_entry(const uint32_t* list, int e,
                                               int nsel) {
   Tile t;
   t.e = e;
   t.t0 = 0;
   if (e < nsel) {
-    t.kb = __builtin_amdgcn_readfirstlane((int)list[e]);
-    t.nv = __builtin_amdgcn_readfirstlane(block_valid<BLK>(vbs, t.kb));
+    const uint32_t x = __builtin_amdgcn_readfirstlane(list[e]);
+    t.kb = (int)(x >> 8);
+    t.nv = (int)(x & 255u);
   } else {
     t.kb = 0;
     t.nv = 0;
@@ -156,49 +187,78 @@ __device__ __forceinline__ Tile tile_at_entry(const uint16_t* list,
   return t;
 }
 
-template <int BLK>
-__device__ __forceinline__ Tile next_tile(const Tile& cur, const uint16_t* list,
-                                          const int32_t* vbs, int nsel) {
+__device__ __forceinline__ Tile next_tile(const Tile& cur, const uint32_t* list,
+                                          int nsel) {
   if (cur.t0 + KT < cur.nv) {
     Tile t = cur;
     t.t0 += KT;
     return t;
   }
-  return tile_at_entry<BLK>(list, vbs, cur.e + 1, nsel);
+  return tile_at_entry(list, cur.e + 1, nsel);
 }
 
-// Per-thread staging registers for one K/V tile.
-template <bool FP8, int NT>
-struct Staging {
-  // bf16: 32 rows x 16 chunks of 16 B for each of K, V.
-  // fp8 : 32 rows x  8 chunks of 16 B for each of K, V.
-  static constexpr int CHUNKS_PER_ROW = FP8 ? 8 : 16;
-  static constexpr int CHUNKS = KT * CHUNKS_PER_ROW;
+// One direct global->LDS load of 16 B per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at LDS address lds_base + 16*l.  Issued as inline
+// assembly so that the compiler does not track it; the loop waits for these
+// loads explicitly (vmcnt) before the barrier that publishes a tile, and the
+// reads of the other stage may proceed while they are in flight.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(lds_base), "v"(gaddr)
+      : "memory", "m0");
+}
+
+// bf16 K/V: the valid rows of a tile go straight from global memory into
+// LDS, no VGPR staging.  One instruction moves 64 lanes x 16 B = 4 rows;
+// lane l fills LDS position (l & 15) of row 4j + l/16, i.e. it loads the
+// chunk that the swizzle puts there.  Rows at or past the valid count are not
+// loaded (their stale LDS contents meet a zero probability or a masked
+// score).
+template <int NW>
+__device__ __forceinline__ void issue_tile_bf16(const char* kg, const char* vg,
+                                                uint32_t stage_lds, int nvt,
+                                                int wave, int lane) {
+#pragma unroll
+  for (int j = wave; j < KT / 4; j += NW) {
+    const int r = 4 * j + (lane >> 4);
+    const int pos = lane & 15;
+    const uint32_t kdst = __builtin_amdgcn_readfirstlane(stage_lds + j * 1024);
+    const uint32_t vdst =
+        __builtin_amdgcn_readfirstlane(stage_lds + TILE_BYTES + j * 1024);
+    if (r < nvt) {
+      const int ck = pos ^ (r & 15);
+      const int cv = pos ^ ((r & 7) << 1);
+      dma16(kg + r * ROWB + ck * 16, kdst);
+      dma16(vg + r * ROWB + cv * 16, vdst);
+    }
+  }
+}
+
+// fp8 K/V: 16 codes per 16-byte load, widened to bf16 in registers and
+// stored into the same swizzled bf16 layout.
+template <int NT>
+struct Fp8Staging {
+  static constexpr int CHUNKS = KT * 8;  // 32 rows x 8 chunks of 16 codes
   static constexpr int PER_THREAD = CHUNKS / NT;
   static_assert(CHUNKS % NT == 0, "tile chunks must divide evenly");
   u32x4 kr[PER_THREAD];
   u32x4 vr[PER_THREAD];
 };
 
-template <bool FP8, int NT>
-__device__ __forceinline__ void load_tile(Staging<FP8, NT>& st, const void* kg,
-                                          const void* vg, int64_t plane_elems,
-                                          const Tile& t, int BLKv, int tid) {
-  constexpr int CPR = Staging<FP8, NT>::CHUNKS_PER_ROW;
-  constexpr int EB = FP8 ? 1 : 2;  // bytes per element
-  const int64_t key0 = (int64_t)t.kb * BLKv + t.t0;
-  const char* kb = (const char*)kg + (plane_elems + key0 * HD) * EB;
-  const char* vb = (const char*)vg + (plane_elems + key0 * HD) * EB;
-  const int nvt = t.nv - t.t0;  // valid rows in this tile (may exceed KT)
+template <int NT>
+__device__ __forceinline__ void load_tile_fp8(Fp8Staging<NT>& st, const char* kg,
+                                              const char* vg, int nvt, int tid) {
 #pragma unroll
-  for (int i = 0; i < Staging<FP8, NT>::PER_THREAD; ++i) {
+  for (int i = 0; i < Fp8Staging<NT>::PER_THREAD; ++i) {
     const int c = tid + i * NT;
-    const int row = c / CPR;
-    const int col = c % CPR;
-    if (row < nvt) {
-      const int64_t off = (int64_t)row * HD * EB + col * 16;
-      st.kr[i] = *(const u32x4*)(kb + off);
-      st.vr[i] = *(const u32x4*)(vb + off);
+    const int r = c >> 3;
+    const int col = c & 7;
+    if (r < nvt) {
+      st.kr[i] = *(const u32x4*)(kg + r * HD + col * 16);
+      st.vr[i] = *(const u32x4*)(vg + r * HD + col * 16);
     } else {
       st.kr[i] = u32x4{0, 0, 0, 0};
       st.vr[i] = u32x4{0, 0, 0, 0};
@@ -206,41 +266,38 @@ __device__ __forceinline__ void load_tile(Staging<FP8, NT>& st, const void* kg,
   }
 }
 
-template <bool FP8, int NT>
-__device__ __forceinline__ void store_tile(const Staging<FP8, NT>& st,
-                                           char* stage, int tid) {
-  constexpr int CPR = Staging<FP8, NT>::CHUNKS_PER_ROW;
+template <int NT>
+__device__ __forceinline__ void store_tile_fp8(const Fp8Staging<NT>& st,
+                                               char* stage, int tid) {
   char* ks = stage;
-  char* vs = stage + K_TILE_BYTES;
+  char* vs = stage + TILE_BYTES;
 #pragma unroll
-  for (int i = 0; i < Staging<FP8, NT>::PER_THREAD; ++i) {
+  for (int i = 0; i < Fp8Staging<NT>::PER_THREAD; ++i) {
     const int c = tid + i * NT;
-    const int row = c / CPR;
-    const int col = c % CPR;
-    if constexpr (!FP8) {
-      *(u32x4*)(ks + row * KPITCH * 2 + col * 16) = st.kr[i];
-      *(u32x4*)(vs + row * VPITCH * 2 + col * 16) = st.vr[i];
-    } else {
-      // 16 fp8 codes -> 16 bf16 (32 B)
-      u32x2 k0 = fp8x4_to_bf16x4(st.kr[i].x), k1 = fp8x4_to_bf16x4(st.kr[i].y);
-      u32x2 k2 = fp8x4_to_bf16x4(st.kr[i].z), k3 = fp8x4_to_bf16x4(st.kr[i].w);
-      u32x2 v0 = fp8x4_to_bf16x4(st.vr[i].x), v1 = fp8x4_to_bf16x4(st.vr[i].y);
-      u32x2 v2 = fp8x4_to_bf16x4(st.vr[i].z), v3 = fp8x4_to_bf16x4(st.vr[i].w);
-      char* kd = ks + row * KPITCH * 2 + col * 32;
-      char* vd = vs + row * VPITCH * 2 + col * 32;
-      *(u32x4*)(kd) = u32x4{k0.x, k0.y, k1.x, k1.y};
-      *(u32x4*)(kd + 16) = u32x4{k2.x, k2.y, k3.x, k3.y};
-      *(u32x4*)(vd) = u32x4{v0.x, v0.y, v1.x, v1.y};
-      *(u32x4*)(vd + 16) = u32x4{v2.x, v2.y, v3.x, v3.y};
-    }
+    const int r = c >> 3;
+    const int col = c & 7;  // bf16 chunks 2*col and 2*col+1
+    const u32x2 k0 = fp8x4_to_bf16x4(st.kr[i].x), k1 = fp8x4_to_bf16x4(st.kr[i].y);
+    const u32x2 k2 = fp8x4_to_bf16x4(st.kr[i].z), k3 = fp8x4_to_bf16x4(st.kr[i].w);
+    const u32x2 v0 = fp8x4_to_bf16x4(st.vr[i].x), v1 = fp8x4_to_bf16x4(st.vr[i].y);
+    const u32x2 v2 = fp8x4_to_bf16x4(st.vr[i].z), v3 = fp8x4_to_bf16x4(st.vr[i].w);
+    *(u32x4*)(ks + k_off(r, 2 * col)) = u32x4{k0.x, k0.y, k1.x, k1.y};
+    *(u32x4*)(ks + k_off(r, 2 * col + 1)) = u32x4{k2.x, k2.y, k3.x, k3.y};
+    *(u32x4*)(vs + v_off(r, 2 * col)) = u32x4{v0.x, v0.y, v1.x, v1.y};
+    *(u32x4*)(vs + v_off(r, 2 * col + 1)) = u32x4{v2.x, v2.y, v3.x, v3.y};
   }
 }
 
+// Waits until this wave's outstanding global loads (including the ones
+// writing LDS directly) have completed.
+__device__ __forceinline__ void wait_vm_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
+}
+
 template <int BLK, bool FP8, bool BITMAP>
-__global__ __launch_bounds__(BLK * 2) void bsa_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
   constexpr int NW = BLK / 32;  // waves; each owns 32 query rows
   constexpr int NT = NW * 64;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ int s_nsel;
 
   const int tid = threadIdx.x;
@@ -251,7 +308,7 @@ __global__ __launch_bounds__(BLK * 2) void bsa_fwd_kernel(FwdParams p) {
 
   const int NK = p.NK;
   uint8_t* bmp = (uint8_t*)(smem + NSTAGE * STAGE_BYTES);
-  uint16_t* list = (uint16_t*)(bmp + ((NK + 15) & ~15));
+  uint32_t* list = (uint32_t*)(bmp + ((NK + 15) & ~15));
 
   // ---- A1: work unit
   const int u = remap_unit(blockIdx.x, p.n_units);
@@ -261,6 +318,10 @@ __global__ __launch_bounds__(BLK * 2) void bsa_fwd_kernel(FwdParams p) {
   const int b = bh / p.H;
   const int64_t plane = (int64_t)bh * p.S * HD;  // element offset of (b, h)
   const int64_t row = (int64_t)b * p.meta_sb + (int64_t)h * p.meta_sh + qb;
+
+  // Zero both stages once: rows that are never loaded must hold finite data.
+  for (int i = tid; i < NSTAGE * STAGE_BYTES / 16; i += NT)
+    *(u32x4*)(smem + i * 16) = u32x4{0, 0, 0, 0};
 
   // ---- A2: selected set -> LDS bitmap
   if constexpr (BITMAP) {
@@ -282,10 +343,11 @@ __global__ __launch_bounds__(BLK * 2) void bsa_fwd_kernel(FwdParams p) {
     int base = 0;
     for (int c0 = 0; c0 < NK; c0 += 64) {
       const int kb = c0 + lane;
-      const bool f = kb < NK && bmp[kb] != 0 && block_valid<BLK>(p.vbs, kb) > 0;
+      const int nv = kb < NK ? block_valid<BLK>(p.vbs, kb) : 0;
+      const bool f = kb < NK && bmp[kb] != 0 && nv > 0;
       const uint64_t bal = __ballot(f);
       const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
-      if (f) list[pos] = (uint16_t)kb;
+      if (f) list[pos] = ((uint32_t)kb << 8) | (uint32_t)nv;
       base += __popcll(bal);
     }
     if (lane == 0) s_nsel = base;
@@ -308,6 +370,32 @@ __global__ __launch_bounds__(BLK * 2) void bsa_fwd_kernel(FwdParams p) {
     return;
   }
 
+  const int eb = FP8 ? 1 : 2;  // bytes per K/V element in global memory
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
+  const char* kplane = (const char*)p.k + plane * eb;
+  const char* vplane = (const char*)p.v + plane * eb;
+
+  // ---- A4 prologue: tile 0 into stage 0
+  const int64_t scale_row = (int64_t)bh * NK;  // fp8 scales of (b, h)
+  Tile cur = tile_at_entry(list, 0, nsel);
+  [[maybe_unused]] float ksc_cur = 1.f, vsc_cur = 1.f;
+  if constexpr (FP8) {
+    ksc_cur = p.k_scale[scale_row + cur.kb];
+    vsc_cur = p.v_scale[scale_row + cur.kb];
+  }
+  [[maybe_unused]] Fp8Staging<NT> st;
+  {
+    const int64_t key0 = (int64_t)cur.kb * BLK + cur.t0;
+    if constexpr (FP8) {
+      load_tile_fp8<NT>(st, kplane + key0 * HD, vplane + key0 * HD,
+                        cur.nv - cur.t0, tid);
+      store_tile_fp8<NT>(st, smem, tid);
+    } else {
+      issue_tile_bf16<NW>(kplane + key0 * ROWB, vplane + key0 * ROWB,
+                          smem_lds, cur.nv - cur.t0, wave, lane);
+    }
+  }
+
   // ---- A3: Q operands (B operand of S^T = K Q^T): Q[row r16][d kk*32+g*8..]
   bf16x8 qreg[2][4];
   {
@@ -324,27 +412,37 @@ __global__ __launch_bounds__(BLK * 2) void bsa_fwd_kernel(FwdParams p) {
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-
-  // ---- A4: prologue -- tile 0 into stage 0
-  Staging<FP8, NT> st;
-  Tile cur = tile_at_entry<BLK>(list, p.vbs, 0, nsel);
-  load_tile<FP8, NT>(st, p.k, p.v, plane, cur, BLK, tid);
-  store_tile<FP8, NT>(st, smem, tid);
-  __syncthreads();
-
-  const int64_t scale_row = (int64_t)bh * NK;
+  float m_run[2] = {-INFINITY, -INFINITY};  // reference (log2 units)
+  float l_run[2] = {0.f, 0.f};              // per-lane partial sums
 
   for (int it = 0;; ++it) {
-    const Tile nxt = next_tile<BLK>(cur, list, p.vbs, nsel);
+    // tile `it` complete in LDS for every wave; stage (it+1)&1 free again
+    wait_vm_all();
+    __syncthreads();
+    const Tile nxt = next_tile(cur, list, nsel);
     const bool has_next = nxt.e < nsel;
-    if (has_next) load_tile<FP8, NT>(st, p.k, p.v, plane, nxt, BLK, tid);
+    char* nstage = smem + ((it + 1) & 1) * STAGE_BYTES;
+    [[maybe_unused]] float ksc_nxt = 1.f, vsc_nxt = 1.f;
+    if (has_next) {
+      const int64_t key0 = (int64_t)nxt.kb * BLK + nxt.t0;
+      if constexpr (FP8) {
+        load_tile_fp8<NT>(st, kplane + key0 * HD, vplane + key0 * HD,
+                          nxt.nv - nxt.t0, tid);
+        ksc_nxt = p.k_scale[scale_row + nxt.kb];
+        vsc_nxt = p.v_scale[scale_row + nxt.kb];
+      }
+      else
+        issue_tile_bf16<NW>(kplane + key0 * ROWB, vplane + key0 * ROWB,
+                            smem_lds + ((it + 1) & 1) * STAGE_BYTES,
+                            nxt.nv - nxt.t0, wave, lane);
+    }
 
     const char* ks = smem + (it & 1) * STAGE_BYTES;
-    const char* vs = ks + K_TILE_BYTES;
+    const char* vs = ks + TILE_BYTES;
+    const int nvt = cur.nv - cur.t0;  // valid keys of this tile (>= 1)
 
-    // ---- A5: S^T[key][query] for the 32 keys x 32 queries of this wave
+    // ---- A5: S^T[key][query] for 32 keys x 32 queries of this wave; the
+    // second 16-key half is skipped when it holds no valid key
     f32x4 sacc[2][2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
@@ -352,10 +450,10 @@ __global__ __launch_bounds__(BLK * 2) void bsa_fwd_kernel(FwdParams p) {
       for (int qt = 0; qt < 2; ++qt) sacc[s2][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
+      if (s2 == 1 && nvt <= 16) break;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 kop =
-            *(const bf16x8*)(ks + ((s2 * 16 + r16) * KPITCH + kk * 32 + g * 8) * 2);
+        const bf16x8 kop = *(const bf16x8*)(ks + k_off(s2 * 16 + r16, kk * 4 + g));
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
           sacc[s2][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -365,79 +463,109 @@ __global__ __launch_bounds__(BLK * 2) void bsa_fwd_kernel(FwdParams p) {
 
     // ---- A6: online softmax (exp2 form)
     float cs = p.c;
-    float vsc = 1.f;
+    [[maybe_unused]] float vsc = 1.f;
     if constexpr (FP8) {
-      cs *= p.k_scale[scale_row + cur.kb];
-      vsc = p.v_scale[scale_row + cur.kb];
+      cs *= ksc_cur;
+      vsc = vsc_cur;
     }
-    const int nvt = cur.nv - cur.t0;  // valid keys of this tile (>= 1)
-    bf16x8 pop[2];
+    const bool partial = nvt < KT;
+    // key of element (s2, j) in this tile: s2*16 + 4g + j
+    float tref[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      float x[8];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[s2 * 4 + j] = sacc[s2][qt][j] * cs;
-      if (nvt < KT) {
+      if (cs >= 0.f) {
+        float mx = -INFINITY;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (s2 * 16 + g * 4 + j >= nvt) x[s2 * 4 + j] = -INFINITY;
-      }
-      float mx = x[0];
+          for (int j = 0; j < 4; ++j) {
+            const float x = sacc[s2][qt][j];
+            mx = fmaxf(mx, (!partial || s2 * 16 + 4 * g + j < nvt) ? x : -INFINITY);
+          }
+        tref[qt] = group_max(mx) * cs;
+      } else {
+        float mn = INFINITY;
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-      mx = wave_max_groups(mx);
-      const float mnew = fmaxf(m_run[qt], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mnew);
-      m_run[qt] = mnew;
-      float ps = 0.f;
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = sacc[s2][qt][j];
+            mn = fminf(mn, (!partial || s2 * 16 + 4 * g + j < nvt) ? x : INFINITY);
+          }
+        tref[qt] = group_min(mn) * cs;
+      }
+    }
+    const bool grow = tref[0] > m_run[0] + TAU || tref[1] > m_run[1] + TAU;
+    if (__any(grow)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float mnew = fmaxf(m_run[qt], tref[qt]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mnew);
+        m_run[qt] = mnew;
+        l_run[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[dt][qt] *= alpha;
+      }
+    }
+    bf16x8 pop[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float nm = -m_run[qt];
       float pv[8];
+      float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(x[i] - mnew);
-        ps += pv[i];
-      }
-      l_run[qt] = l_run[qt] * alpha + ps;
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) oacc[dt][qt] *= alpha;
+        for (int j = 0; j < 4; ++j) {
+          float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s2][qt][j], cs, nm));
+          if (partial && s2 * 16 + 4 * g + j >= nvt) e = 0.f;
+          pv[s2 * 4 + j] = e;
+          ps += e;
+        }
+      l_run[qt] += ps;
       if constexpr (FP8) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) pv[i] *= vsc;
       }
-      u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                  pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+      const u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                        pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
       pop[qt] = __builtin_bit_cast(bf16x8, pk);
     }
 
     // ---- A7: O^T[d][query] += V^T P^T.  The MFMA K index 8g+i maps to tile
     // key 4g+i (i<4) and 16+4g+(i-4) (i>=4), matching P's accumulator layout.
+    {
+      const int vr = lane >> 2;                  // rows vr and vr+16
+      const int half = (lane & 1) * 8;           // byte within the chunk
+      const int csub = (lane & 3) >> 1;          // chunk = 2*dt + csub
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const char* va = vs + ((lane >> 2) * VPITCH + dt * 16 + (lane & 3) * 4) * 2;
-      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)va);
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(va + 16 * VPITCH * 2));
-      const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, vv);
+      for (int dt = 0; dt < 8; ++dt) {
+        const char* va0 = vs + v_off(vr, 2 * dt + csub) + half;
+        const char* va1 = vs + v_off(vr + 16, 2 * dt + csub) + half;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)va0);
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)va1);
+        const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-        oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            vop, pop[qt], oacc[dt][qt], 0, 0, 0);
+        for (int qt = 0; qt < 2; ++qt)
+          oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              vop, pop[qt], oacc[dt][qt], 0, 0, 0);
+      }
     }
 
     if (!has_next) break;
-    store_tile<FP8, NT>(st, smem + ((it + 1) & 1) * STAGE_BYTES, tid);
-    __syncthreads();
+    if constexpr (FP8) {
+      store_tile_fp8<NT>(st, nstage, tid);
+      ksc_cur = ksc_nxt;
+      vsc_cur = vsc_nxt;
+    }
     cur = nxt;
   }
 
   // ---- A8: epilogue
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const float l = wave_sum_groups(l_run[qt]);  // >= 1: the row max has weight 1
+    const float l = group_sum(l_run[qt]);  // >= 1 unless weights underflow
     const float inv = 1.0f / l;
     const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
 #pragma unroll
@@ -455,7 +583,7 @@ __global__ __launch_bounds__(BLK * 2) void bsa_fwd_kernel(FwdParams p) {
 
 size_t lds_bytes(int NK) {
   return (size_t)NSTAGE * STAGE_BYTES + (size_t)((NK + 15) & ~15) +
-         (size_t)NK * sizeof(uint16_t);
+         (size_t)NK * sizeof(uint32_t);
 }
 
 template <int BLK, bool FP8, bool BITMAP>
