@@ -158,6 +158,9 @@ def main() -> int:
                     help="named workload index (default 2: video-shaped VSA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (the "
+                         "reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -169,6 +172,16 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        n = 1 << 29  # 2**29 bf16 = 1 GiB read + 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        progress("copy calibration: 3 copies of 1 GiB")
+        return 0
 
     progress(f"generating workload {args.workload}")
     w = workloads.make_config(args.workload)

@@ -53,11 +53,6 @@ constexpr int TILE_BYTES = KT * ROWB;   // one K or V tile (8 KB)
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 constexpr int NSTAGE = 2;
 constexpr float LOG2E = 1.4426950408889634f;
-// Lazy rescaling: the running reference m of a row is only raised when a
-// tile's maximum exceeds it by more than TAU (log2 units), so weights stay
-// below 2^TAU and the accumulator is rescaled rarely.  Any reference gives
-// the same O and LSE in exact arithmetic.
-constexpr float TAU = 8.0f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -197,44 +192,20 @@ __device__ __forceinline__ Tile next_tile(const Tile& cur, const uint32_t* list,
   return tile_at_entry(list, cur.e + 1, nsel);
 }
 
-// One direct global->LDS load of 16 B per lane (global_load_lds_dwordx4):
-// lane l's 16 bytes land at LDS address lds_base + 16*l.  Issued as inline
-// assembly so that the compiler does not track it; the loop waits for these
-// loads explicitly (vmcnt) before the barrier that publishes a tile, and the
-// reads of the other stage may proceed while they are in flight.
-__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+// One direct global->LDS load of 16 B per lane (global_load_lds_dwordx4,
+// SGPR base + 32-bit VGPR offset): lane l's 16 bytes land at LDS address
+// lds_base + 16*l.  Issued as inline assembly so that the compiler does not
+// track it; the loop waits for these loads explicitly (vmcnt) before the
+// barrier that publishes a tile, and the reads of the other stage proceed
+// while they are in flight.
+__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff,
+                                      uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, off"
+      "global_load_lds_dwordx4 %1, %2"
       :
-      : "s"(lds_base), "v"(gaddr)
+      : "s"(lds_base), "v"(voff), "s"(gbase)
       : "memory", "m0");
-}
-
-// bf16 K/V: the valid rows of a tile go straight from global memory into
-// LDS, no VGPR staging.  One instruction moves 64 lanes x 16 B = 4 rows;
-// lane l fills LDS position (l & 15) of row 4j + l/16, i.e. it loads the
-// chunk that the swizzle puts there.  Rows at or past the valid count are not
-// loaded (their stale LDS contents meet a zero probability or a masked
-// score).
-template <int NW>
-__device__ __forceinline__ void issue_tile_bf16(const char* kg, const char* vg,
-                                                uint32_t stage_lds, int nvt,
-                                                int wave, int lane) {
-#pragma unroll
-  for (int j = wave; j < KT / 4; j += NW) {
-    const int r = 4 * j + (lane >> 4);
-    const int pos = lane & 15;
-    const uint32_t kdst = __builtin_amdgcn_readfirstlane(stage_lds + j * 1024);
-    const uint32_t vdst =
-        __builtin_amdgcn_readfirstlane(stage_lds + TILE_BYTES + j * 1024);
-    if (r < nvt) {
-      const int ck = pos ^ (r & 15);
-      const int cv = pos ^ ((r & 7) << 1);
-      dma16(kg + r * ROWB + ck * 16, kdst);
-      dma16(vg + r * ROWB + cv * 16, vdst);
-    }
-  }
 }
 
 // fp8 K/V: 16 codes per 16-byte load, widened to bf16 in registers and
@@ -293,16 +264,163 @@ __device__ __forceinline__ void wait_vm_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
 }
 
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return fmaxf(fmaxf(a, b), c);
+}
+
+// Tile shapes of the K loop: FULL = 32 valid keys; PART = 1..31 valid keys
+// (keys past the count masked; the second 16-key half's QK^T is skipped
+// when it holds no valid key).
+enum TileKind { FULL = 0, PART = 1 };
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// Accumulator state of one wave: O^T tiles, per-row reference m (log2
+// units, identical in the four lanes of a row) and per-lane partial sums l.
+struct Acc {
+  f32x4 o[8][2];
+  float m[2];
+  float l[2];
+};
+
+// Raw scores of one tile for this wave: s[qt][e], e = 4*s2 + j is key
+// s2*16 + 4g + j of the tile and query qt*16 + r16.  Keys at or past the
+// valid count (lane limit lim = nvt - 4g) are set to -inf.
+template <int KIND>
+__device__ __forceinline__ void tile_scores(const char* sb, uint32_t kbase,
+                                            const bf16x8 (&qreg)[2][4], int nvt,
+                                            int lim, float (&s)[2][8]) {
+  f32x4 sacc[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const bf16x8 kop = *(const bf16x8*)(sb + (kbase ^ (kk << 6)));
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+      sacc[0][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          kop, qreg[qt][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[0][qt],
+          0, 0, 0);
+  }
+  sacc[1][0] = sacc[1][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (KIND == FULL || nvt > 16) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 kop = *(const bf16x8*)(sb + (kbase ^ (kk << 6)) + 16 * ROWB);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        sacc[1][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            kop, qreg[qt][kk], sacc[1][qt], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = sacc[e >> 2][qt][e & 3];
+      s[qt][e] = (KIND == FULL || (e >> 2) * 16 + (e & 3) < lim) ? x : -INFINITY;
+    }
+}
+
+// Row maximum of the tile, scaled: max over valid keys of s*cs (cs > 0),
+// reduced over the four lanes of each row.
+__device__ __forceinline__ void tile_max(const float (&s)[2][8], float cs,
+                                         float (&tm)[2]) {
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float m0 = max3f(s[qt][0], s[qt][1], s[qt][2]);
+    const float m1 = max3f(s[qt][3], s[qt][4], s[qt][5]);
+    const float m2 = max3f(s[qt][6], s[qt][7], m0);
+    tm[qt] = group_max(fmaxf(m1, m2)) * cs;
+  }
+}
+
+// P = 2^(s*cs - m) (zero for masked keys), added to the partial row sums,
+// scaled by vsc (fp8 V scale) and packed to bf16 in the PV operand layout.
+template <bool SCALE_P>
+__device__ __forceinline__ void tile_probs(const float (&s)[2][8], float cs,
+                                           float vsc, Acc& acc, bf16x8 (&pop)[2]) {
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float nm = -acc.m[qt];
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][e], cs, nm));
+    acc.l[qt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) +
+                 ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    if constexpr (SCALE_P) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] *= vsc;
+    }
+    const u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                      pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+    pop[qt] = __builtin_bit_cast(bf16x8, pk);
+  }
+}
+
+// O^T[d][query] += V^T P^T.  The MFMA K index 8g+i maps to tile key 4g+i
+// (i<4) and 16+4g+(i-4) (i>=4), matching P's accumulator layout; V^T comes
+// from transposing LDS reads at vbase ^ (dt << 5) (+16 rows).
+__device__ __forceinline__ void tile_pv(const char* sb, uint32_t vbase,
+                                        const bf16x8 (&pop)[2], Acc& acc) {
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const uint32_t va = vbase ^ (uint32_t)(dt << 5);
+    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + va));
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(sb + va + 16 * ROWB));
+    const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x8 vop = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+      acc.o[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[qt],
+                                                               acc.o[dt][qt], 0, 0, 0);
+  }
+}
+
+// Direct loads of this wave's slices of a bf16 tile (wave index W known at
+// compile time, so every LDS destination and row offset is a constant).
+// Slice j = W + i*NW covers rows 4j..4j+3; lane l fills LDS position l & 15
+// of row 4j + l/16 with the chunk the swizzle places there (per-lane
+// offsets dmak ^ ((j & 3) << 6) and dmav ^ ((j & 1) << 7)).
+template <int NW, int W>
+__device__ __forceinline__ void issue_bf16_w(const char* kg, const char* vg,
+                                             uint32_t stage_lds, int nvt,
+                                             uint32_t dmak, uint32_t dmav, int l4) {
+#pragma unroll
+  for (int i = 0; i < (KT / 4) / NW; ++i) {
+    constexpr int dummy = 0;
+    (void)dummy;
+    const int j = W + i * NW;
+    const uint32_t ko = dmak ^ ((uint32_t)(j & 3) << 6);
+    const uint32_t vo = dmav ^ ((uint32_t)(j & 1) << 7);
+    const uint32_t kd = stage_lds + j * 1024;
+    const uint32_t vd = stage_lds + TILE_BYTES + j * 1024;
+    if (nvt >= KT || 4 * j + 4 <= nvt) {  // whole slice valid
+      dma16(kg + j * 1024, ko, kd);
+      dma16(vg + j * 1024, vo, vd);
+    } else if (4 * j < nvt) {             // partly valid: rows below nvt only
+      if (4 * j + l4 < nvt) {
+        dma16(kg + j * 1024, ko, kd);
+        dma16(vg + j * 1024, vo, vd);
+      }
+    }
+  }
+}
+
 template <int BLK, bool FP8, bool BITMAP>
 __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
   constexpr int NW = BLK / 32;  // waves; each owns 32 query rows
   constexpr int NT = NW * 64;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ int s_nsel;
+  __shared__ int s_redo;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;    // lane group: 0..3
   const int r16 = lane & 15;  // row within a 16-row MFMA tile
 
@@ -322,6 +440,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
   // Zero both stages once: rows that are never loaded must hold finite data.
   for (int i = tid; i < NSTAGE * STAGE_BYTES / 16; i += NT)
     *(u32x4*)(smem + i * 16) = u32x4{0, 0, 0, 0};
+  if (tid == 0) s_redo = 0;
 
   // ---- A2: selected set -> LDS bitmap
   if constexpr (BITMAP) {
@@ -370,31 +489,24 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
     return;
   }
 
-  const int eb = FP8 ? 1 : 2;  // bytes per K/V element in global memory
+  constexpr int EB = FP8 ? 1 : 2;  // bytes per K/V element in global memory
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
-  const char* kplane = (const char*)p.k + plane * eb;
-  const char* vplane = (const char*)p.v + plane * eb;
-
-  // ---- A4 prologue: tile 0 into stage 0
+  const char* kplane = (const char*)p.k + plane * EB;
+  const char* vplane = (const char*)p.v + plane * EB;
   const int64_t scale_row = (int64_t)bh * NK;  // fp8 scales of (b, h)
-  Tile cur = tile_at_entry(list, 0, nsel);
-  [[maybe_unused]] float ksc_cur = 1.f, vsc_cur = 1.f;
-  if constexpr (FP8) {
-    ksc_cur = p.k_scale[scale_row + cur.kb];
-    vsc_cur = p.v_scale[scale_row + cur.kb];
-  }
-  [[maybe_unused]] Fp8Staging<NT> st;
-  {
-    const int64_t key0 = (int64_t)cur.kb * BLK + cur.t0;
-    if constexpr (FP8) {
-      load_tile_fp8<NT>(st, kplane + key0 * HD, vplane + key0 * HD,
-                        cur.nv - cur.t0, tid);
-      store_tile_fp8<NT>(st, smem, tid);
-    } else {
-      issue_tile_bf16<NW>(kplane + key0 * ROWB, vplane + key0 * ROWB,
-                          smem_lds, cur.nv - cur.t0, wave, lane);
-    }
-  }
+
+  // Per-lane constant byte offsets (the XOR swizzles make every address a
+  // per-lane base XORed with a constant): K operand kbase ^ (kk << 6),
+  // keys 16..31 at +16 rows; V^T transposing reads vbase ^ (dt << 5), rows
+  // 16..31 at +16 rows; DMA offsets within a 4-row slice dmak / dmav.
+  const uint32_t kbase = (uint32_t)(r16 * ROWB + ((g ^ r16) << 4));
+  const uint32_t vbase = (uint32_t)(TILE_BYTES + (lane >> 2) * ROWB +
+                                    ((2 * ((lane >> 2) & 7) + ((lane & 3) >> 1)) << 4) +
+                                    (lane & 1) * 8);
+  const int l4 = lane >> 4, pos = lane & 15;
+  [[maybe_unused]] const uint32_t dmak = (uint32_t)(l4 * ROWB + ((pos ^ l4) << 4));
+  [[maybe_unused]] const uint32_t dmav =
+      (uint32_t)(l4 * ROWB + ((pos ^ (2 * l4)) << 4));
 
   // ---- A3: Q operands (B operand of S^T = K Q^T): Q[row r16][d kk*32+g*8..]
   bf16x8 qreg[2][4];
@@ -407,174 +519,157 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
         qreg[qt][kk] = *(const bf16x8*)(qg + (qt * 16 + r16) * HD + kk * 32 + g * 8);
   }
 
-  f32x4 oacc[8][2];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY};  // reference (log2 units)
-  float l_run[2] = {0.f, 0.f};              // per-lane partial sums
+  [[maybe_unused]] Fp8Staging<NT> st;
+  [[maybe_unused]] float ksc_cur = 1.f, vsc_cur = 1.f, ksc_nxt = 1.f, vsc_nxt = 1.f;
 
-  for (int it = 0;; ++it) {
-    // tile `it` complete in LDS for every wave; stage (it+1)&1 free again
-    wait_vm_all();
-    __syncthreads();
-    const Tile nxt = next_tile(cur, list, nsel);
-    const bool has_next = nxt.e < nsel;
-    char* nstage = smem + ((it + 1) & 1) * STAGE_BYTES;
-    [[maybe_unused]] float ksc_nxt = 1.f, vsc_nxt = 1.f;
-    if (has_next) {
-      const int64_t key0 = (int64_t)nxt.kb * BLK + nxt.t0;
-      if constexpr (FP8) {
-        load_tile_fp8<NT>(st, kplane + key0 * HD, vplane + key0 * HD,
-                          nxt.nv - nxt.t0, tid);
-        ksc_nxt = p.k_scale[scale_row + nxt.kb];
-        vsc_nxt = p.v_scale[scale_row + nxt.kb];
-      }
-      else
-        issue_tile_bf16<NW>(kplane + key0 * ROWB, vplane + key0 * ROWB,
-                            smem_lds + ((it + 1) & 1) * STAGE_BYTES,
-                            nxt.nv - nxt.t0, wave, lane);
-    }
-
-    const char* ks = smem + (it & 1) * STAGE_BYTES;
-    const char* vs = ks + TILE_BYTES;
-    const int nvt = cur.nv - cur.t0;  // valid keys of this tile (>= 1)
-
-    // ---- A5: S^T[key][query] for 32 keys x 32 queries of this wave; the
-    // second 16-key half is skipped when it holds no valid key
-    f32x4 sacc[2][2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) sacc[s2][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      if (s2 == 1 && nvt <= 16) break;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 kop = *(const bf16x8*)(ks + k_off(s2 * 16 + r16, kk * 4 + g));
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-          sacc[s2][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              kop, qreg[qt][kk], sacc[s2][qt], 0, 0, 0);
-      }
-    }
-
-    // ---- A6: online softmax (exp2 form)
-    float cs = p.c;
-    [[maybe_unused]] float vsc = 1.f;
+  // Starts the loads of tile t into stage `stg` (bf16: DMA; fp8: registers).
+  auto issue = [&](const Tile& t, int stg) {
+    const int64_t key0 = (int64_t)t.kb * BLK + t.t0;
+    const int nvt = t.nv - t.t0;
     if constexpr (FP8) {
-      cs *= ksc_cur;
-      vsc = vsc_cur;
-    }
-    const bool partial = nvt < KT;
-    // key of element (s2, j) in this tile: s2*16 + 4g + j
-    float tref[2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      if (cs >= 0.f) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = sacc[s2][qt][j];
-            mx = fmaxf(mx, (!partial || s2 * 16 + 4 * g + j < nvt) ? x : -INFINITY);
-          }
-        tref[qt] = group_max(mx) * cs;
+      load_tile_fp8<NT>(st, kplane + key0 * HD, vplane + key0 * HD, nvt, tid);
+      ksc_nxt = p.k_scale[scale_row + t.kb];
+      vsc_nxt = p.v_scale[scale_row + t.kb];
+    } else {
+      const char* kg = kplane + key0 * ROWB;
+      const char* vg = vplane + key0 * ROWB;
+      const uint32_t sl = smem_lds + stg * STAGE_BYTES;
+      if constexpr (NW == 2) {
+        if (wave == 0) issue_bf16_w<2, 0>(kg, vg, sl, nvt, dmak, dmav, l4);
+        else           issue_bf16_w<2, 1>(kg, vg, sl, nvt, dmak, dmav, l4);
       } else {
-        float mn = INFINITY;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = sacc[s2][qt][j];
-            mn = fminf(mn, (!partial || s2 * 16 + 4 * g + j < nvt) ? x : INFINITY);
-          }
-        tref[qt] = group_min(mn) * cs;
+        if (wave == 0)      issue_bf16_w<4, 0>(kg, vg, sl, nvt, dmak, dmav, l4);
+        else if (wave == 1) issue_bf16_w<4, 1>(kg, vg, sl, nvt, dmak, dmav, l4);
+        else if (wave == 2) issue_bf16_w<4, 2>(kg, vg, sl, nvt, dmak, dmav, l4);
+        else                issue_bf16_w<4, 3>(kg, vg, sl, nvt, dmak, dmav, l4);
       }
     }
-    const bool grow = tref[0] > m_run[0] + TAU || tref[1] > m_run[1] + TAU;
-    if (__any(grow)) {
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const float mnew = fmaxf(m_run[qt], tref[qt]);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mnew);
-        m_run[qt] = mnew;
-        l_run[qt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) oacc[dt][qt] *= alpha;
-      }
-    }
-    bf16x8 pop[2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const float nm = -m_run[qt];
-      float pv[8];
-      float ps = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s2][qt][j], cs, nm));
-          if (partial && s2 * 16 + 4 * g + j >= nvt) e = 0.f;
-          pv[s2 * 4 + j] = e;
-          ps += e;
-        }
-      l_run[qt] += ps;
-      if constexpr (FP8) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] *= vsc;
-      }
-      const u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                        pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-      pop[qt] = __builtin_bit_cast(bf16x8, pk);
-    }
+  };
 
-    // ---- A7: O^T[d][query] += V^T P^T.  The MFMA K index 8g+i maps to tile
-    // key 4g+i (i<4) and 16+4g+(i-4) (i>=4), matching P's accumulator layout.
-    {
-      const int vr = lane >> 2;                  // rows vr and vr+16
-      const int half = (lane & 1) * 8;           // byte within the chunk
-      const int csub = (lane & 3) >> 1;          // chunk = 2*dt + csub
+  // One pass of the K loop over every selected tile.
+  //  SAFE = false: the reference m of each row is fixed at the first tile's
+  //  row maximum; weights 2^(t - m) may exceed 1 but the accumulators are
+  //  never rescaled.  The caller checks afterwards that nothing overflowed.
+  //  SAFE = true: online softmax -- every tile raises m to the running
+  //  maximum and rescales O and l by 2^(m_old - m_new).
+  // Both give the same O and LSE in exact arithmetic (any reference does).
+  auto run_pass = [&](auto safe_c, Acc& acc) {
+    constexpr bool SAFE = decltype(safe_c)::value;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const char* va0 = vs + v_off(vr, 2 * dt + csub) + half;
-        const char* va1 = vs + v_off(vr + 16, 2 * dt + csub) + half;
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)va0);
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)va1);
-        const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, vv);
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-          oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              vop, pop[qt], oacc[dt][qt], 0, 0, 0);
-      }
-    }
+      for (int qt = 0; qt < 2; ++qt) acc.o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.m[0] = acc.m[1] = -INFINITY;
+    acc.l[0] = acc.l[1] = 0.f;
 
-    if (!has_next) break;
+    Tile cur = tile_at_entry(list, 0, nsel);
+    issue(cur, 0);
     if constexpr (FP8) {
-      store_tile_fp8<NT>(st, nstage, tid);
+      store_tile_fp8<NT>(st, smem, tid);
       ksc_cur = ksc_nxt;
       vsc_cur = vsc_nxt;
     }
-    cur = nxt;
+
+    // stg_c: LDS stage of `cur` (compile-time); first_c: this is tile 0
+    auto step = [&](auto stg_c, auto first_c) -> bool {
+      constexpr int STG = decltype(stg_c)::value;
+      constexpr bool FIRST = decltype(first_c)::value != 0;
+      // tile `cur` complete in LDS for every wave; stage STG^1 free again
+      wait_vm_all();
+      __syncthreads();
+      const Tile nxt = next_tile(cur, list, nsel);
+      const bool has_next = nxt.e < nsel;
+      if (has_next) issue(nxt, STG ^ 1);
+
+      const int nvt = cur.nv - cur.t0;  // valid keys of this tile (>= 1)
+      const int lim = nvt - 4 * g;
+      const char* sb = smem + STG * STAGE_BYTES;
+      float cs = p.c;
+      float vsc = 1.f;
+      if constexpr (FP8) {
+        cs *= ksc_cur;
+        vsc = vsc_cur;
+      }
+
+      // ---- A5 + A6: scores and probabilities
+      bf16x8 pop[2];
+      auto body = [&](auto kind_c) {
+        constexpr int KIND = decltype(kind_c)::value;
+        float sv[2][8];
+        tile_scores<KIND>(sb, kbase, qreg, nvt, lim, sv);
+        if constexpr (SAFE || FIRST) {
+          float tm[2];
+          tile_max(sv, cs, tm);
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            const float mnew = fmaxf(acc.m[qt], tm[qt]);
+            if constexpr (SAFE && !FIRST) {
+              const float alpha = __builtin_amdgcn_exp2f(acc.m[qt] - mnew);
+              acc.l[qt] *= alpha;
+#pragma unroll
+              for (int dt = 0; dt < 8; ++dt) acc.o[dt][qt] *= alpha;
+            }
+            acc.m[qt] = mnew;
+          }
+        }
+        tile_probs<FP8>(sv, cs, vsc, acc, pop);
+      };
+      if (nvt >= KT) body(IntC<FULL>{});
+      else body(IntC<PART>{});
+
+      // ---- A7: PV
+      tile_pv(sb, vbase, pop, acc);
+
+      if (!has_next) return true;
+      if constexpr (FP8) {
+        store_tile_fp8<NT>(st, smem + (STG ^ 1) * STAGE_BYTES, tid);
+        ksc_cur = ksc_nxt;
+        vsc_cur = vsc_nxt;
+      }
+      cur = nxt;
+      return false;
+    };
+
+    if (!step(IntC<0>{}, IntC<1>{})) {
+      while (true) {
+        if (step(IntC<1>{}, IntC<0>{})) break;
+        if (step(IntC<0>{}, IntC<0>{})) break;
+      }
+    }
+  };
+
+  Acc acc;
+  if (p.c > 0.f) {
+    run_pass(IntC<0>{}, acc);
+    // The fixed reference is valid unless a weight or a sum overflowed (a
+    // score more than ~2^7 log2 units above the first tile's maximum).
+    bool bad = !(acc.l[0] <= 1e37f) || !(acc.l[1] <= 1e37f);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bad |= !(__builtin_fabsf(acc.o[dt][qt][i]) <= 3e38f);
+    if (__any(bad)) s_redo = 1;
+    __syncthreads();  // every wave is done with both stages; s_redo visible
+    if (s_redo) run_pass(IntC<1>{}, acc);
+  } else {
+    run_pass(IntC<1>{}, acc);
   }
 
   // ---- A8: epilogue
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const float l = group_sum(l_run[qt]);  // >= 1 unless weights underflow
+    const float l = group_sum(acc.l[qt]);  // >= 1: the reference key has weight >= 1
     const float inv = 1.0f / l;
     const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const f32x4 o = oacc[dt][qt] * inv;
+      const f32x4 o = acc.o[dt][qt] * inv;
       *(u32x2*)(p.out + r * HD + dt * 16 + g * 4) =
           u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }
-    if (p.lse && g == 0) p.lse[r] = m_run[qt] + __builtin_amdgcn_logf(l);
+    if (p.lse && g == 0) p.lse[r] = acc.m[qt] + __builtin_amdgcn_logf(l);
   }
 }
 

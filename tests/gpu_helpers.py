@@ -76,13 +76,21 @@ def gather_units(w, out, lse, units):
     return og, lg
 
 
-def check(o_gpu, l_gpu, o_ref, l_ref, label="", o_rel=0.0):
-    """Asserts parity: no NaN, O within O_TOL (+ o_rel*|O|), LSE within
+def scaled_input_bounds(v_max_abs: float):
+    """(o_abs, o_rel) for inputs beyond N(0, 1).  The kernel rounds each
+    probability to bf16 before the PV product (relative error <= 2^-9), which
+    moves O by at most 2^-9 * max|v|, and rounds O to bf16 (at most 2^-8 |O|
+    with margin); 1e-2 covers the remaining fp32 accumulation."""
+    return O_TOL + 2.0 ** -9 * v_max_abs, 2.0 ** -8
+
+
+def check(o_gpu, l_gpu, o_ref, l_ref, label="", o_rel=0.0, o_abs=O_TOL):
+    """Asserts parity: no NaN, O within o_abs (+ o_rel*|O|), LSE within
     LSE_TOL, and empty rows bit-exact (+0 output, the finite sentinel).
 
-    o_rel = 2**-8 adds the bf16 output rounding (half an ulp is at most
-    2^-8 |O|); it is used only for inputs scaled beyond N(0, 1), where |O|
-    exceeds 2.56 and one rounding step alone is larger than 1e-2."""
+    The defaults are the benchmark spec's bound (max-abs 1e-2).  For inputs scaled
+    beyond N(0, 1) the bound is derived from the arithmetic (see
+    scaled_input_bounds)."""
     o_gpu = np.asarray(o_gpu, dtype=np.float64)
     assert not np.isnan(o_gpu).any(), f"{label}: unwritten/NaN output"
     empty = l_ref == oracle.LSE_EMPTY
@@ -101,6 +109,6 @@ def check(o_gpu, l_gpu, o_ref, l_ref, label="", o_rel=0.0):
         oe = o_gpu[empty]
         assert (oe == 0).all() and not np.signbit(oe).any(), \
             f"{label}: empty rows not +0"
-    assert err_o <= O_TOL, msg
+    assert err_o <= o_abs, msg
     log("  " + msg + f" empty_rows={int(empty.sum())}")
     return err_o
