@@ -107,6 +107,57 @@ def stored_traffic(workload_name: str):
     return e.get("hbm_bytes_per_launch")
 
 
+def _counter_means(csv_path: str, counter: str, kernel_substr: str):
+    """Mean of one rocprofv3 counter over the dispatches of a kernel."""
+    import csv
+    vals = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr} in {csv_path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def record_traffic(pmc_dir: str, workload: int) -> int:
+    """Turns four rocprofv3 --pmc runs under pmc_dir (copy_fetch, copy_write:
+    this script's --copy-calibration; fetch, write: this script on the
+    workload) into HBM bytes per launch of the forward kernel, each counter
+    scaled by what it reads for a copy of exactly 1 GiB read + 1 GiB
+    written, and stores them in the traffic file under the workload name,
+    keyed to the current kernel source."""
+    csv_of = lambda n: os.path.join(pmc_dir, n, "run_counter_collection.csv")
+    gib = float(1 << 30)
+    cf, _ = _counter_means(csv_of("copy_fetch"), "FETCH_SIZE", "copyBuffer")
+    cw, _ = _counter_means(csv_of("copy_write"), "WRITE_SIZE", "copyBuffer")
+    f_fac, w_fac = gib / (cf * 1024.0), gib / (cw * 1024.0)
+    kf, nf = _counter_means(csv_of("fetch"), "FETCH_SIZE", "bsa_fwd_kernel")
+    kw, nw = _counter_means(csv_of("write"), "WRITE_SIZE", "bsa_fwd_kernel")
+    fetch = kf * 1024.0 * f_fac
+    write = kw * 1024.0 * w_fac
+    name = workloads.CONFIG_NAMES[workload]
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table[name] = {
+        "kernel_sha256_16": kernel_hash(),
+        "hbm_bytes_per_launch": round(fetch + write),
+        "fetch_bytes_per_launch": round(fetch),
+        "write_bytes_per_launch": round(write),
+        "fetch_scale": round(f_fac, 4),
+        "write_scale": round(w_fac, 4),
+        "dispatches_averaged": [nf, nw],
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({name: table[name]}))
+    return 0
+
+
 def cpu_baseline(w, target_s: float):
     """The oracle (as it stands) on a bounded sample of the same workload's
     work units; throughput in the same unit as the GPU metric."""
@@ -161,8 +212,14 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the "
                          "reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--record-traffic", metavar="PMC_DIR",
+                    help="no GPU work: read rocprofv3 FETCH_SIZE/WRITE_SIZE "
+                         "runs from PMC_DIR and store the workload's HBM "
+                         "bytes per launch")
     args = ap.parse_args()
 
+    if args.record_traffic:
+        return record_traffic(args.record_traffic, args.workload)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the forward "
               "pass on a single MI355X (each GPU would take its own share of "
