@@ -165,32 +165,49 @@ struct Tile {
   int e, kb, t0, nv;
 };
 
-// The selected-block list holds (kb << 8) | nv per entry, nv = valid keys.
-__device__ __forceinline__ Tile tile_at_entry(const uint32_t* list, int e,
-                                              int nsel) {
-  Tile t;
-  t.e = e;
-  t.t0 = 0;
-  if (e < nsel) {
-    const uint32_t x = __builtin_amdgcn_readfirstlane(list[e]);
-    t.kb = (int)(x >> 8);
-    t.nv = (int)(x & 255u);
-  } else {
+// Reader of the selected-block list ((kb << 8) | nv per entry, nv = valid
+// keys).  Entries are fetched from LDS 64 at a time into one VGPR (lane i
+// holds entry base + i) and picked out with v_readlane, so moving to the
+// next block costs no LDS round trip on the critical path.
+struct ListCursor {
+  const uint32_t* list;
+  int nsel;
+  int base;
+  uint32_t chunk;
+
+  __device__ __forceinline__ void reset(int lane) {
+    base = 0;
+    chunk = lane < nsel ? list[lane] : 0u;
+  }
+
+  // Entries are visited in increasing order, one at a time.
+  __device__ __forceinline__ Tile at(int e, int lane) {
+    Tile t;
+    t.e = e;
+    t.t0 = 0;
     t.kb = 0;
     t.nv = 0;
-  }
-  return t;
-}
-
-__device__ __forceinline__ Tile next_tile(const Tile& cur, const uint32_t* list,
-                                          int nsel) {
-  if (cur.t0 + KT < cur.nv) {
-    Tile t = cur;
-    t.t0 += KT;
+    if (e < nsel) {
+      if (e >= base + 64) {
+        base += 64;
+        chunk = base + lane < nsel ? list[base + lane] : 0u;
+      }
+      const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)chunk, e - base);
+      t.kb = (int)(x >> 8);
+      t.nv = (int)(x & 255u);
+    }
     return t;
   }
-  return tile_at_entry(list, cur.e + 1, nsel);
-}
+
+  __device__ __forceinline__ Tile next(const Tile& cur, int lane) {
+    if (cur.t0 + KT < cur.nv) {
+      Tile t = cur;
+      t.t0 += KT;
+      return t;
+    }
+    return at(cur.e + 1, lane);
+  }
+};
 
 // One direct global->LDS load of 16 B per lane (global_load_lds_dwordx4,
 // SGPR base + 32-bit VGPR offset): lane l's 16 bytes land at LDS address
@@ -380,32 +397,36 @@ __device__ __forceinline__ void tile_pv(const char* sb, uint32_t vbase,
   }
 }
 
-// Direct loads of this wave's slices of a bf16 tile (wave index W known at
-// compile time, so every LDS destination and row offset is a constant).
-// Slice j = W + i*NW covers rows 4j..4j+3; lane l fills LDS position l & 15
-// of row 4j + l/16 with the chunk the swizzle places there (per-lane
-// offsets dmak ^ ((j & 3) << 6) and dmav ^ ((j & 1) << 7)).
-template <int NW, int W>
-__device__ __forceinline__ void issue_bf16_w(const char* kg, const char* vg,
-                                             uint32_t stage_lds, int nvt,
-                                             uint32_t dmak, uint32_t dmav, int l4) {
+// Direct loads of this wave's share of a bf16 tile.  The tile's 8 slices
+// of 4 rows (1 KB) are dealt round-robin to the NW waves: slice
+// j = wave + i*NW lands at LDS stage + j*1024 (K) and stage + TILE_BYTES +
+// j*1024 (V); lane l fills LDS position l & 15 of row 4j + l/16 with the
+// chunk the swizzle places there, read from global offset ko[i] / vo[i]
+// (row offset and swizzle folded in, fixed per lane).  In a tile with
+// nvt < 32 valid rows, lanes of rows at or past nvt re-read the chunk at the
+// same position of the tile's row 0 instead (always a valid key; the row is
+// masked to -inf in the scores and meets a zero weight in PV), so the load
+// count never depends on nvt and no row past the block's valid count is read.
+template <int NW>
+__device__ __forceinline__ void issue_bf16(const char* kg, const char* vg,
+                                           uint32_t kdst, uint32_t vdst,
+                                           const uint32_t (&ko)[8 / NW],
+                                           const uint32_t (&vo)[8 / NW], int wave,
+                                           int l4, int nvt) {
+  if (nvt >= KT) {
 #pragma unroll
-  for (int i = 0; i < (KT / 4) / NW; ++i) {
-    constexpr int dummy = 0;
-    (void)dummy;
-    const int j = W + i * NW;
-    const uint32_t ko = dmak ^ ((uint32_t)(j & 3) << 6);
-    const uint32_t vo = dmav ^ ((uint32_t)(j & 1) << 7);
-    const uint32_t kd = stage_lds + j * 1024;
-    const uint32_t vd = stage_lds + TILE_BYTES + j * 1024;
-    if (nvt >= KT || 4 * j + 4 <= nvt) {  // whole slice valid
-      dma16(kg + j * 1024, ko, kd);
-      dma16(vg + j * 1024, vo, vd);
-    } else if (4 * j < nvt) {             // partly valid: rows below nvt only
-      if (4 * j + l4 < nvt) {
-        dma16(kg + j * 1024, ko, kd);
-        dma16(vg + j * 1024, vo, vd);
-      }
+    for (int i = 0; i < 8 / NW; ++i) {
+      const uint32_t j = (uint32_t)(wave + i * NW);
+      dma16(kg, ko[i], kdst + j * 1024u);
+      dma16(vg, vo[i], vdst + j * 1024u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8 / NW; ++i) {
+      const int j = wave + i * NW;
+      const bool ok = 4 * j + l4 < nvt;
+      dma16(kg, ok ? ko[i] : (ko[i] & 0xFFu), kdst + (uint32_t)j * 1024u);
+      dma16(vg, ok ? vo[i] : (vo[i] & 0xFFu), vdst + (uint32_t)j * 1024u);
     }
   }
 }
@@ -414,9 +435,9 @@ template <int BLK, bool FP8, bool BITMAP>
 __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
   constexpr int NW = BLK / 32;  // waves; each owns 32 query rows
   constexpr int NT = NW * 64;
+  // All LDS is dynamic, so the stages start at LDS address 0 and every
+  // operand address is a per-lane constant plus an immediate offset.
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  __shared__ int s_nsel;
-  __shared__ int s_redo;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -425,7 +446,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
   const int r16 = lane & 15;  // row within a 16-row MFMA tile
 
   const int NK = p.NK;
-  uint8_t* bmp = (uint8_t*)(smem + NSTAGE * STAGE_BYTES);
+  int* s_nsel = (int*)(smem + NSTAGE * STAGE_BYTES);
+  int* s_redo = s_nsel + 1;
+  uint8_t* bmp = (uint8_t*)(smem + NSTAGE * STAGE_BYTES + 16);
   uint32_t* list = (uint32_t*)(bmp + ((NK + 15) & ~15));
 
   // ---- A1: work unit
@@ -440,7 +463,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
   // Zero both stages once: rows that are never loaded must hold finite data.
   for (int i = tid; i < NSTAGE * STAGE_BYTES / 16; i += NT)
     *(u32x4*)(smem + i * 16) = u32x4{0, 0, 0, 0};
-  if (tid == 0) s_redo = 0;
+  if (tid == 0) *s_redo = 0;
 
   // ---- A2: selected set -> LDS bitmap
   if constexpr (BITMAP) {
@@ -469,10 +492,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
       if (f) list[pos] = ((uint32_t)kb << 8) | (uint32_t)nv;
       base += __popcll(bal);
     }
-    if (lane == 0) s_nsel = base;
+    if (lane == 0) *s_nsel = base;
   }
   __syncthreads();
-  const int nsel = s_nsel;
+  const int nsel = *s_nsel;
 
   const int qrow0 = qb * BLK + wave * 32;  // first query row of this wave
 
@@ -504,9 +527,14 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
                                     ((2 * ((lane >> 2) & 7) + ((lane & 3) >> 1)) << 4) +
                                     (lane & 1) * 8);
   const int l4 = lane >> 4, pos = lane & 15;
-  [[maybe_unused]] const uint32_t dmak = (uint32_t)(l4 * ROWB + ((pos ^ l4) << 4));
-  [[maybe_unused]] const uint32_t dmav =
-      (uint32_t)(l4 * ROWB + ((pos ^ (2 * l4)) << 4));
+  // DMA source offsets of this lane for its wave's slices (see issue_bf16)
+  [[maybe_unused]] uint32_t dko[8 / NW], dvo[8 / NW];
+#pragma unroll
+  for (int i = 0; i < 8 / NW; ++i) {
+    const int j = wave + i * NW;
+    dko[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ l4) ^ ((j & 3) << 2)) << 4));
+    dvo[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ (2 * l4)) ^ ((j & 1) << 3)) << 4));
+  }
 
   // ---- A3: Q operands (B operand of S^T = K Q^T): Q[row r16][d kk*32+g*8..]
   bf16x8 qreg[2][4];
@@ -519,6 +547,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
         qreg[qt][kk] = *(const bf16x8*)(qg + (qt * 16 + r16) * HD + kk * 32 + g * 8);
   }
 
+  ListCursor cursor{list, nsel, 0, 0u};
   [[maybe_unused]] Fp8Staging<NT> st;
   [[maybe_unused]] float ksc_cur = 1.f, vsc_cur = 1.f, ksc_nxt = 1.f, vsc_nxt = 1.f;
 
@@ -534,15 +563,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
       const char* kg = kplane + key0 * ROWB;
       const char* vg = vplane + key0 * ROWB;
       const uint32_t sl = smem_lds + stg * STAGE_BYTES;
-      if constexpr (NW == 2) {
-        if (wave == 0) issue_bf16_w<2, 0>(kg, vg, sl, nvt, dmak, dmav, l4);
-        else           issue_bf16_w<2, 1>(kg, vg, sl, nvt, dmak, dmav, l4);
-      } else {
-        if (wave == 0)      issue_bf16_w<4, 0>(kg, vg, sl, nvt, dmak, dmav, l4);
-        else if (wave == 1) issue_bf16_w<4, 1>(kg, vg, sl, nvt, dmak, dmav, l4);
-        else if (wave == 2) issue_bf16_w<4, 2>(kg, vg, sl, nvt, dmak, dmav, l4);
-        else                issue_bf16_w<4, 3>(kg, vg, sl, nvt, dmak, dmav, l4);
-      }
+      issue_bf16<NW>(kg, vg, sl, sl + TILE_BYTES, dko, dvo, wave, l4, nvt);
     }
   };
 
@@ -562,7 +583,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
     acc.m[0] = acc.m[1] = -INFINITY;
     acc.l[0] = acc.l[1] = 0.f;
 
-    Tile cur = tile_at_entry(list, 0, nsel);
+    cursor.reset(lane);
+    Tile cur = cursor.at(0, lane);
     issue(cur, 0);
     if constexpr (FP8) {
       store_tile_fp8<NT>(st, smem, tid);
@@ -577,7 +599,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
       // tile `cur` complete in LDS for every wave; stage STG^1 free again
       wait_vm_all();
       __syncthreads();
-      const Tile nxt = next_tile(cur, list, nsel);
+      const Tile nxt = cursor.next(cur, lane);
       const bool has_next = nxt.e < nsel;
       if (has_next) issue(nxt, STG ^ 1);
 
@@ -650,9 +672,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) bad |= !(__builtin_fabsf(acc.o[dt][qt][i]) <= 3e38f);
-    if (__any(bad)) s_redo = 1;
+    if (__any(bad)) *s_redo = 1;
     __syncthreads();  // every wave is done with both stages; s_redo visible
-    if (s_redo) run_pass(IntC<1>{}, acc);
+    if (*s_redo) run_pass(IntC<1>{}, acc);
   } else {
     run_pass(IntC<1>{}, acc);
   }
@@ -677,7 +699,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
 // host side
 
 size_t lds_bytes(int NK) {
-  return (size_t)NSTAGE * STAGE_BYTES + (size_t)((NK + 15) & ~15) +
+  return (size_t)NSTAGE * STAGE_BYTES + 16 + (size_t)((NK + 15) & ~15) +
          (size_t)NK * sizeof(uint32_t);
 }
 
