@@ -431,8 +431,18 @@ __device__ __forceinline__ void issue_bf16(const char* kg, const char* vg,
   }
 }
 
+// Waves per SIMD the register budget is sized for.  A 128-row unit runs 4
+// waves in 32 KB of LDS, so LDS would allow 4 per SIMD; capping registers
+// at 168 gives 3 (bf16 only: the fp8 staging registers do not fit).  A
+// 64-row unit is held at 2 per SIMD by LDS anyway.
+template <int BLK, bool FP8>
+constexpr int waves_per_simd() {
+  return (BLK == 128 && !FP8) ? 3 : 2;
+}
+
 template <int BLK, bool FP8, bool BITMAP>
-__global__ __launch_bounds__(BLK * 2, 2) void bsa_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, FP8>())) void bsa_fwd_kernel(
+    FwdParams p) {
   constexpr int NW = BLK / 32;  // waves; each owns 32 query rows
   constexpr int NT = NW * 64;
   // All LDS is dynamic, so the stages start at LDS address 0 and every
