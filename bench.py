@@ -33,6 +33,7 @@ import block_sparse_attention_tile_amd as bsa  # noqa: E402
 import workloads  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_attention_tile_amd", "csrc",
                              "bsa_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsa_fwd_traffic.json")
@@ -200,6 +201,44 @@ def cpu_baseline(w, target_s: float):
     }
 
 
+def bench_mask_to_lut(args) -> int:
+    """Times the block-map compaction on the selection matrix of a named
+    workload (one row per work unit).  HBM-bound integer kernel: algorithmic
+    bytes = mask read (1 B per entry) + LUT write (4 B per entry) + counts."""
+    progress(f"generating workload {args.workload}")
+    w = workloads.make_config(args.workload)
+    mask = selected_matrix(w).to(torch.int8).cuda()
+    rows, nk = mask.shape
+    nbytes = rows * nk * 5 + rows * 4
+    for _ in range(args.warmup):
+        bsa.bsa_mask_to_lut(mask)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        bsa.bsa_mask_to_lut(mask)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "block-map -> LUT compaction, GB/s of mask read + LUT write",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8->i32",
+        "data": "synthetic",
+        "config": {"workload": f"mask_to_lut of {w.name} selection",
+                   "rows": rows, "nk": nk, "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +251,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the "
                          "reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--op", default="fwd", choices=("fwd", "mask_to_lut"),
+                    help="fwd (default): the forward pass; mask_to_lut: the "
+                         "block-map compaction on the workload's selection")
     ap.add_argument("--record-traffic", metavar="PMC_DIR",
                     help="no GPU work: read rocprofv3 FETCH_SIZE/WRITE_SIZE "
                          "runs from PMC_DIR and store the workload's HBM "
@@ -230,6 +272,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
 
+    if args.op == "mask_to_lut":
+        return bench_mask_to_lut(args)
     if args.copy_calibration:
         n = 1 << 29  # 2**29 bf16 = 1 GiB read + 1 GiB written per copy
         src = torch.ones(n, dtype=torch.bfloat16, device="cuda")

@@ -16,6 +16,8 @@ from .api import (  # noqa: F401
     LSE_EMPTY,
     BsaError,
     bsa_fwd_bitmap,
+    bsa_fwd_from_mask,
     bsa_fwd_lut,
+    bsa_mask_to_lut,
     bsa_status_str,
 )

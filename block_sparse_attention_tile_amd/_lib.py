@@ -11,7 +11,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsa.so")
 
 # The exported C symbols, as declared in include/bsa.h.
-EXPORTS = ("bsa_fwd_lut", "bsa_fwd_bitmap", "bsa_status_str")
+EXPORTS = ("bsa_fwd_lut", "bsa_fwd_bitmap", "bsa_mask_to_lut", "bsa_status_str")
 
 _lib = None
 
@@ -36,6 +36,8 @@ def load():
     lib.bsa_fwd_bitmap.argtypes = [
         P, P, P, i32, P, P, P, i64, i64, P, f32, P, P,
         i32, i32, i32, i32, i32, P]
+    lib.bsa_mask_to_lut.restype = ctypes.c_int32
+    lib.bsa_mask_to_lut.argtypes = [P, i64, i32, P, P, P]
     lib.bsa_status_str.restype = ctypes.c_char_p
     lib.bsa_status_str.argtypes = [i32]
     _lib = lib

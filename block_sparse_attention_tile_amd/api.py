@@ -143,3 +143,38 @@ def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if rc != BSA_OK:
         raise BsaError(rc)
     return out, lse
+
+
+def bsa_mask_to_lut(mask: torch.Tensor,
+                    stream: Optional[torch.cuda.Stream] = None):
+    """Compacts a block map ``mask [..., NK]`` (nonzero = selected) on the
+    GPU into ``(q2k_idx [..., NK] int32, q2k_num [...] int32)``: ascending
+    selected key blocks, then -1 padding."""
+    m = mask.to(torch.int8).contiguous()
+    if m.dim() < 1:
+        raise ValueError("mask must have a key-block dimension")
+    nk = int(m.shape[-1])
+    rows = m.numel() // nk if nk > 0 else 0
+    idx = torch.empty(m.shape, dtype=torch.int32, device=m.device)
+    num = torch.empty(m.shape[:-1], dtype=torch.int32, device=m.device)
+    st = (stream or torch.cuda.current_stream(m.device)).cuda_stream
+    rc = _lib.load().bsa_mask_to_lut(_ptr(m), int(rows), nk, _ptr(idx),
+                                     _ptr(num), ctypes.c_void_p(st))
+    if rc != BSA_OK:
+        raise BsaError(rc)
+    return idx, num
+
+
+def bsa_fwd_from_mask(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      mask: torch.Tensor,
+                      variable_block_sizes: Optional[torch.Tensor] = None, *,
+                      block: int, mask_strides: Optional[Tuple[int, int]] = None,
+                      **kw):
+    """The from-mask route: compaction on the GPU, then the LUT form.  Gives
+    the same result as ``bsa_fwd_bitmap`` on the same mask; also returns the
+    look-up table for reuse.  Returns ``(out, lse, q2k_idx, q2k_num)``."""
+    idx, num = bsa_mask_to_lut(mask, stream=kw.get("stream"))
+    out, lse = bsa_fwd_lut(q, k, v, idx.reshape(-1, idx.shape[-1]),
+                           num.reshape(-1), variable_block_sizes, block=block,
+                           meta_strides=mask_strides, **kw)
+    return out, lse, idx, num

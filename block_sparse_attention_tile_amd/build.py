@@ -13,7 +13,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "bsa_fwd.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "bsa_fwd.hip"),
+           os.path.join(PKG, "csrc", "bsa_mask.hip")]
 LIB = os.path.join(PKG, "libbsa.so")
 
 HIPCC_FLAGS = [

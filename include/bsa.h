@@ -49,7 +49,7 @@ extern "C" {
 #define BSA_LSE_EMPTY (-FLT_MAX)
 
 /* Largest supported number of key blocks S/block (LDS holds one byte and
- * one 16-bit list entry per key block per work unit). */
+ * one 32-bit list entry per key block per work unit). */
 #define BSA_MAX_KEY_BLOCKS 16384
 
 typedef enum {
@@ -129,6 +129,29 @@ bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v,
                           const int32_t* variable_block_sizes, float sm_scale,
                           void* out, float* lse, int32_t B, int32_t H,
                           int32_t S, int32_t D, int32_t block, void* stream);
+
+/*
+ * bsa_mask_to_lut -- compaction of a block map into the look-up-table form
+ * (the `map_to_index` step that FastVideo "block_sparse_attn_sm100a.py"
+ * runs before its from-mask launch, `block_sparse_attn_sm100a_from_mask`).
+ *
+ *  mask         int8 [rows, nk] row-major, device memory: nonzero = the key
+ *               block is selected.  No alignment required.
+ *  rows         number of rows (>= 0; 0 launches nothing).
+ *  nk           key blocks per row, 1 <= nk <= BSA_MAX_KEY_BLOCKS.
+ *  q2k_idx      int32 [rows, nk], written in full: row r holds its selected
+ *               key blocks in ascending order, then -1 up to nk.
+ *  q2k_num      int32 [rows]: the number of selected key blocks of each row.
+ *  stream       hipStream_t (void*), NULL = null stream.
+ *
+ * The result feeds bsa_fwd_lut with max_kv = nk and the mask's row strides,
+ * and gives the same attention as bsa_fwd_bitmap on the mask.  Exact
+ * (integer) result.  Errors: BSA_ERR_SHAPE (rows < 0 or nk <= 0),
+ * BSA_ERR_UNSUPPORTED (nk too large), BSA_ERR_NULL, BSA_ERR_HIP; on error
+ * nothing is launched.
+ */
+bsa_status bsa_mask_to_lut(const int8_t* mask, int64_t rows, int32_t nk,
+                           int32_t* q2k_idx, int32_t* q2k_num, void* stream);
 
 /* Static text of a status code (never NULL). */
 const char* bsa_status_str(int32_t status);

@@ -20,7 +20,7 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(bsa_[a-z_0-9]+)\s*\(", text)))
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_exactly_the_exported_entry_points():
     assert declared_functions() == sorted(_lib.EXPORTS)
 
 
@@ -105,3 +105,23 @@ def test_python_binding_checks_dtypes_before_calling():
     with pytest.raises(TypeError):
         api.bsa_fwd_lut(q, q, q, torch.zeros((1, 1), dtype=torch.int32),
                         torch.zeros((1,), dtype=torch.int32), block=64)
+
+
+def mask_lut(**over):
+    args = dict(mask=A, rows=4, nk=8, idx=A, num=A, stream=None)
+    args.update(over)
+    return _lib.load().bsa_mask_to_lut(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(mask=None), api.BSA_ERR_NULL),
+    (dict(idx=None), api.BSA_ERR_NULL),
+    (dict(num=None), api.BSA_ERR_NULL),
+    (dict(rows=-1), api.BSA_ERR_SHAPE),
+    (dict(nk=0), api.BSA_ERR_SHAPE),
+    (dict(nk=16385), api.BSA_ERR_UNSUPPORTED),
+    (dict(rows=0), api.BSA_OK),                       # empty: nothing launched
+    (dict(rows=0, mask=None, idx=None, num=None), api.BSA_OK),
+])
+def test_mask_to_lut_rejects_invalid_static_arguments(over, status):
+    assert mask_lut(**over) == status
