@@ -92,7 +92,9 @@ typedef struct {
   const float* v_scale;
   const int32_t* vbs;
   double sm_scale;
-  int32_t H, S, D, block;
+  int32_t H, Hk;  /* query heads, key/value heads (H a multiple of Hk) */
+  int32_t Sq, Sk; /* query and key sequence lengths */
+  int32_t D, block;
 } attn_args;
 
 static double kv_value(const attn_args* a, const void* base, const float* scale,
@@ -104,13 +106,17 @@ static double kv_value(const attn_args* a, const void* base, const float* scale,
 }
 
 /* Computes the `block` output rows of unit (b, h, qb) given its selected set.
- * keys and t are scratch arrays of length S, qd of length D. */
+ * Query head h reads key/value head h / (H/Hk): consecutive query heads
+ * share one K/V head (rocke "sparse_attention.py": separate query and KV
+ * head counts, a KV head index per head).  keys and t are scratch arrays of
+ * length Sk, qd of length D. */
 static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
                         const unsigned char* sel, int64_t* keys, double* t,
                         double* qd, double* out, double* lse) {
-  const int32_t D = a->D, S = a->S, block = a->block, NK = S / block;
-  const int64_t head = (int64_t)b * a->H + h; /* (b, h) plane index */
-  const int64_t plane = head * (int64_t)S * D;
+  const int32_t D = a->D, block = a->block, NK = a->Sk / block;
+  const int64_t qplane = ((int64_t)b * a->H + h) * (int64_t)a->Sq * D;
+  const int64_t kvhead = (int64_t)b * a->Hk + h / (a->H / a->Hk);
+  const int64_t plane = kvhead * (int64_t)a->Sk * D;
   const double c = a->sm_scale / log(2.0); /* sm_scale * log2(e) */
 
   /* attended keys, ascending */
@@ -123,7 +129,7 @@ static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
 
   for (int32_t r = 0; r < block; ++r) {
     double* o = out + (int64_t)r * D;
-    const int64_t qrow = plane + ((int64_t)qb * block + r) * D;
+    const int64_t qrow = qplane + ((int64_t)qb * block + r) * D;
     if (n_att == 0) {
       for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
       lse[r] = -(double)FLT_MAX;
@@ -134,7 +140,7 @@ static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
     double m = -INFINITY;
     for (int64_t j = 0; j < n_att; ++j) {
       const int64_t key = keys[j];
-      const int64_t srow = head * (S / block) + key / block;
+      const int64_t srow = kvhead * NK + key / block;
       double s = 0.0;
       for (int32_t d = 0; d < D; ++d)
         s += qd[d] * kv_value(a, a->k, a->k_scale, plane + key * D + d, srow);
@@ -146,7 +152,7 @@ static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
     for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
     for (int64_t j = 0; j < n_att; ++j) {
       const int64_t key = keys[j];
-      const int64_t srow = head * (S / block) + key / block;
+      const int64_t srow = kvhead * NK + key / block;
       const double w = exp2(t[j] - m);
       l += w;
       for (int32_t d = 0; d < D; ++d)
@@ -159,10 +165,11 @@ static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
 
 /* ---- argument checks shared by the entry points ---------------------- */
 
-static int check_dims(int32_t B, int32_t H, int32_t S, int32_t D,
-                      int32_t block) {
-  if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || block <= 0) return 1;
-  if (S % block != 0) return 1;
+static int check_dims(int32_t B, int32_t H, int32_t Hk, int32_t Sq,
+                      int32_t Sk, int32_t D, int32_t block) {
+  if (B <= 0 || H <= 0 || Hk <= 0 || Sq <= 0 || Sk <= 0 || D <= 0 || block <= 0)
+    return 1;
+  if (H % Hk != 0 || Sq % block != 0 || Sk % block != 0) return 1;
   return 0;
 }
 
@@ -196,13 +203,13 @@ static void unit_select(const sel_args* s, int32_t b, int32_t h, int32_t qb,
 static int run_fwd(const attn_args* a, const sel_args* s, int32_t B,
                    const int64_t* units, int64_t n_units, double* out,
                    double* lse) {
-  const int32_t NQ = a->S / a->block, NK = NQ;
+  const int32_t NQ = a->Sq / a->block, NK = a->Sk / a->block;
   int failed = 0;
 #pragma omp parallel
   {
     unsigned char* sel = (unsigned char*)malloc((size_t)NK);
-    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)a->S);
-    double* t = (double*)malloc(sizeof(double) * (size_t)a->S);
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)a->Sk);
+    double* t = (double*)malloc(sizeof(double) * (size_t)a->Sk);
     double* qd = (double*)malloc(sizeof(double) * (size_t)a->D);
     const int ok = sel && keys && t && qd;
     if (!ok) {
@@ -237,16 +244,17 @@ int bsa_oracle_fwd_lut(const uint16_t* q, const void* k, const void* v,
                        const int32_t* q2k_idx, const int32_t* q2k_num,
                        int32_t max_kv, int64_t meta_stride_b,
                        int64_t meta_stride_h, const int32_t* vbs,
-                       double sm_scale, int32_t B, int32_t H, int32_t S,
-                       int32_t D, int32_t block, const int64_t* units,
-                       int64_t n_units, double* out, double* lse) {
+                       double sm_scale, int32_t B, int32_t H, int32_t Hk,
+                       int32_t Sq, int32_t Sk, int32_t D, int32_t block,
+                       const int64_t* units, int64_t n_units, double* out,
+                       double* lse) {
   if (!q || !k || !v || !q2k_idx || !q2k_num || !out || !lse) return 1;
-  if (check_dims(B, H, S, D, block) || max_kv < 1) return 1;
+  if (check_dims(B, H, Hk, Sq, Sk, D, block) || max_kv < 1) return 1;
   if (kv_dtype != ORACLE_KV_BF16 && kv_dtype != ORACLE_KV_FP8E4M3) return 1;
   if (kv_dtype == ORACLE_KV_FP8E4M3 && (!k_scale || !v_scale)) return 1;
-  if (check_units(units, n_units, (int64_t)B * H * (S / block))) return 1;
-  attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, vbs, sm_scale, H, S, D,
-                 block};
+  if (check_units(units, n_units, (int64_t)B * H * (Sq / block))) return 1;
+  attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, vbs, sm_scale, H, Hk,
+                 Sq, Sk, D, block};
   sel_args s = {FORM_LUT, q2k_idx, q2k_num, max_kv, meta_stride_b,
                 meta_stride_h, NULL};
   return run_fwd(&a, &s, B, units, n_units, out, lse);
@@ -257,16 +265,16 @@ int bsa_oracle_fwd_bitmap(const uint16_t* q, const void* k, const void* v,
                           const float* v_scale, const int8_t* mask,
                           int64_t mask_stride_b, int64_t mask_stride_h,
                           const int32_t* vbs, double sm_scale, int32_t B,
-                          int32_t H, int32_t S, int32_t D, int32_t block,
-                          const int64_t* units, int64_t n_units, double* out,
-                          double* lse) {
+                          int32_t H, int32_t Hk, int32_t Sq, int32_t Sk,
+                          int32_t D, int32_t block, const int64_t* units,
+                          int64_t n_units, double* out, double* lse) {
   if (!q || !k || !v || !mask || !out || !lse) return 1;
-  if (check_dims(B, H, S, D, block)) return 1;
+  if (check_dims(B, H, Hk, Sq, Sk, D, block)) return 1;
   if (kv_dtype != ORACLE_KV_BF16 && kv_dtype != ORACLE_KV_FP8E4M3) return 1;
   if (kv_dtype == ORACLE_KV_FP8E4M3 && (!k_scale || !v_scale)) return 1;
-  if (check_units(units, n_units, (int64_t)B * H * (S / block))) return 1;
-  attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, vbs, sm_scale, H, S, D,
-                 block};
+  if (check_units(units, n_units, (int64_t)B * H * (Sq / block))) return 1;
+  attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, vbs, sm_scale, H, Hk,
+                 Sq, Sk, D, block};
   sel_args s = {FORM_BITMAP, NULL, NULL, 0, mask_stride_b, mask_stride_h,
                 mask};
   return run_fwd(&a, &s, B, units, n_units, out, lse);
@@ -277,14 +285,14 @@ int bsa_oracle_key_counts(int form, const int32_t* q2k_idx,
                           int64_t meta_stride_b, int64_t meta_stride_h,
                           const int8_t* mask, int64_t mask_stride_b,
                           int64_t mask_stride_h, const int32_t* vbs, int32_t B,
-                          int32_t H, int32_t S, int32_t block,
+                          int32_t H, int32_t Sq, int32_t Sk, int32_t block,
                           const int64_t* units, int64_t n_units,
                           int32_t* counts) {
-  if (!counts || check_dims(B, H, S, 1, block)) return 1;
+  if (!counts || check_dims(B, H, H, Sq, Sk, 1, block)) return 1;
   if (form == FORM_LUT && (!q2k_idx || !q2k_num || max_kv < 1)) return 1;
   if (form == FORM_BITMAP && !mask) return 1;
   if (form != FORM_LUT && form != FORM_BITMAP) return 1;
-  const int32_t NQ = S / block, NK = NQ;
+  const int32_t NQ = Sq / block, NK = Sk / block;
   if (check_units(units, n_units, (int64_t)B * H * NQ)) return 1;
   sel_args s;
   if (form == FORM_LUT) {

@@ -65,19 +65,22 @@ double bsa_oracle_bf16_value(uint16_t bits);
 /* Value of one OCP fp8 e4m3fn byte (exact; NaN for S.1111.111). */
 double bsa_oracle_fp8e4m3_value(uint8_t byte);
 
-/* q: bf16 bits [B,H,S,D]; k, v: bf16 bits or fp8 bytes [B,H,S,D];
- * k_scale, v_scale: fp32 [B,H,S/block] (fp8 only, else ignored);
+/* q: bf16 bits [B,H,Sq,D]; k, v: bf16 bits or fp8 bytes [B,Hk,Sk,D] with
+ * H a multiple of Hk (query head h reads K/V head h/(H/Hk));
+ * k_scale, v_scale: fp32 [B,Hk,Sk/block] (fp8 only, else ignored);
  * q2k_idx: int32 rows x max_kv, q2k_num: int32 rows, with
- * row = b*meta_stride_b + h*meta_stride_h + qb;
- * vbs: int32 [S/block] or NULL (all blocks full). */
+ * row = b*meta_stride_b + h*meta_stride_h + qb (qb < Sq/block), entries
+ * naming key blocks in [0, Sk/block);
+ * vbs: int32 [Sk/block] or NULL (all blocks full). */
 int bsa_oracle_fwd_lut(const uint16_t* q, const void* k, const void* v,
                        int kv_dtype, const float* k_scale, const float* v_scale,
                        const int32_t* q2k_idx, const int32_t* q2k_num,
                        int32_t max_kv, int64_t meta_stride_b,
                        int64_t meta_stride_h, const int32_t* vbs,
-                       double sm_scale, int32_t B, int32_t H, int32_t S,
-                       int32_t D, int32_t block, const int64_t* units,
-                       int64_t n_units, double* out, double* lse);
+                       double sm_scale, int32_t B, int32_t H, int32_t Hk,
+                       int32_t Sq, int32_t Sk, int32_t D, int32_t block,
+                       const int64_t* units, int64_t n_units, double* out,
+                       double* lse);
 
 /* As above, with the selected set given by an i8 bitmap:
  * mask row = b*mask_stride_b + h*mask_stride_h + qb, NK bytes per row,
@@ -87,9 +90,9 @@ int bsa_oracle_fwd_bitmap(const uint16_t* q, const void* k, const void* v,
                           const float* v_scale, const int8_t* mask,
                           int64_t mask_stride_b, int64_t mask_stride_h,
                           const int32_t* vbs, double sm_scale, int32_t B,
-                          int32_t H, int32_t S, int32_t D, int32_t block,
-                          const int64_t* units, int64_t n_units, double* out,
-                          double* lse);
+                          int32_t H, int32_t Hk, int32_t Sq, int32_t Sk,
+                          int32_t D, int32_t block, const int64_t* units,
+                          int64_t n_units, double* out, double* lse);
 
 /* Integer decode only: counts[i][kb] = number of attended keys of key block
  * kb for the i-th requested unit (clamp(vbs[kb],0,block) if kb is selected,
@@ -100,7 +103,7 @@ int bsa_oracle_key_counts(int form, const int32_t* q2k_idx,
                           int64_t meta_stride_b, int64_t meta_stride_h,
                           const int8_t* mask, int64_t mask_stride_b,
                           int64_t mask_stride_h, const int32_t* vbs, int32_t B,
-                          int32_t H, int32_t S, int32_t block,
+                          int32_t H, int32_t Sq, int32_t Sk, int32_t block,
                           const int64_t* units, int64_t n_units,
                           int32_t* counts);
 

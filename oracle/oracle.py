@@ -51,15 +51,15 @@ def _lib():
         lib.bsa_oracle_fwd_lut.restype = ctypes.c_int
         lib.bsa_oracle_fwd_lut.argtypes = [
             P, P, P, ctypes.c_int, P, P, P, P, i32, i64, i64, P, f64,
-            i32, i32, i32, i32, i32, P, i64, P, P]
+            i32, i32, i32, i32, i32, i32, i32, P, i64, P, P]
         lib.bsa_oracle_fwd_bitmap.restype = ctypes.c_int
         lib.bsa_oracle_fwd_bitmap.argtypes = [
             P, P, P, ctypes.c_int, P, P, P, i64, i64, P, f64,
-            i32, i32, i32, i32, i32, P, i64, P, P]
+            i32, i32, i32, i32, i32, i32, i32, P, i64, P, P]
         lib.bsa_oracle_key_counts.restype = ctypes.c_int
         lib.bsa_oracle_key_counts.argtypes = [
             ctypes.c_int, P, P, i32, i64, i64, P, i64, i64, P,
-            i32, i32, i32, i32, P, i64, P]
+            i32, i32, i32, i32, i32, P, i64, P]
         lib.bsa_oracle_mask_to_lut.restype = ctypes.c_int
         lib.bsa_oracle_mask_to_lut.argtypes = [P, i64, i32, P, P]
         lib.bsa_oracle_num_threads.restype = ctypes.c_int
@@ -114,6 +114,8 @@ def _outputs(units, n, B, H, S, D, block):
 def _common(q, k, v, k_scale, v_scale):
     q = _cpu(q)
     assert q.dtype == torch.bfloat16 and q.dim() == 4
+    assert k.dim() == 4 and k.shape == v.shape and k.shape[0] == q.shape[0]
+    assert k.shape[3] == q.shape[3] and q.shape[1] % k.shape[1] == 0
     kb, kdt = _kv_bits(k)
     vb, vdt = _kv_bits(v)
     assert kdt == vdt, "K and V must share a dtype"
@@ -130,8 +132,10 @@ def fwd_lut(q, k, v, q2k_idx, q2k_num, vbs=None, *, block, sm_scale=None,
     """Oracle forward, LUT form.  ``q2k_idx`` is ``[..., max_kv]`` int32 and
     ``q2k_num`` the matching per-row counts; ``meta_strides=(sb, sh)`` gives
     the row of (b, h, qb) as ``b*sb + h*sh + qb`` (default: one row per
-    (b, h, qb), i.e. ``(H*NQ, NQ)``)."""
+    (b, h, qb), i.e. ``(H*NQ, NQ)``).  ``q`` is ``[B, H, Sq, D]``,
+    ``k``/``v`` ``[B, Hk, Sk, D]`` with H a multiple of Hk."""
     B, H, S, D = q.shape
+    Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
     qb_, kb_, vb_, kdt, ks, vs = _common(q, k, v, k_scale, v_scale)
     idx = _cpu(q2k_idx.to(torch.int32))
@@ -146,7 +150,7 @@ def fwd_lut(q, k, v, q2k_idx, q2k_num, vbs=None, *, block, sm_scale=None,
     rc = _lib().bsa_oracle_fwd_lut(
         _ptr(qb_), _ptr(kb_), _ptr(vb_), kdt, _ptr(ks), _ptr(vs),
         _ptr(idx), _ptr(num), max_kv, sb, sh, _ptr(vbs_t), float(sm_scale),
-        B, H, S, D, block, _ptr(u), n,
+        B, H, Hk, S, Sk, D, block, _ptr(u), n,
         out.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p))
     if rc != 0:
         raise ValueError(f"bsa_oracle_fwd_lut failed (rc={rc})")
@@ -157,8 +161,9 @@ def fwd_bitmap(q, k, v, mask, vbs=None, *, block, sm_scale=None,
                k_scale=None, v_scale=None, mask_strides=None, units=None):
     """Oracle forward, bitmap form.  ``mask`` is i8 rows of NK bytes;
     ``mask_strides=(sb, sh)`` as for the LUT (``(0, 0)`` = one shared
-    ``[NQ, NK]`` mask)."""
+    ``[NQ, NK]`` mask).  Shapes as for ``fwd_lut``."""
     B, H, S, D = q.shape
+    Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
     qb_, kb_, vb_, kdt, ks, vs = _common(q, k, v, k_scale, v_scale)
     m = _cpu(mask.to(torch.int8))
@@ -171,7 +176,7 @@ def fwd_bitmap(q, k, v, mask, vbs=None, *, block, sm_scale=None,
     rc = _lib().bsa_oracle_fwd_bitmap(
         _ptr(qb_), _ptr(kb_), _ptr(vb_), kdt, _ptr(ks), _ptr(vs),
         _ptr(m), sb, sh, _ptr(vbs_t), float(sm_scale),
-        B, H, S, D, block, _ptr(u), n,
+        B, H, Hk, S, Sk, D, block, _ptr(u), n,
         out.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p))
     if rc != 0:
         raise ValueError(f"bsa_oracle_fwd_bitmap failed (rc={rc})")
@@ -179,13 +184,16 @@ def fwd_bitmap(q, k, v, mask, vbs=None, *, block, sm_scale=None,
 
 
 def key_counts(*, B, H, S, block, q2k_idx=None, q2k_num=None, mask=None,
-               vbs=None, meta_strides=None, mask_strides=None, units=None):
+               vbs=None, meta_strides=None, mask_strides=None, units=None,
+               Sk=None):
     """Integer decode: ``[n_units, NK]`` int32 attended-key counts per key
-    block (LUT form if ``q2k_idx`` is given, else bitmap form)."""
-    NQ = S // block
+    block (LUT form if ``q2k_idx`` is given, else bitmap form).  ``S`` is the
+    query length, ``Sk`` the key length (default ``S``)."""
+    Sk = S if Sk is None else Sk
+    NQ, NK = S // block, Sk // block
     vbs_t = None if vbs is None else _cpu(vbs.to(torch.int32))
     u, n = _units_arg(units, B * H * NQ)
-    counts = np.empty((n, NQ), dtype=np.int32)
+    counts = np.empty((n, NK), dtype=np.int32)
     lib = _lib()
     if q2k_idx is not None:
         idx = _cpu(q2k_idx.to(torch.int32))
@@ -193,14 +201,14 @@ def key_counts(*, B, H, S, block, q2k_idx=None, q2k_num=None, mask=None,
         sb, sh = meta_strides if meta_strides is not None else (H * NQ, NQ)
         rc = lib.bsa_oracle_key_counts(
             0, _ptr(idx), _ptr(num), int(idx.shape[-1]), sb, sh, None, 0, 0,
-            _ptr(vbs_t), B, H, S, block, _ptr(u), n,
+            _ptr(vbs_t), B, H, S, Sk, block, _ptr(u), n,
             counts.ctypes.data_as(ctypes.c_void_p))
     else:
         m = _cpu(mask.to(torch.int8))
         sb, sh = mask_strides if mask_strides is not None else (H * NQ, NQ)
         rc = lib.bsa_oracle_key_counts(
             1, None, None, 0, 0, 0, _ptr(m), sb, sh,
-            _ptr(vbs_t), B, H, S, block, _ptr(u), n,
+            _ptr(vbs_t), B, H, S, Sk, block, _ptr(u), n,
             counts.ctypes.data_as(ctypes.c_void_p))
     if rc != 0:
         raise ValueError(f"bsa_oracle_key_counts failed (rc={rc})")

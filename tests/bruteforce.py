@@ -22,7 +22,7 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 def selected_sets(w) -> list:
     """Python sets of selected key blocks, indexed by unit u=(b*H+h)*NQ+qb."""
-    NQ = w.NQ
+    NQ, NK = w.NQ, w.NK
     out = []
     for b in range(w.B):
         for h in range(w.H):
@@ -33,42 +33,46 @@ def selected_sets(w) -> list:
                     n = int(w.q2k_num[row])
                     n = max(0, min(n, w.q2k_idx.shape[-1]))
                     s = {int(x) for x in w.q2k_idx[row, :n].tolist()
-                         if 0 <= int(x) < NQ}
+                         if 0 <= int(x) < NK}
                 else:
                     sb, sh = w.mask_strides
                     row = b * sb + h * sh + qb
-                    s = {kb for kb in range(NQ) if int(w.mask[row, kb]) != 0}
+                    s = {kb for kb in range(NK) if int(w.mask[row, kb]) != 0}
                 out.append(s)
     return out
 
 
 def dense_mask(w) -> np.ndarray:
-    """[B, H, S, S] bool attend mask."""
-    S, blk, NQ = w.S, w.block, w.NQ
-    vbs = [blk] * NQ if w.vbs is None else [
+    """[B, H, Sq, Sk] bool attend mask."""
+    S, Sk, blk, NQ, NK = w.S, w.Sk, w.block, w.NQ, w.NK
+    vbs = [blk] * NK if w.vbs is None else [
         max(0, min(blk, int(x))) for x in w.vbs.tolist()]
     sets = selected_sets(w)
-    m = np.zeros((w.B, w.H, S, S), dtype=bool)
+    m = np.zeros((w.B, w.H, S, Sk), dtype=bool)
     for u, sel in enumerate(sets):
         qb = u % NQ
         h = (u // NQ) % w.H
         b = u // (NQ * w.H)
-        for c in range(S):
+        for c in range(Sk):
             if c // blk in sel and c % blk < vbs[c // blk]:
                 m[b, h, qb * blk:(qb + 1) * blk, c] = True
     return m
 
 
 def kv_f64(w):
-    """Decoded K and V as float64 [B,H,S,D] (fp8: code value x block scale,
-    decoded by torch's float8_e4m3fn)."""
+    """Decoded K and V as float64 [B,H,Sk,D], one copy per query head
+    (query head h uses K/V head h // (H // Hk)); fp8: code value x block
+    scale, decoded by torch's float8_e4m3fn."""
     if w.kv_fp8:
         k = to_f64(w.k.to(torch.float32))
         v = to_f64(w.v.to(torch.float32))
         ks = np.repeat(to_f64(w.k_scale), w.block, axis=-1)[..., None]
         vs = np.repeat(to_f64(w.v_scale), w.block, axis=-1)[..., None]
-        return k * ks, v * vs
-    return to_f64(w.k), to_f64(w.v)
+        k, v = k * ks, v * vs
+    else:
+        k, v = to_f64(w.k), to_f64(w.v)
+    group = w.H // w.Hk
+    return np.repeat(k, group, axis=1), np.repeat(v, group, axis=1)
 
 
 def attention(w, mask=None):

@@ -87,6 +87,50 @@ def test_full_bitmap_equals_dense_sdpa_custom_scale():
     np.testing.assert_allclose(lse, lse_ref, atol=1e-10, rtol=1e-10)
 
 
+@pytest.mark.parametrize("H,Hk,S,Sk", [(4, 2, 256, 512), (3, 1, 512, 256),
+                                       (2, 2, 128, 384)])
+def test_rectangular_grouped_full_lut_equals_dense_sdpa(H, Hk, S, Sk):
+    """Every key block selected with S_q != S_k and H query heads over Hk
+    key/value heads reduces to dense attention with each K/V head repeated
+    for its H/Hk query heads (rocke "sparse_attention.py": separate query
+    and KV head counts and sequence lengths)."""
+    w = workloads.make_random(60 + H + Sk // 64, B=2, H=H, S=S, block=64,
+                              density=1.0, Hk=Hk, Sk=Sk)
+    assert int(w.q2k_num.min()) == Sk // 64
+    o, lse = run_oracle(w)
+    q = w.q.to(torch.float64)
+    k = w.k.to(torch.float64).repeat_interleave(H // Hk, dim=1).contiguous()
+    v = w.v.to(torch.float64).repeat_interleave(H // Hk, dim=1).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, scale=w.sm_scale).numpy()
+    lse_ref = (torch.logsumexp(q @ k.transpose(-1, -2) * w.sm_scale, dim=-1)
+               * LOG2E).numpy()
+    np.testing.assert_allclose(o, ref, atol=1e-10, rtol=1e-9)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-10, rtol=1e-10)
+
+
+def test_grouped_heads_equal_repeated_kv_heads():
+    """GQA is the same computation as repeating each K/V head (and its fp8
+    scales) for its query-head group: the oracle gives bitwise the same
+    result both ways."""
+    for kv in ("bf16", "fp8"):
+        w = workloads.make_random(70, B=2, H=6, S=256, block=64, kv=kv,
+                                  Hk=2, Sk=384, count_mode="uniform",
+                                  vbs_mode="random")
+        o, lse = run_oracle(w)
+        def rep(t):
+            return None if t is None else t.repeat_interleave(3, dim=1).contiguous()
+
+        w2 = workloads.Workload(w.name, w.B, w.H, w.S, w.D, w.block, w.form,
+                                w.q, rep(w.k), rep(w.v), k_scale=rep(w.k_scale),
+                                v_scale=rep(w.v_scale), q2k_idx=w.q2k_idx,
+                                q2k_num=w.q2k_num, meta_strides=w.meta_strides,
+                                vbs=w.vbs, sm_scale=w.sm_scale)
+        assert w2.Hk == w.H
+        o2, l2 = run_oracle(w2)
+        assert np.array_equal(o, o2) and np.array_equal(lse, l2), kv
+
+
 # ------------------------------------------------------ dense brute force
 
 BRUTE_CASES = [
@@ -103,6 +147,12 @@ BRUTE_CASES = [
     dict(seed=7, block=64, S=256, kv="fp8", density=0.5, vbs_mode="random"),
     dict(seed=8, block=128, S=256, kv="fp8", form="bitmap", density=0.7,
          std=3.0),
+    dict(seed=9, block=64, S=256, Sk=448, H=4, Hk=2, count_mode="uniform",
+         vbs_mode="zero_some"),
+    dict(seed=10, block=64, S=384, Sk=192, H=3, Hk=1, form="bitmap",
+         density=0.5, vbs_mode="partial"),
+    dict(seed=11, block=128, S=256, Sk=512, H=4, Hk=1, kv="fp8",
+         count_mode="uniform", vbs_mode="random"),
 ]
 
 
@@ -110,7 +160,8 @@ BRUTE_CASES = [
 def test_oracle_matches_dense_bruteforce(case):
     case = dict(case)
     seed = case.pop("seed")
-    w = workloads.make_random(seed, B=2, H=2, **case)
+    case.setdefault("H", 2)
+    w = workloads.make_random(seed, B=2, **case)
     o, lse = run_oracle(w)
     o_ref, lse_ref = bf.attention(w)
     np.testing.assert_allclose(o, o_ref, atol=1e-10, rtol=1e-9)
@@ -378,12 +429,13 @@ def test_fp8_scales_fold_linearly():
 
 # ---------------------------------------------------- integer decode only
 
-@pytest.mark.parametrize("form", ["lut", "bitmap"])
-def test_key_counts_match_python_sets(form):
+@pytest.mark.parametrize("form,Sk", [("lut", None), ("bitmap", None),
+                                     ("lut", 832), ("bitmap", 192)])
+def test_key_counts_match_python_sets(form, Sk):
     w = workloads.make_random(41, B=2, H=2, S=512, block=64, form=form,
                               count_mode="uniform", density=0.3,
-                              vbs_mode="random")
-    kw = dict(B=w.B, H=w.H, S=w.S, block=w.block, vbs=w.vbs)
+                              vbs_mode="random", Sk=Sk)
+    kw = dict(B=w.B, H=w.H, S=w.S, Sk=w.Sk, block=w.block, vbs=w.vbs)
     if form == "lut":
         c = oracle.key_counts(q2k_idx=w.q2k_idx, q2k_num=w.q2k_num,
                               meta_strides=w.meta_strides, **kw)
@@ -393,7 +445,7 @@ def test_key_counts_match_python_sets(form):
     vbs = w.vbs.tolist()
     for u, s in enumerate(sets):
         want = [min(max(vbs[kb], 0), w.block) if kb in s else 0
-                for kb in range(w.NQ)]
+                for kb in range(w.NK)]
         assert c[u].tolist() == want
 
 

@@ -36,7 +36,7 @@ class Workload:
     q: torch.Tensor
     k: torch.Tensor
     v: torch.Tensor
-    k_scale: Optional[torch.Tensor] = None  # fp32 [B, H, NK] (fp8 K/V only)
+    k_scale: Optional[torch.Tensor] = None  # fp32 [B, Hk, NK] (fp8 K/V only)
     v_scale: Optional[torch.Tensor] = None
     q2k_idx: Optional[torch.Tensor] = None  # int32 [rows, max_kv]
     q2k_num: Optional[torch.Tensor] = None  # int32 [rows]
@@ -50,6 +50,20 @@ class Workload:
     @property
     def NQ(self) -> int:
         return self.S // self.block
+
+    @property
+    def Hk(self) -> int:
+        """Key/value heads (query head h reads K/V head h // (H // Hk))."""
+        return int(self.k.shape[1])
+
+    @property
+    def Sk(self) -> int:
+        """Key sequence length."""
+        return int(self.k.shape[2])
+
+    @property
+    def NK(self) -> int:
+        return self.Sk // self.block
 
     @property
     def n_units(self) -> int:
@@ -170,54 +184,58 @@ def make_config(i: int, seed: Optional[int] = None) -> Workload:
 def make_random(seed: int, *, B=1, H=2, S=512, block=64, form="lut",
                 density=0.5, max_kv=None, count_mode="fixed", vbs_mode="full",
                 kv="bf16", std=1.0, shared_meta=False, pad_value=-1,
-                sort=False) -> Workload:
+                sort=False, Hk=None, Sk=None) -> Workload:
     """Small random workloads for parity and invariance tests.
 
     count_mode: "fixed" (round(density*NK) per row), "uniform" (U{0..max_kv}),
     "zero" (every row 0).  vbs_mode: "full" (None), "random" (U{0..block}),
     "partial" (U{1..block}), "zero_some" (some blocks 0).  kv: "bf16" or
-    "fp8"."""
+    "fp8".  Hk (key/value heads, default H) and Sk (key length, default S)
+    give grouped-query and rectangular cases."""
     g = _gen(seed)
     D = HEAD_DIM
+    Hk = H if Hk is None else Hk
+    Sk = S if Sk is None else Sk
     NQ = S // block
+    NK = Sk // block
     q = _randn(g, (B, H, S, D), std=std)
     if kv == "bf16":
-        k = _randn(g, (B, H, S, D), std=std)
-        v = _randn(g, (B, H, S, D), std=std)
+        k = _randn(g, (B, Hk, Sk, D), std=std)
+        v = _randn(g, (B, Hk, Sk, D), std=std)
         ks = vs = None
     else:
         k, ks = quantize_fp8_per_block(
-            torch.randn((B, H, S, D), generator=g) * std, block)
+            torch.randn((B, Hk, Sk, D), generator=g) * std, block)
         v, vs = quantize_fp8_per_block(
-            torch.randn((B, H, S, D), generator=g) * std, block)
+            torch.randn((B, Hk, Sk, D), generator=g) * std, block)
     rows = NQ if shared_meta else B * H * NQ
     strides = (0, 0) if shared_meta else (H * NQ, NQ)
     if vbs_mode == "full":
         vbs = None
     elif vbs_mode == "random":
-        vbs = torch.randint(0, block + 1, (NQ,), generator=g, dtype=torch.int32)
+        vbs = torch.randint(0, block + 1, (NK,), generator=g, dtype=torch.int32)
     elif vbs_mode == "partial":
-        vbs = torch.randint(1, block + 1, (NQ,), generator=g, dtype=torch.int32)
+        vbs = torch.randint(1, block + 1, (NK,), generator=g, dtype=torch.int32)
     elif vbs_mode == "zero_some":
-        vbs = torch.randint(0, block + 1, (NQ,), generator=g, dtype=torch.int32)
-        vbs[torch.rand((NQ,), generator=g) < 0.3] = 0
+        vbs = torch.randint(0, block + 1, (NK,), generator=g, dtype=torch.int32)
+        vbs[torch.rand((NK,), generator=g) < 0.3] = 0
     else:
         raise ValueError(vbs_mode)
     if form == "bitmap":
-        mask = (torch.rand((rows, NQ), generator=g) < density).to(torch.int8)
+        mask = (torch.rand((rows, NK), generator=g) < density).to(torch.int8)
         return Workload(f"random_bitmap_{seed}", B, H, S, D, block, "bitmap",
                         q, k, v, k_scale=ks, v_scale=vs, mask=mask,
                         mask_strides=strides, vbs=vbs)
     if max_kv is None:
-        max_kv = NQ
-    take = min(max_kv, NQ)
+        max_kv = NK
+    take = min(max_kv, NK)
     idx = torch.full((rows, max_kv), pad_value, dtype=torch.int32)
-    sel = _distinct_rows(g, rows, NQ, take)
+    sel = _distinct_rows(g, rows, NK, take)
     if sort:
         sel = sel.sort(dim=-1).values
     idx[:, :take] = sel
     if count_mode == "fixed":
-        n = max(0, min(take, round(density * NQ)))
+        n = max(0, min(take, round(density * NK)))
         num = torch.full((rows,), n, dtype=torch.int32)
     elif count_mode == "uniform":
         num = torch.randint(0, take + 1, (rows,), generator=g, dtype=torch.int32)
