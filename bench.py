@@ -51,7 +51,7 @@ def kernel_hash() -> str:
 def selected_matrix(w) -> torch.Tensor:
     """[n_units, NK] bool: key block kb is selected by unit u (set semantics:
     LUT entries below the clamped count, inside [0, NK))."""
-    NQ = w.NQ
+    NQ, NK = w.NQ, w.NK
     u = torch.arange(w.n_units)
     qb, h, b = u % NQ, (u // NQ) % w.H, u // (NQ * w.H)
     if w.form == "lut":
@@ -60,11 +60,11 @@ def selected_matrix(w) -> torch.Tensor:
         idx = w.q2k_idx.long()[rows]
         n = w.q2k_num.long()[rows].clamp(0, idx.shape[-1])
         ok = (torch.arange(idx.shape[-1])[None, :] < n[:, None]) & \
-             (idx >= 0) & (idx < NQ)
-        sel = torch.zeros((w.n_units, NQ + 1), dtype=torch.bool)
-        sel.scatter_(1, torch.where(ok, idx, torch.full_like(idx, NQ)),
+             (idx >= 0) & (idx < NK)
+        sel = torch.zeros((w.n_units, NK + 1), dtype=torch.bool)
+        sel.scatter_(1, torch.where(ok, idx, torch.full_like(idx, NK)),
                      torch.ones_like(ok))
-        return sel[:, :NQ]
+        return sel[:, :NK]
     sb, sh = w.mask_strides
     rows = b * sb + h * sh + qb
     return w.mask[rows] != 0
@@ -76,7 +76,7 @@ def attended_pairs(w, units=None) -> int:
     sel = selected_matrix(w)
     if units is not None:
         sel = sel[torch.as_tensor(units, dtype=torch.long)]
-    nv = torch.full((w.NQ,), w.block, dtype=torch.long) if w.vbs is None \
+    nv = torch.full((w.NK,), w.block, dtype=torch.long) if w.vbs is None \
         else w.vbs.long().clamp(0, w.block)
     return int((sel.long() * nv[None, :]).sum()) * w.block
 

@@ -31,11 +31,11 @@ def load():
     lib.bsa_fwd_lut.restype = ctypes.c_int32
     lib.bsa_fwd_lut.argtypes = [
         P, P, P, i32, P, P, P, P, i32, i64, i64, P, f32, P, P,
-        i32, i32, i32, i32, i32, P]
+        i32, i32, i32, i32, i32, i32, i32, P]
     lib.bsa_fwd_bitmap.restype = ctypes.c_int32
     lib.bsa_fwd_bitmap.argtypes = [
         P, P, P, i32, P, P, P, i64, i64, P, f32, P, P,
-        i32, i32, i32, i32, i32, P]
+        i32, i32, i32, i32, i32, i32, i32, P]
     lib.bsa_mask_to_lut.restype = ctypes.c_int32
     lib.bsa_mask_to_lut.argtypes = [P, i64, i32, P, P, P]
     lib.bsa_status_str.restype = ctypes.c_char_p

@@ -59,8 +59,10 @@ def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block):
     if q.dtype != torch.bfloat16 or q.dim() != 4:
         raise TypeError("q must be a 4-D bf16 [B, H, S, D] tensor")
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must have the same [B, H, S, D] shape")
+    if k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] \
+            or k.shape[3] != q.shape[3] or q.shape[1] % k.shape[1] != 0:
+        raise ValueError("q must be [B, H, S, D] and k, v [B, Hk, Sk, D] with "
+                         "H a multiple of Hk")
     kvd = _kv_dtype(k, v)
     if kvd == BSA_KV_FP8E4M3:
         if k_scale is None or v_scale is None:
@@ -90,11 +92,13 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 lse: Optional[torch.Tensor] = None,
                 stream: Optional[torch.cuda.Stream] = None):
     """VSA form.  Returns ``(out, lse)`` (``lse`` is None if not needed).
-    ``meta_strides=(sb, sh)``: the LUT row of (b, h, qb) is
-    ``b*sb + h*sh + qb``; default one row per unit."""
+    ``q`` is ``[B, H, S, D]``, ``k``/``v`` ``[B, Hk, Sk, D]`` (query head h
+    reads K/V head h // (H // Hk)).  ``meta_strides=(sb, sh)``: the LUT row
+    of (b, h, qb) is ``b*sb + h*sh + qb``; default one row per unit."""
     q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
                                               lse, need_lse, block)
     B, H, S, D = q.shape
+    Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
     idx = _i32(q2k_idx)
     num = _i32(q2k_num)
@@ -106,7 +110,7 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     rc = _lib.load().bsa_fwd_lut(
         _ptr(q), _ptr(k), _ptr(v), kvd, _ptr(ks), _ptr(vs), _ptr(idx),
         _ptr(num), int(idx.shape[-1]), int(sb), int(sh), _ptr(vbs),
-        float(sm_scale), _ptr(out), _ptr(lse), B, H, S, D, int(block),
+        float(sm_scale), _ptr(out), _ptr(lse), B, H, Hk, S, Sk, D, int(block),
         ctypes.c_void_p(st))
     if rc != BSA_OK:
         raise BsaError(rc)
@@ -125,10 +129,12 @@ def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    stream: Optional[torch.cuda.Stream] = None):
     """Jenga form.  ``mask`` is an int8 (or bool) tensor of rows of S/block
     bytes; ``mask_strides=(sb, sh)`` as in the LUT form ((0, 0) = one
-    [NQ, NK] mask shared by all batches and heads)."""
+    [NQ, NK] mask shared by all batches and heads).  Shapes as in the LUT
+    form."""
     q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
                                               lse, need_lse, block)
     B, H, S, D = q.shape
+    Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
     m = mask.to(torch.int8).contiguous()
     vbs = _i32(variable_block_sizes)
@@ -139,7 +145,7 @@ def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     rc = _lib.load().bsa_fwd_bitmap(
         _ptr(q), _ptr(k), _ptr(v), kvd, _ptr(ks), _ptr(vs), _ptr(m),
         int(sb), int(sh), _ptr(vbs), float(sm_scale), _ptr(out), _ptr(lse),
-        B, H, S, D, int(block), ctypes.c_void_p(st))
+        B, H, Hk, S, Sk, D, int(block), ctypes.c_void_p(st))
     if rc != BSA_OK:
         raise BsaError(rc)
     return out, lse

@@ -4,7 +4,10 @@
 // qb of head h of batch b.  The steps, in order:
 //
 //  A1  unit id -> (b, h, qb), with workgroups of consecutive ids spread so
-//      that each XCD (and its L2) serves a contiguous range of heads.
+//      that each XCD (and its L2) serves a contiguous range of heads.  Query
+//      head h reads K/V head h / (H/Hk) (grouped-query attention; rocke
+//      "sparse_attention.py" keeps separate query and KV head counts and
+//      query and key lengths, both supported here).
 //  A2  selected-set decode into LDS.  LUT form: the row's first
 //      clamp(num, 0, max_kv) entries are scattered into a byte bitmap
 //      (duplicate stores write the same 1, out-of-range entries are dropped),
@@ -81,7 +84,11 @@ struct FwdParams {
   float* lse;           // or null
   float c;              // sm_scale * log2(e)
   int32_t max_kv;
-  int32_t H, S, NK;
+  int32_t H;            // query heads
+  int32_t group;        // query heads per K/V head (H / Hk)
+  int32_t Hk;           // key/value heads
+  int32_t S, Sk;        // query and key sequence lengths
+  int32_t NQ, NK;       // query blocks, key blocks
   int32_t n_units;
 };
 
@@ -96,8 +103,9 @@ __device__ __forceinline__ int block_valid(const int32_t* vbs, int kb) {
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (id % 8).  Give XCD x the
-// contiguous unit range [x*n/8, (x+1)*n/8) so the units of one head, which
-// share K/V blocks, meet in the same L2.
+// contiguous unit range [x*n/8, (x+1)*n/8) so the units of one head (and of
+// the query heads that share its K/V head), which read the same K/V blocks,
+// meet in the same L2.
 __device__ __forceinline__ int remap_unit(int bid, int n) {
   if (n % 8 != 0) return bid;
   return (bid % 8) * (n / 8) + bid / 8;
@@ -463,11 +471,14 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, FP8>())) void bsa_fwd
 
   // ---- A1: work unit
   const int u = remap_unit(blockIdx.x, p.n_units);
-  const int qb = u % NK;
-  const int bh = u / NK;
+  const int qb = u % p.NQ;
+  const int bh = u / p.NQ;
   const int h = bh % p.H;
   const int b = bh / p.H;
-  const int64_t plane = (int64_t)bh * p.S * HD;  // element offset of (b, h)
+  const int64_t plane = (int64_t)bh * p.S * HD;  // element offset of Q/O (b, h)
+  // query head h reads K/V head h / group (grouped-query attention)
+  const int64_t kvh = (int64_t)b * p.Hk + h / p.group;
+  const int64_t kvplane = kvh * p.Sk * HD;       // element offset of K/V
   const int64_t row = (int64_t)b * p.meta_sb + (int64_t)h * p.meta_sh + qb;
 
   // Zero both stages once: rows that are never loaded must hold finite data.
@@ -524,9 +535,9 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, FP8>())) void bsa_fwd
 
   constexpr int EB = FP8 ? 1 : 2;  // bytes per K/V element in global memory
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
-  const char* kplane = (const char*)p.k + plane * EB;
-  const char* vplane = (const char*)p.v + plane * EB;
-  const int64_t scale_row = (int64_t)bh * NK;  // fp8 scales of (b, h)
+  const char* kplane = (const char*)p.k + kvplane * EB;
+  const char* vplane = (const char*)p.v + kvplane * EB;
+  const int64_t scale_row = kvh * NK;  // fp8 scales of the K/V head
 
   // Per-lane constant byte offsets (the XOR swizzles make every address a
   // per-lane base XORed with a constant): K operand kbase ^ (kk << 6),
@@ -740,18 +751,21 @@ bool aligned16(const void* x) { return ((uintptr_t)x & 15u) == 0; }
 bsa_status check_common(const void* q, const void* k, const void* v,
                         int32_t kv_dtype, const float* k_scale,
                         const float* v_scale, const void* out, int32_t B,
-                        int32_t H, int32_t S, int32_t D, int32_t block) {
+                        int32_t H, int32_t Hk, int32_t S, int32_t Sk,
+                        int32_t D, int32_t block) {
   if (!q || !k || !v || !out) return BSA_ERR_NULL;
-  if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || block <= 0) return BSA_ERR_SHAPE;
-  if (S % block != 0) return BSA_ERR_SHAPE;
+  if (B <= 0 || H <= 0 || Hk <= 0 || S <= 0 || Sk <= 0 || D <= 0 || block <= 0)
+    return BSA_ERR_SHAPE;
+  if (S % block != 0 || Sk % block != 0 || H % Hk != 0) return BSA_ERR_SHAPE;
   if (D != HD) return BSA_ERR_UNSUPPORTED;
   if (block != 64 && block != 128) return BSA_ERR_UNSUPPORTED;
   if (kv_dtype != BSA_KV_BF16 && kv_dtype != BSA_KV_FP8E4M3)
     return BSA_ERR_UNSUPPORTED;
   if (kv_dtype == BSA_KV_FP8E4M3 && (!k_scale || !v_scale)) return BSA_ERR_NULL;
-  if (S / block > BSA_MAX_KEY_BLOCKS) return BSA_ERR_UNSUPPORTED;
+  if (Sk / block > BSA_MAX_KEY_BLOCKS) return BSA_ERR_UNSUPPORTED;
   const int64_t units = (int64_t)B * H * (S / block);
-  if (units > INT32_MAX || (int64_t)B * H * S > INT32_MAX)
+  if (units > INT32_MAX || (int64_t)B * H * S > INT32_MAX ||
+      (int64_t)B * Hk * Sk > INT32_MAX)
     return BSA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return BSA_ERR_ALIGN;
@@ -761,7 +775,8 @@ bsa_status check_common(const void* q, const void* k, const void* v,
 FwdParams make_params(const void* q, const void* k, const void* v,
                       const float* k_scale, const float* v_scale,
                       const int32_t* vbs, float sm_scale, void* out, float* lse,
-                      int32_t B, int32_t H, int32_t S, int32_t block) {
+                      int32_t B, int32_t H, int32_t Hk, int32_t S, int32_t Sk,
+                      int32_t block) {
   FwdParams p{};
   p.q = (const uint16_t*)q;
   p.k = k;
@@ -773,8 +788,12 @@ FwdParams make_params(const void* q, const void* k, const void* v,
   p.lse = lse;
   p.c = sm_scale * LOG2E;
   p.H = H;
+  p.Hk = Hk;
+  p.group = H / Hk;
   p.S = S;
-  p.NK = S / block;
+  p.Sk = Sk;
+  p.NQ = S / block;
+  p.NK = Sk / block;
   p.n_units = B * H * (S / block);
   return p;
 }
@@ -788,15 +807,16 @@ extern "C" bsa_status bsa_fwd_lut(const void* q, const void* k, const void* v,
                                   int64_t meta_stride_b, int64_t meta_stride_h,
                                   const int32_t* variable_block_sizes,
                                   float sm_scale, void* out, float* lse,
-                                  int32_t B, int32_t H, int32_t S, int32_t D,
-                                  int32_t block, void* stream) {
-  bsa_status st =
-      check_common(q, k, v, kv_dtype, k_scale, v_scale, out, B, H, S, D, block);
+                                  int32_t B, int32_t H, int32_t Hk, int32_t S,
+                                  int32_t Sk, int32_t D, int32_t block,
+                                  void* stream) {
+  bsa_status st = check_common(q, k, v, kv_dtype, k_scale, v_scale, out, B, H,
+                               Hk, S, Sk, D, block);
   if (st != BSA_OK) return st;
   if (!q2k_idx || !q2k_num) return BSA_ERR_NULL;
   if (max_kv < 1 || meta_stride_b < 0 || meta_stride_h < 0) return BSA_ERR_SHAPE;
   FwdParams p = make_params(q, k, v, k_scale, v_scale, variable_block_sizes,
-                            sm_scale, out, lse, B, H, S, block);
+                            sm_scale, out, lse, B, H, Hk, S, Sk, block);
   p.idx = q2k_idx;
   p.num = q2k_num;
   p.max_kv = max_kv;
@@ -812,15 +832,16 @@ extern "C" bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v
                                      int64_t mask_stride_b, int64_t mask_stride_h,
                                      const int32_t* variable_block_sizes,
                                      float sm_scale, void* out, float* lse,
-                                     int32_t B, int32_t H, int32_t S, int32_t D,
+                                     int32_t B, int32_t H, int32_t Hk,
+                                     int32_t S, int32_t Sk, int32_t D,
                                      int32_t block, void* stream) {
-  bsa_status st =
-      check_common(q, k, v, kv_dtype, k_scale, v_scale, out, B, H, S, D, block);
+  bsa_status st = check_common(q, k, v, kv_dtype, k_scale, v_scale, out, B, H,
+                               Hk, S, Sk, D, block);
   if (st != BSA_OK) return st;
   if (!mask) return BSA_ERR_NULL;
   if (mask_stride_b < 0 || mask_stride_h < 0) return BSA_ERR_SHAPE;
   FwdParams p = make_params(q, k, v, k_scale, v_scale, variable_block_sizes,
-                            sm_scale, out, lse, B, H, S, block);
+                            sm_scale, out, lse, B, H, Hk, S, Sk, block);
   p.mask = mask;
   p.meta_sb = mask_stride_b;
   p.meta_sh = mask_stride_h;
@@ -832,7 +853,9 @@ extern "C" const char* bsa_status_str(int32_t status) {
   switch (status) {
     case BSA_OK: return "ok";
     case BSA_ERR_NULL: return "a required pointer is NULL";
-    case BSA_ERR_SHAPE: return "invalid size (<= 0, or S not a multiple of block)";
+    case BSA_ERR_SHAPE:
+      return "invalid size (<= 0, S or Sk not a multiple of block, or H not a "
+             "multiple of Hk)";
     case BSA_ERR_UNSUPPORTED:
       return "unsupported configuration (D != 128, block not 64/128, "
              "too many key blocks, or unknown kv dtype)";

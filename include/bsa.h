@@ -55,7 +55,8 @@ extern "C" {
 typedef enum {
   BSA_OK = 0,
   BSA_ERR_NULL = 1,        /* a required pointer is NULL                      */
-  BSA_ERR_SHAPE = 2,       /* a size is <= 0 or S is not a multiple of block  */
+  BSA_ERR_SHAPE = 2,       /* a size is <= 0, S or Sk not a multiple of block,
+                              or H not a multiple of Hk                    */
   BSA_ERR_UNSUPPORTED = 3, /* valid but not built: D != 128, block not 64/128,
                               too many key blocks, unknown kv dtype           */
   BSA_ERR_ALIGN = 4,       /* q, k, v or out not 16-byte aligned              */
@@ -75,14 +76,15 @@ typedef enum {
  * bsa_fwd_lut -- VSA (look-up-table) form.
  *
  *  q            bf16 [B, H, S, D], contiguous (BHSD), 16-byte aligned.
- *  k, v         [B, H, S, D] contiguous, bf16 or fp8 e4m3 per kv_dtype,
- *               16-byte aligned.
+ *  k, v         [B, Hk, Sk, D] contiguous, bf16 or fp8 e4m3 per kv_dtype,
+ *               16-byte aligned.  Query head h reads K/V head h / (H/Hk)
+ *               (grouped-query attention; Hk = H is ordinary attention).
  *  kv_dtype     a bsa_kv_dtype value.
- *  k_scale,     fp32 [B, H, S/block]: per-(b, h, key block) scales; required
- *  v_scale      for BSA_KV_FP8E4M3, ignored (may be NULL) for bf16.
+ *  k_scale,     fp32 [B, Hk, Sk/block]: per-(b, K/V head, key block) scales;
+ *  v_scale      required for BSA_KV_FP8E4M3, ignored (may be NULL) for bf16.
  *  q2k_idx      int32 rows x max_kv: selected key-block indices of a row.
  *               Only entries below the row's count are read.  Entries
- *               outside [0, S/block) are skipped; order and repetitions do
+ *               outside [0, Sk/block) are skipped; order and repetitions do
  *               not matter (the row is a set).
  *  q2k_num      int32 per row: the count, clamped to [0, max_kv].
  *  max_kv       row length of q2k_idx (>= 1).
@@ -92,14 +94,18 @@ typedef enum {
  *               (H*S/block, S/block) = one row per unit; (0, 0) = one
  *               [S/block, max_kv] table shared by every batch and head.
  *  variable_block_sizes
- *               int32 [S/block] shared by every batch and head: valid keys
+ *               int32 [Sk/block] shared by every batch and head: valid keys
  *               of each key block, clamped to [0, block]; keys at or past it
  *               are masked.  NULL = every block full.
  *  sm_scale     natural-log softmax scale (1/sqrt(D) is the usual value).
  *  out          bf16 [B, H, S, D] contiguous, 16-byte aligned; every element
  *               is written.
  *  lse          fp32 [B, H, S] base-2 LSE, or NULL to skip it.
- *  B, H, S, D   sizes; D must be 128, S a multiple of block.
+ *  B, H, Hk     batch, query heads, key/value heads (H a multiple of Hk).
+ *  S, Sk        query and key sequence lengths, multiples of block
+ *               (rocke "sparse_attention.py" specs carry seqlen_q and
+ *               seqlen_k and separate query / KV head counts).
+ *  D            head dimension; must be 128.
  *  block        64 or 128: the query-block and key-block size.
  *  stream       hipStream_t (void*), NULL = null stream.
  */
@@ -109,18 +115,20 @@ bsa_status bsa_fwd_lut(const void* q, const void* k, const void* v,
                        const int32_t* q2k_num, int32_t max_kv,
                        int64_t meta_stride_b, int64_t meta_stride_h,
                        const int32_t* variable_block_sizes, float sm_scale,
-                       void* out, float* lse, int32_t B, int32_t H, int32_t S,
-                       int32_t D, int32_t block, void* stream);
+                       void* out, float* lse, int32_t B, int32_t H, int32_t Hk,
+                       int32_t S, int32_t Sk, int32_t D, int32_t block,
+                       void* stream);
 
 /*
  * bsa_fwd_bitmap -- Jenga (bitmap) form.  Arguments as bsa_fwd_lut, except:
  *
- *  mask         int8 rows x (S/block): nonzero = the key block is attended
+ *  mask         int8 rows x (Sk/block): nonzero = the key block is attended
  *               (rocke "sparse_attention.py", module docstring).
  *  mask_stride_b, mask_stride_h
  *               the mask row of unit (b, h, qb) is
  *               b*mask_stride_b + h*mask_stride_h + qb (in rows);
- *               (0, 0) = one [S/block, S/block] mask for every batch and head.
+ *               (0, 0) = one [S/block, Sk/block] mask for every batch and
+ *               head.
  */
 bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v,
                           int32_t kv_dtype, const float* k_scale,
@@ -128,7 +136,8 @@ bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v,
                           int64_t mask_stride_b, int64_t mask_stride_h,
                           const int32_t* variable_block_sizes, float sm_scale,
                           void* out, float* lse, int32_t B, int32_t H,
-                          int32_t S, int32_t D, int32_t block, void* stream);
+                          int32_t Hk, int32_t S, int32_t Sk, int32_t D,
+                          int32_t block, void* stream);
 
 /*
  * bsa_mask_to_lut -- compaction of a block map into the look-up-table form

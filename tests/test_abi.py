@@ -48,15 +48,15 @@ A = 0x10000
 def lut(**over):
     args = dict(q=A, k=A, v=A, kv=0, ks=None, vs=None, idx=A, num=A, max_kv=4,
                 sb=8, sh=8, vbs=None, scale=0.1, out=A, lse=None, B=1, H=1,
-                S=512, D=128, block=64, stream=None)
+                Hk=1, S=512, Sk=512, D=128, block=64, stream=None)
     args.update(over)
     return _lib.load().bsa_fwd_lut(*args.values())
 
 
 def bitmap(**over):
     args = dict(q=A, k=A, v=A, kv=0, ks=None, vs=None, mask=A, sb=8, sh=8,
-                vbs=None, scale=0.1, out=A, lse=None, B=1, H=1, S=512, D=128,
-                block=64, stream=None)
+                vbs=None, scale=0.1, out=A, lse=None, B=1, H=1, Hk=1, S=512,
+                Sk=512, D=128, block=64, stream=None)
     args.update(over)
     return _lib.load().bsa_fwd_bitmap(*args.values())
 
@@ -73,13 +73,18 @@ def bitmap(**over):
     (dict(B=0), api.BSA_ERR_SHAPE),
     (dict(H=-1), api.BSA_ERR_SHAPE),
     (dict(S=500), api.BSA_ERR_SHAPE),           # not a multiple of block
+    (dict(Sk=500), api.BSA_ERR_SHAPE),
+    (dict(Sk=0), api.BSA_ERR_SHAPE),
+    (dict(H=6, Hk=4), api.BSA_ERR_SHAPE),       # H not a multiple of Hk
+    (dict(Hk=0), api.BSA_ERR_SHAPE),
     (dict(max_kv=0), api.BSA_ERR_SHAPE),
     (dict(sb=-1), api.BSA_ERR_SHAPE),
     (dict(D=64), api.BSA_ERR_UNSUPPORTED),
     (dict(block=32, S=512), api.BSA_ERR_UNSUPPORTED),
     (dict(block=256, S=512), api.BSA_ERR_UNSUPPORTED),
     (dict(kv=7), api.BSA_ERR_UNSUPPORTED),
-    (dict(S=64 * 16385), api.BSA_ERR_UNSUPPORTED),  # > BSA_MAX_KEY_BLOCKS
+    (dict(S=64 * 16385, Sk=64 * 16385), api.BSA_ERR_UNSUPPORTED),
+    (dict(Sk=64 * 16385), api.BSA_ERR_UNSUPPORTED),  # > BSA_MAX_KEY_BLOCKS
     (dict(q=A + 8), api.BSA_ERR_ALIGN),
     (dict(out=A + 2), api.BSA_ERR_ALIGN),
 ])
@@ -91,6 +96,8 @@ def test_lut_rejects_invalid_static_arguments(over, status):
     (dict(mask=None), api.BSA_ERR_NULL),
     (dict(q=None), api.BSA_ERR_NULL),
     (dict(S=100), api.BSA_ERR_SHAPE),
+    (dict(Sk=96), api.BSA_ERR_SHAPE),
+    (dict(H=3, Hk=2), api.BSA_ERR_SHAPE),
     (dict(sh=-3), api.BSA_ERR_SHAPE),
     (dict(D=256), api.BSA_ERR_UNSUPPORTED),
     (dict(v=A + 4), api.BSA_ERR_ALIGN),

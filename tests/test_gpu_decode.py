@@ -28,7 +28,7 @@ def _need_gpu():
 
 
 def _one_hot_v(w, chunk):
-    S, D, blk = w.S, w.D, w.block
+    S, D, blk = w.Sk, w.D, w.block
     key_block = torch.arange(S) // blk
     col = key_block - D * chunk
     v1 = torch.zeros((S, D), dtype=torch.float32)
@@ -39,7 +39,7 @@ def _one_hot_v(w, chunk):
 
 def decode_counts_gpu(w):
     """[n_units, NK] integer counts recovered from the kernel's outputs."""
-    NK = w.NQ
+    NK = w.NK
     counts = np.zeros((w.n_units, NK), dtype=np.int64)
     q0 = torch.zeros_like(w.q)
     nchunks = (NK + w.D - 1) // w.D
@@ -47,11 +47,11 @@ def decode_counts_gpu(w):
     for chunk in range(nchunks):
         v1 = _one_hot_v(w, chunk)
         if w.kv_fp8:
-            v = v1.expand(w.B, w.H, w.S, w.D).to(torch.float8_e4m3fn)
+            v = v1.expand(w.B, w.Hk, w.Sk, w.D).to(torch.float8_e4m3fn)
             ks = torch.ones_like(w.k_scale)
             vs = torch.ones_like(w.v_scale)
         else:
-            v = v1.expand(w.B, w.H, w.S, w.D).to(torch.bfloat16)
+            v = v1.expand(w.B, w.Hk, w.Sk, w.D).to(torch.bfloat16)
             ks = vs = None
         import copy
         w2 = copy.copy(w)
@@ -73,20 +73,34 @@ def decode_counts_gpu(w):
 
 
 CASES = [("tiny", 0), ("jenga_bitmap", 1), ("video_lut", 2),
-         ("blk128_counts0to64", 3), ("fp8kv", 4)]
+         ("blk128_counts0to64", 3), ("fp8kv", 4),
+         # grouped K/V heads with key length != query length
+         ("gqa_rect_lut", dict(seed=301, B=2, H=4, Hk=2, S=512, Sk=9216,
+                               block=64, count_mode="uniform", max_kv=48,
+                               vbs_mode="random")),
+         ("gqa_rect_bitmap128", dict(seed=302, B=1, H=3, Hk=1, S=1024, Sk=512,
+                                     block=128, form="bitmap", density=0.5,
+                                     vbs_mode="zero_some")),
+         ("gqa_fp8", dict(seed=303, B=1, H=4, Hk=1, S=256, Sk=1024, block=64,
+                          kv="fp8", density=0.4))]
 
 
 @pytest.mark.parametrize("label,cfg", CASES, ids=[c[0] for c in CASES])
 def test_decode_is_bit_exact_on_named_workloads(label, cfg):
-    w = workloads.make_config(cfg)
-    log(f"[decode] {w.name} units={w.n_units}")
+    if isinstance(cfg, int):
+        w = workloads.make_config(cfg)
+    else:
+        kw = dict(cfg)
+        w = workloads.make_random(kw.pop("seed"), **kw)
+    log(f"[decode] {w.name} units={w.n_units} H={w.H} Hk={w.Hk} S={w.S} "
+        f"Sk={w.Sk}")
     got, n_att = decode_counts_gpu(w)
     if w.form == "lut":
-        want = oracle.key_counts(B=w.B, H=w.H, S=w.S, block=w.block,
+        want = oracle.key_counts(B=w.B, H=w.H, S=w.S, Sk=w.Sk, block=w.block,
                                  q2k_idx=w.q2k_idx, q2k_num=w.q2k_num,
                                  vbs=w.vbs, meta_strides=w.meta_strides)
     else:
-        want = oracle.key_counts(B=w.B, H=w.H, S=w.S, block=w.block,
+        want = oracle.key_counts(B=w.B, H=w.H, S=w.S, Sk=w.Sk, block=w.block,
                                  mask=w.mask, vbs=w.vbs,
                                  mask_strides=w.mask_strides)
     empty = want.sum(axis=1) == 0

@@ -56,6 +56,20 @@ SMALL = [
     ("lut64_long_nk1024", dict(seed=117, B=1, H=1, S=65536, block=64,
                                max_kv=40, density=0.0006, count_mode="uniform",
                                vbs_mode="partial")),
+    # grouped K/V heads (query head h reads K/V head h // (H // Hk)) and
+    # query length != key length
+    ("gqa_lut64", dict(seed=118, B=2, H=4, Hk=2, S=512, block=64,
+                       count_mode="uniform", vbs_mode="random")),
+    ("gqa_bitmap128", dict(seed=119, B=1, H=6, Hk=1, S=1024, block=128,
+                           form="bitmap", density=0.4, vbs_mode="partial")),
+    ("rect_q_short", dict(seed=120, B=1, H=2, S=256, Sk=1024, block=64,
+                          density=0.5, vbs_mode="partial")),
+    ("rect_q_long", dict(seed=121, B=2, H=2, Hk=1, S=1024, Sk=256, block=64,
+                         count_mode="uniform", vbs_mode="zero_some")),
+    ("gqa_fp8_rect", dict(seed=122, B=1, H=4, Hk=2, S=512, Sk=768, block=64,
+                          kv="fp8", density=0.5, vbs_mode="random")),
+    ("gqa_rect128_shared", dict(seed=123, B=2, H=4, Hk=4, S=512, Sk=1536,
+                                block=128, shared_meta=True, density=0.3)),
 ]
 
 
@@ -63,7 +77,7 @@ SMALL = [
 def test_small_random_parity(label, kw):
     kw = dict(kw)
     w = workloads.make_random(kw.pop("seed"), **kw)
-    log(f"[parity] {label} B{w.B} H{w.H} S{w.S} blk{w.block} form={w.form} "
+    log(f"[parity] {label} B{w.B} H{w.H} Hk{w.Hk} S{w.S} Sk{w.Sk} blk{w.block} form={w.form} "
         f"fp8={w.kv_fp8}")
     out, lse = run_gpu(w)
     units = None
