@@ -82,16 +82,19 @@ def attended_pairs(w, units=None) -> int:
 
 
 def launch(w, d, out, lse):
+    """One forward pass; lse=None is the inference route (no LSE store)."""
     if w.form == "lut":
         bsa.bsa_fwd_lut(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"],
                         d["vbs"], block=w.block, sm_scale=w.sm_scale,
                         k_scale=d["k_scale"], v_scale=d["v_scale"],
-                        meta_strides=w.meta_strides, out=out, lse=lse)
+                        meta_strides=w.meta_strides, out=out, lse=lse,
+                        need_lse=lse is not None)
     else:
         bsa.bsa_fwd_bitmap(d["q"], d["k"], d["v"], d["mask"], d["vbs"],
                            block=w.block, sm_scale=w.sm_scale,
                            k_scale=d["k_scale"], v_scale=d["v_scale"],
-                           mask_strides=w.mask_strides, out=out, lse=lse)
+                           mask_strides=w.mask_strides, out=out, lse=lse,
+                           need_lse=lse is not None)
 
 
 def stored_traffic(workload_name: str):
@@ -247,6 +250,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2,
                     help="named workload index (default 2: video-shaped VSA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lse", action="store_true",
+                    help="inference route: the forward pass without the LSE "
+                         "output")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the "
@@ -293,7 +299,8 @@ def main() -> int:
          for n in ("q", "k", "v", "k_scale", "v_scale", "q2k_idx", "q2k_num",
                    "mask", "vbs")}
     out = torch.empty(tuple(w.q.shape), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    lse = None if args.no_lse else torch.empty((w.B, w.H, w.S),
+                                               dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     progress(f"warmup {args.warmup} steps on {w.name}")
@@ -333,7 +340,7 @@ def main() -> int:
         "config": {
             "workload": w.name,
             "B": w.B, "H": w.H, "S": w.S, "D": w.D, "block": w.block,
-            "form": w.form,
+            "form": w.form, "need_lse": not args.no_lse,
             "attended_pairs": pairs,
             "effective_flop_per_step": flop,
             "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
