@@ -1,4 +1,5 @@
-"""CPU oracle for block-sparse attention forward -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for block-sparse attention (forward and its gradients) -- TEST
+INFRASTRUCTURE ONLY.
 
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -12,6 +13,7 @@ from .oracle import (  # noqa: F401
     LSE_EMPTY,
     bf16_value,
     build,
+    bwd,
     fp8e4m3_value,
     fwd_bitmap,
     fwd_lut,

@@ -319,6 +319,146 @@ int bsa_oracle_key_counts(int form, const int32_t* q2k_idx,
   return 0;
 }
 
+/* ---- backward pass (gradients of the forward definition) ------------- */
+
+/* For one work unit, the plain chain rule of softmax attention over the
+ * unit's attended keys, in natural-log units (the base-2 form of the forward
+ * pass is the same function):
+ *   s_j  = sm_scale * (q_r . k_j),  p_j = e^(s_j - m) / sum_i e^(s_i - m)
+ *   O_r  = sum_j p_j v_j
+ *   dv_j += p_j dO_r
+ *   dp_j  = dO_r . v_j,   delta = sum_j p_j dp_j  (= dO_r . O_r)
+ *   ds_j  = p_j (dp_j - delta)
+ *   dq_r  = sm_scale * sum_j ds_j k_j,   dk_j += sm_scale * ds_j q_r
+ * A row with no attended key has no dependence on K or V and dq_r = 0.
+ * K/V head kvh = h / (H/Hk) receives the gradients of all its query heads. */
+static void backward_unit(const attn_args* a, const uint16_t* dout, int32_t b,
+                          int32_t h, int32_t qb, const unsigned char* sel,
+                          int64_t* keys, double* s, double* dp, double* qd,
+                          double* dod, double* dq, double* dk, double* dv) {
+  const int32_t D = a->D, block = a->block, NK = a->Sk / block;
+  const int64_t qplane = ((int64_t)b * a->H + h) * (int64_t)a->Sq * D;
+  const int64_t kvhead = (int64_t)b * a->Hk + h / (a->H / a->Hk);
+  const int64_t plane = kvhead * (int64_t)a->Sk * D;
+
+  int64_t n_att = 0;
+  for (int32_t kb = 0; kb < NK; ++kb) {
+    if (!sel[kb]) continue;
+    int32_t nv = block_valid(a->vbs, kb, block);
+    for (int32_t tt = 0; tt < nv; ++tt) keys[n_att++] = (int64_t)kb * block + tt;
+  }
+  if (n_att == 0) return; /* dq rows stay 0 */
+
+  for (int32_t r = 0; r < block; ++r) {
+    const int64_t qrow = qplane + ((int64_t)qb * block + r) * D;
+    for (int32_t d = 0; d < D; ++d) {
+      qd[d] = bsa_oracle_bf16_value(a->q[qrow + d]);
+      dod[d] = bsa_oracle_bf16_value(dout[qrow + d]);
+    }
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n_att; ++j) {
+      const int64_t krow = plane + keys[j] * D;
+      double acc = 0.0;
+      for (int32_t d = 0; d < D; ++d)
+        acc += qd[d] * bsa_oracle_bf16_value(((const uint16_t*)a->k)[krow + d]);
+      s[j] = acc * a->sm_scale;
+      if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < n_att; ++j) {
+      s[j] = exp(s[j] - m); /* unnormalised weight */
+      l += s[j];
+    }
+    double delta = 0.0;
+    for (int64_t j = 0; j < n_att; ++j) {
+      const int64_t vrow = plane + keys[j] * D;
+      s[j] /= l; /* p_j */
+      double acc = 0.0;
+      for (int32_t d = 0; d < D; ++d)
+        acc += dod[d] * bsa_oracle_bf16_value(((const uint16_t*)a->v)[vrow + d]);
+      dp[j] = acc;
+      delta += s[j] * acc;
+    }
+    double* dqr = dq + qrow;
+    for (int64_t j = 0; j < n_att; ++j) {
+      const int64_t row = plane + keys[j] * D;
+      const double ds = s[j] * (dp[j] - delta);
+      for (int32_t d = 0; d < D; ++d) {
+        dqr[d] += a->sm_scale * ds *
+                  bsa_oracle_bf16_value(((const uint16_t*)a->k)[row + d]);
+        dk[row + d] += a->sm_scale * ds * qd[d];
+        dv[row + d] += s[j] * dod[d];
+      }
+    }
+  }
+}
+
+int bsa_oracle_bwd(int form, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* v, const uint16_t* dout,
+                   const int32_t* q2k_idx, const int32_t* q2k_num,
+                   int32_t max_kv, const int8_t* mask, int64_t meta_stride_b,
+                   int64_t meta_stride_h, const int32_t* vbs, double sm_scale,
+                   int32_t B, int32_t H, int32_t Hk, int32_t Sq, int32_t Sk,
+                   int32_t D, int32_t block, double* dq, double* dk,
+                   double* dv) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
+  if (check_dims(B, H, Hk, Sq, Sk, D, block)) return 1;
+  if (form == FORM_LUT && (!q2k_idx || !q2k_num || max_kv < 1)) return 1;
+  if (form == FORM_BITMAP && !mask) return 1;
+  if (form != FORM_LUT && form != FORM_BITMAP) return 1;
+  attn_args a = {q, k, v, ORACLE_KV_BF16, NULL, NULL, vbs, sm_scale, H, Hk,
+                 Sq, Sk, D, block};
+  sel_args s;
+  if (form == FORM_LUT) {
+    sel_args t = {FORM_LUT, q2k_idx, q2k_num, max_kv, meta_stride_b,
+                  meta_stride_h, NULL};
+    s = t;
+  } else {
+    sel_args t = {FORM_BITMAP, NULL, NULL, 0, meta_stride_b, meta_stride_h,
+                  mask};
+    s = t;
+  }
+  const int32_t NQ = Sq / block, NK = Sk / block, G = H / Hk;
+  memset(dq, 0, sizeof(double) * (size_t)B * H * Sq * D);
+  memset(dk, 0, sizeof(double) * (size_t)B * Hk * Sk * D);
+  memset(dv, 0, sizeof(double) * (size_t)B * Hk * Sk * D);
+  int failed = 0;
+  /* one (batch, K/V head) group per iteration: it owns its dk/dv rows and
+   * the dq rows of its query heads */
+#pragma omp parallel
+  {
+    unsigned char* sel = (unsigned char*)malloc((size_t)NK);
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)Sk);
+    double* sv = (double*)malloc(sizeof(double) * (size_t)Sk);
+    double* dpv = (double*)malloc(sizeof(double) * (size_t)Sk);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+    double* dod = (double*)malloc(sizeof(double) * (size_t)D);
+    const int ok = sel && keys && sv && dpv && qd && dod;
+    if (!ok) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t grp = 0; grp < (int64_t)B * Hk; ++grp) {
+      if (!ok) continue;
+      const int32_t b = (int32_t)(grp / Hk), kvh = (int32_t)(grp % Hk);
+      for (int32_t h = kvh * G; h < (kvh + 1) * G; ++h)
+        for (int32_t qb = 0; qb < NQ; ++qb) {
+          unit_select(&s, b, h, qb, NK, sel);
+          backward_unit(&a, dout, b, h, qb, sel, keys, sv, dpv, qd, dod, dq,
+                        dk, dv);
+        }
+    }
+    free(sel);
+    free(keys);
+    free(sv);
+    free(dpv);
+    free(qd);
+    free(dod);
+  }
+  return failed ? 3 : 0;
+}
+
 int bsa_oracle_mask_to_lut(const int8_t* mask, int64_t rows, int32_t NK,
                            int32_t* idx, int32_t* num) {
   if (!mask || !idx || !num || rows < 0 || NK <= 0) return 1;

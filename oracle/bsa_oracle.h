@@ -107,6 +107,21 @@ int bsa_oracle_key_counts(int form, const int32_t* q2k_idx,
                           const int64_t* units, int64_t n_units,
                           int32_t* counts);
 
+/* Gradients (dq [B,H,Sq,D], dk and dv [B,Hk,Sk,D], fp64, overwritten) of
+ * sum(O * dout) for the forward pass with bf16 K/V, by the plain chain rule
+ * of softmax attention over each unit's attended keys.  form 0 = LUT
+ * (q2k_idx/q2k_num/max_kv), form 1 = bitmap (mask); meta_stride_b/h give
+ * the metadata row of (b, h, qb) for either form.  dout: bf16 bits
+ * [B,H,Sq,D].  Query rows with no attended key get dq = 0. */
+int bsa_oracle_bwd(int form, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* v, const uint16_t* dout,
+                   const int32_t* q2k_idx, const int32_t* q2k_num,
+                   int32_t max_kv, const int8_t* mask, int64_t meta_stride_b,
+                   int64_t meta_stride_h, const int32_t* vbs, double sm_scale,
+                   int32_t B, int32_t H, int32_t Hk, int32_t Sq, int32_t Sk,
+                   int32_t D, int32_t block, double* dq, double* dk,
+                   double* dv);
+
 /* Compaction of a bitmap into the LUT form: for each of `rows` rows of NK
  * bytes, idx[row][0..n) = ascending positions of the nonzero bytes, the rest
  * of the row = -1, num[row] = n.  idx is rows x NK. */

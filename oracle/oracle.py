@@ -60,6 +60,10 @@ def _lib():
         lib.bsa_oracle_key_counts.argtypes = [
             ctypes.c_int, P, P, i32, i64, i64, P, i64, i64, P,
             i32, i32, i32, i32, i32, P, i64, P]
+        lib.bsa_oracle_bwd.restype = ctypes.c_int
+        lib.bsa_oracle_bwd.argtypes = [
+            ctypes.c_int, P, P, P, P, P, P, i32, P, i64, i64, P, f64,
+            i32, i32, i32, i32, i32, i32, i32, P, P, P]
         lib.bsa_oracle_mask_to_lut.restype = ctypes.c_int
         lib.bsa_oracle_mask_to_lut.argtypes = [P, i64, i32, P, P]
         lib.bsa_oracle_num_threads.restype = ctypes.c_int
@@ -213,6 +217,46 @@ def key_counts(*, B, H, S, block, q2k_idx=None, q2k_num=None, mask=None,
     if rc != 0:
         raise ValueError(f"bsa_oracle_key_counts failed (rc={rc})")
     return counts
+
+
+def bwd(q, k, v, dout, *, block, q2k_idx=None, q2k_num=None, mask=None,
+        vbs=None, sm_scale=None, meta_strides=None):
+    """Oracle backward (bf16 K/V): gradients ``(dq, dk, dv)`` of
+    ``sum(O * dout)``, float64 numpy arrays shaped like q, k, v.  LUT form if
+    ``q2k_idx`` is given, else bitmap form (``mask``); ``meta_strides``
+    addresses the metadata rows of either form (default one row per
+    unit)."""
+    B, H, S, D = q.shape
+    Hk, Sk = int(k.shape[1]), int(k.shape[2])
+    NQ = S // block
+    qb_, kb_, vb_, kdt, _, _ = _common(q, k, v, None, None)
+    assert kdt == KV_BF16, "the backward pass takes bf16 K/V"
+    do = _cpu(dout)
+    assert do.dtype == torch.bfloat16 and tuple(do.shape) == tuple(q.shape)
+    do = do.view(torch.int16)
+    sb, sh = meta_strides if meta_strides is not None else (H * NQ, NQ)
+    vbs_t = None if vbs is None else _cpu(vbs.to(torch.int32))
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    dq = np.empty((B, H, S, D))
+    dk = np.empty((B, Hk, Sk, D))
+    dv = np.empty((B, Hk, Sk, D))
+    if q2k_idx is not None:
+        idx = _cpu(q2k_idx.to(torch.int32))
+        num = _cpu(q2k_num.to(torch.int32))
+        form, max_kv, m = 0, int(idx.shape[-1]), None
+    else:
+        idx = num = None
+        form, max_kv, m = 1, 0, _cpu(mask.to(torch.int8))
+    rc = _lib().bsa_oracle_bwd(
+        form, _ptr(qb_), _ptr(kb_), _ptr(vb_), _ptr(do), _ptr(idx), _ptr(num),
+        max_kv, _ptr(m), sb, sh, _ptr(vbs_t), float(sm_scale),
+        B, H, Hk, S, Sk, D, block,
+        dq.ctypes.data_as(ctypes.c_void_p), dk.ctypes.data_as(ctypes.c_void_p),
+        dv.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError(f"bsa_oracle_bwd failed (rc={rc})")
+    return dq, dk, dv
 
 
 def mask_to_lut(mask):

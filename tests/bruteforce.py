@@ -91,3 +91,28 @@ def attention(w, mask=None):
     o = np.where(any_key[..., None], o, 0.0)
     lse2 = np.where(any_key, lse_e / np.log(2.0), LSE_EMPTY)
     return o, lse2
+
+
+def grads_autograd(w, dout, mask=None):
+    """(dq, dk, dv) of sum(O * dout) by torch autograd through a dense
+    float64 masked softmax (bf16 K/V; GQA by repeating K/V heads, whose
+    gradients autograd sums back).  Rows with no attended key output 0."""
+    if mask is None:
+        mask = dense_mask(w)
+    m = torch.from_numpy(mask)
+    q = w.q.to(torch.float64).requires_grad_(True)
+    k = w.k.to(torch.float64).requires_grad_(True)
+    v = w.v.to(torch.float64).requires_grad_(True)
+    group = w.H // w.Hk
+    kr = k.repeat_interleave(group, dim=1)
+    vr = v.repeat_interleave(group, dim=1)
+    logits = torch.matmul(q, kr.transpose(-1, -2)) * w.sm_scale
+    a = torch.where(m, logits, torch.full_like(logits, -torch.inf))
+    mx = a.max(dim=-1, keepdim=True).values.detach()
+    mx = torch.where(torch.isfinite(mx), mx, torch.zeros_like(mx))
+    e = torch.where(m, torch.exp(a - mx), torch.zeros_like(a))
+    den = e.sum(dim=-1, keepdim=True)
+    p = e / torch.where(den > 0, den, torch.ones_like(den))
+    o = torch.matmul(p, vr)
+    (o * dout.to(torch.float64)).sum().backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
