@@ -34,8 +34,8 @@ import workloads  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_attention_tile_amd", "csrc",
-                             "bsa_fwd.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_tile_amd", "csrc",
+                               f) for f in ("bsa_fwd.hip", "bsa_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsa_fwd_traffic.json")
 
 
@@ -44,8 +44,13 @@ def progress(msg: str) -> None:
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernel's sources (the stored counter figures
+    apply only to the kernel they were taken on)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def selected_matrix(w) -> torch.Tensor:

@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     BSA_OK,
     LSE_EMPTY,
     BsaError,
+    bsa_bwd,
     bsa_fwd_bitmap,
     bsa_fwd_from_mask,
     bsa_fwd_lut,

@@ -11,7 +11,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsa.so")
 
 # The exported C symbols, as declared in include/bsa.h.
-EXPORTS = ("bsa_fwd_lut", "bsa_fwd_bitmap", "bsa_mask_to_lut", "bsa_status_str")
+EXPORTS = ("bsa_fwd_lut", "bsa_fwd_bitmap", "bsa_mask_to_lut",
+           "bsa_bwd_workspace_size", "bsa_bwd_lut", "bsa_bwd_bitmap",
+           "bsa_status_str")
 
 _lib = None
 
@@ -38,6 +40,17 @@ def load():
         i32, i32, i32, i32, i32, i32, i32, P]
     lib.bsa_mask_to_lut.restype = ctypes.c_int32
     lib.bsa_mask_to_lut.argtypes = [P, i64, i32, P, P, P]
+    sz = ctypes.c_size_t
+    lib.bsa_bwd_workspace_size.restype = sz
+    lib.bsa_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.bsa_bwd_lut.restype = ctypes.c_int32
+    lib.bsa_bwd_lut.argtypes = [
+        P, P, P, P, P, P, P, P, i32, i64, i64, P, f32, P, P, P, P, sz,
+        i32, i32, i32, i32, i32, i32, i32, P]
+    lib.bsa_bwd_bitmap.restype = ctypes.c_int32
+    lib.bsa_bwd_bitmap.argtypes = [
+        P, P, P, P, P, P, P, i64, i64, P, f32, P, P, P, P, sz,
+        i32, i32, i32, i32, i32, i32, i32, P]
     lib.bsa_status_str.restype = ctypes.c_char_p
     lib.bsa_status_str.argtypes = [i32]
     _lib = lib

@@ -184,3 +184,57 @@ def bsa_fwd_from_mask(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                            num.reshape(-1), variable_block_sizes, block=block,
                            meta_strides=mask_strides, **kw)
     return out, lse, idx, num
+
+
+def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, *,
+            block: int, q2k_idx: Optional[torch.Tensor] = None,
+            q2k_num: Optional[torch.Tensor] = None,
+            mask: Optional[torch.Tensor] = None,
+            variable_block_sizes: Optional[torch.Tensor] = None,
+            sm_scale: Optional[float] = None,
+            meta_strides: Optional[Tuple[int, int]] = None,
+            workspace: Optional[torch.Tensor] = None,
+            stream: Optional[torch.cuda.Stream] = None):
+    """Gradients ``(dq, dk, dv)`` of ``sum(out * dout)`` for the forward pass
+    that produced ``out`` and ``lse`` from the same inputs (bf16 K/V).  LUT
+    form if ``q2k_idx`` is given, else bitmap form (``mask``);
+    ``meta_strides`` addresses the metadata rows of either form.  The
+    workspace (delta and the key-block -> query-block map) is allocated here
+    unless given (uint8, at least ``bsa_bwd_workspace_size`` bytes)."""
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or \
+            v.dtype != torch.bfloat16:
+        raise TypeError("the backward pass takes bf16 q, k, v")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    out, dout = out.contiguous(), dout.to(torch.bfloat16).contiguous()
+    lse = lse.to(torch.float32).contiguous()
+    B, H, S, D = q.shape
+    Hk, Sk = int(k.shape[1]), int(k.shape[2])
+    NQ = S // block
+    lib = _lib.load()
+    need = int(lib.bsa_bwd_workspace_size(B, H, S, Sk, int(block)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    vbs = _i32(variable_block_sizes)
+    sb, sh = meta_strides if meta_strides is not None else (H * NQ, NQ)
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    st = ctypes.c_void_p((stream or torch.cuda.current_stream(q.device)).cuda_stream)
+    common_tail = (float(sm_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                   int(workspace.numel()), B, H, Hk, S, Sk, D, int(block), st)
+    if q2k_idx is not None:
+        idx, num = _i32(q2k_idx), _i32(q2k_num)
+        rc = lib.bsa_bwd_lut(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                             _ptr(lse), _ptr(idx), _ptr(num), int(idx.shape[-1]),
+                             int(sb), int(sh), _ptr(vbs), *common_tail)
+    else:
+        m = mask.to(torch.int8).contiguous()
+        rc = lib.bsa_bwd_bitmap(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                _ptr(lse), _ptr(m), int(sb), int(sh), _ptr(vbs),
+                                *common_tail)
+    if rc != BSA_OK:
+        raise BsaError(rc)
+    return dq, dk, dv

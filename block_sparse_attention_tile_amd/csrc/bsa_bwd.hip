@@ -1,0 +1,721 @@
+// bsa_bwd.hip -- gradients of the block-sparse attention forward pass on
+// MI355X (gfx950).
+//
+// The forward pass returns O and the base-2 row LSE so that a backward pass
+// can rebuild the softmax weights without a second reduction (FastVideo
+// "block_sparse_attn_sm100a.py": the LSE-producing path is kept for
+// forward/backward pairing).  With t = (q . k) * sm_scale * log2(e):
+//
+//   P  = 2^(t - LSE)                (the forward weights, normalised)
+//   dP = dO V^T,   delta = rowsum(dO * O),   dS = P * (dP - delta)
+//   dQ = sm_scale * dS K,  dK = sm_scale * dS^T Q,  dV = P^T dO
+//
+// over each unit's attended keys.  Four launches:
+//   1. delta_kernel     delta[row] = sum_d O * dO (fp32), one pass over O, dO.
+//   2. k2q_kernel       the transposed selection: for every (b, K/V head,
+//                       key block) a byte per (query head of the group,
+//                       query block) that attends it (1 = attends, the key
+//                       block has >= 1 valid key).  Duplicate stores write
+//                       the same 1, so no atomics are needed.
+//   3. dq_kernel        one workgroup per query unit, the same selected-block
+//                       walk as the forward pass; dQ accumulates in
+//                       registers and is written once.
+//   4. dkdv_kernel      one workgroup per (b, K/V head, key block): its keys
+//                       stay in registers while it walks every query unit
+//                       that attends the block (from the byte map), so dK and
+//                       dV are complete in one workgroup -- grouped query
+//                       heads included -- and written once, without atomics.
+//
+// All MFMA work is v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32
+// accumulation); P and dS are rounded to bf16 as operands, the outputs to
+// bf16 (RNE).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bsa.h"
+#include "bsa_device.h"
+
+namespace {
+
+constexpr int BSTAGE = 2 * TILE_BYTES;  // two 32-row tiles per stage
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;
+  const float* delta;
+  const int32_t* idx;   // LUT form
+  const int32_t* num;
+  const int8_t* mask;   // bitmap form
+  const int8_t* k2q;    // [B*Hk*NK, G*NQ]
+  int64_t meta_sb, meta_sh;
+  const int32_t* vbs;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float c;              // sm_scale * log2(e)
+  float sm_scale;
+  int32_t max_kv;
+  int32_t H, Hk, group, S, Sk, NQ, NK;
+  int32_t n_units;
+};
+
+// ---------------------------------------------------------------------------
+// 1. delta = rowsum(O * dO): 16 lanes per 128-element row, 16 B per lane.
+
+__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ out,
+                                                    const uint16_t* __restrict__ dout,
+                                                    float* __restrict__ delta,
+                                                    int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  float s = 0.f;
+  if (row < rows) {
+    const u32x4 a = *(const u32x4*)(out + row * HD + part * 8);
+    const u32x4 b = *(const u32x4*)(dout + row * HD + part * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s += __uint_as_float(a[i] << 16) * __uint_as_float(b[i] << 16);
+      s += __uint_as_float(a[i] & 0xFFFF0000u) * __uint_as_float(b[i] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
+  if (row < rows && part == 0) delta[row] = s;
+}
+
+// ---------------------------------------------------------------------------
+// 2. transposed selection map.
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* __restrict__ p,
+                                                        int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * 256)
+    p[i] = u32x4{0, 0, 0, 0};
+}
+
+__global__ __launch_bounds__(256) void fill_zero_bytes_kernel(int8_t* __restrict__ p,
+                                                              int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256)
+    p[i] = 0;
+}
+
+// One wave per query unit (b, h, qb): every selected key block kb with at
+// least one valid key sets byte [(b*Hk + h/G)*NK + kb][(h%G)*NQ + qb].
+template <bool BITMAP>
+__global__ __launch_bounds__(256) void k2q_kernel(BwdParams p) {
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (u >= p.n_units) return;
+  const int qb = (int)(u % p.NQ);
+  const int64_t bh = u / p.NQ;
+  const int h = (int)(bh % p.H);
+  const int b = (int)(bh / p.H);
+  const int64_t row = (int64_t)b * p.meta_sb + (int64_t)h * p.meta_sh + qb;
+  const int64_t gq = (int64_t)p.group * p.NQ;
+  int8_t* base = (int8_t*)p.k2q + ((int64_t)b * p.Hk + h / p.group) * p.NK * gq +
+                 (int64_t)(h % p.group) * p.NQ + qb;
+  if constexpr (BITMAP) {
+    const int8_t* mrow = p.mask + row * p.NK;
+    for (int kb = lane; kb < p.NK; kb += 64)
+      if (mrow[kb] != 0 && (p.vbs == nullptr || p.vbs[kb] > 0)) base[kb * gq] = 1;
+  } else {
+    const int n = clampi(p.num[row], 0, p.max_kv);
+    const int32_t* irow = p.idx + row * p.max_kv;
+    for (int j = lane; j < n; j += 64) {
+      const int kb = irow[j];
+      if (kb >= 0 && kb < p.NK && (p.vbs == nullptr || p.vbs[kb] > 0))
+        base[(int64_t)kb * gq] = 1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared pieces of the two gradient kernels.
+
+// Ascending list of the set entries of an LDS byte map of n entries, each
+// entry stored as (index << 8) | payload, payload = map byte.  One wave.
+__device__ __forceinline__ int compact_list(const uint8_t* map, int n,
+                                            uint32_t* list, int lane) {
+  int base = 0;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int i = c0 + lane;
+    const uint32_t m = i < n ? map[i] : 0u;
+    const bool f = m != 0;
+    const uint64_t bal = __ballot(f);
+    const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+    if (f) list[pos] = ((uint32_t)i << 8) | m;
+    base += __popcll(bal);
+  }
+  return base;
+}
+
+// Address of this lane's transposing read (ds_read_b64_tr_b16) of a tile
+// stored with the row swizzle c ^ (r & 15): rows lane/4 (and +16), the
+// 4-element column group (lane & 3) of 16-column group dt: base ^ (dt << 5).
+__device__ __forceinline__ uint32_t tr_base(int lane) {
+  const int row = lane >> 2;
+  const int hb = (lane & 3) >> 1;
+  return (uint32_t)(row * ROWB + ((hb ^ (row & 15)) << 4) + (lane & 1) * 8);
+}
+
+__device__ __forceinline__ bf16x8 tr_read(const char* tile, uint32_t addr) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + addr));
+  const i16x4 b =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + addr + 16 * ROWB));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
+  const u32x4 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                    pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+  return __builtin_bit_cast(bf16x8, pk);
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ: one workgroup per query unit, BLK/32 waves of 32 query rows.
+//
+// Per 32-key tile (K and V tiles in LDS, both stored with the row swizzle):
+//   S^T[key][q] = K Q^T              A = K rows,   B = Q (registers)
+//   P^T = 2^(S^T c - LSE_q)          keys past the block's count -> 0
+//   dP^T[key][q] = V dO^T            A = V rows,   B = dO (registers)
+//   dS^T = P^T (dP^T - delta_q)
+//   dQ^T[d][q] += K^T dS^T           A = K^T (transposing reads), B = dS^T
+// The accumulator layout of dS^T is the B operand layout with the key
+// permutation 8g+i <-> 4g+i / 16+4g+(i-4), matched by the transposing reads
+// of rows lane/4 and lane/4 + 16.
+
+template <int BLK, bool BITMAP>
+__global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
+  constexpr int NW = BLK / 32;
+  constexpr int NT = NW * 64;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int NK = p.NK;
+  int* s_nsel = (int*)(smem + 2 * BSTAGE);
+  uint8_t* bmp = (uint8_t*)(smem + 2 * BSTAGE + 16);
+  uint32_t* list = (uint32_t*)(bmp + ((NK + 15) & ~15));
+
+  const int u = remap_unit(blockIdx.x, p.n_units);
+  const int qb = u % p.NQ;
+  const int bh = u / p.NQ;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int64_t plane = (int64_t)bh * p.S * HD;
+  const int64_t kvh = (int64_t)b * p.Hk + h / p.group;
+  const int64_t kvplane = kvh * p.Sk * HD;
+  const int64_t row = (int64_t)b * p.meta_sb + (int64_t)h * p.meta_sh + qb;
+  const int qrow0 = qb * BLK + wave * 32;
+
+  // selected set -> bmp[kb] = valid keys of kb if selected, else 0
+  if constexpr (BITMAP) {
+    const int8_t* mrow = p.mask + row * NK;
+    for (int i = tid; i < NK; i += NT)
+      bmp[i] = mrow[i] != 0 ? (uint8_t)block_valid<BLK>(p.vbs, i) : 0;
+  } else {
+    for (int i = tid; i < NK; i += NT) bmp[i] = 0;
+    __syncthreads();
+    const int n = clampi(p.num[row], 0, p.max_kv);
+    const int32_t* irow = p.idx + row * p.max_kv;
+    for (int j = tid; j < n; j += NT) {
+      const int kb = irow[j];
+      if (kb >= 0 && kb < NK) bmp[kb] = (uint8_t)block_valid<BLK>(p.vbs, kb);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int n = compact_list(bmp, NK, list, lane);
+    if (lane == 0) *s_nsel = n;
+  }
+  __syncthreads();
+  const int nsel = *s_nsel;
+
+  if (nsel == 0) {  // no attended key: dQ = 0
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *(u32x2*)(p.dq + r * HD + dt * 16 + g * 4) = u32x2{0u, 0u};
+    }
+    return;
+  }
+
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
+  const char* kplane = (const char*)(p.k + kvplane);
+  const char* vplane = (const char*)(p.v + kvplane);
+
+  // Q and dO as B operands: row r16 (+16 qt), columns kk*32 + g*8 ..
+  bf16x8 qreg[2][4], doreg[2][4];
+  float lse[2], dlt[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      qreg[qt][kk] = *(const bf16x8*)(p.q + r * HD + kk * 32 + g * 8);
+      doreg[qt][kk] = *(const bf16x8*)(p.dout + r * HD + kk * 32 + g * 8);
+    }
+    lse[qt] = p.lse[r];
+    dlt[qt] = p.delta[r];
+  }
+
+  const int l4 = lane >> 4, pos = lane & 15;
+  uint32_t dko[8 / NW];
+#pragma unroll
+  for (int i = 0; i < 8 / NW; ++i) {
+    const int j = wave + i * NW;
+    dko[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ l4) ^ ((j & 3) << 2)) << 4));
+  }
+  const uint32_t kbase = (uint32_t)(r16 * ROWB + ((g ^ r16) << 4));
+  const uint32_t trb = tr_base(lane);
+
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    acc[dt][0] = acc[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  ListCursor cursor{list, nsel, 0, 0u};
+  cursor.reset(lane);
+  auto issue = [&](const Tile& t, int stg) {
+    const int64_t off = ((int64_t)t.kb * BLK + t.t0) * ROWB;
+    const uint32_t sl = smem_lds + stg * BSTAGE;
+    issue_rows<NW>(kplane + off, sl, dko, wave, l4, t.nv - t.t0);
+    issue_rows<NW>(vplane + off, sl + TILE_BYTES, dko, wave, l4, t.nv - t.t0);
+  };
+
+  Tile cur = cursor.at(0, lane);
+  issue(cur, 0);
+  auto step = [&](auto stg_c) -> bool {
+    constexpr int STG = decltype(stg_c)::value;
+    wait_vm_all();
+    __syncthreads();
+    const Tile nxt = cursor.next(cur, lane);
+    const bool has_next = nxt.e < nsel;
+    if (has_next) issue(nxt, STG ^ 1);
+    const int lim = cur.nv - cur.t0 - 4 * g;  // valid keys of this lane's group
+    const char* kt = smem + STG * BSTAGE;
+    const char* vt = kt + TILE_BYTES;
+
+    // S^T and dP^T, both 2 key halves x 2 query tiles
+    f32x4 s[2][2], dp[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t a = (kbase ^ (kk << 6)) + hh * 16 * ROWB;
+        const bf16x8 kop = *(const bf16x8*)(kt + a);
+        const bf16x8 vop = *(const bf16x8*)(vt + a);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          s[hh][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kop, qreg[qt][kk], kk == 0 ? z : s[hh][qt], 0, 0, 0);
+          dp[hh][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              vop, doreg[qt][kk], kk == 0 ? z : dp[hh][qt], 0, 0, 0);
+        }
+      }
+    // dS^T, packed as B operands (8 keys per lane: 4 of each half)
+    bf16x8 dsop[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int hh = e >> 2, j = e & 3;
+        const float pr = 16 * hh + j < lim
+                             ? __builtin_amdgcn_exp2f(
+                                   __builtin_fmaf(s[hh][qt][j], p.c, -lse[qt]))
+                             : 0.f;
+        x[e] = pr * (dp[hh][qt][j] - dlt[qt]);
+      }
+      dsop[qt] = pack8(x);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const bf16x8 ktop = tr_read(kt, trb ^ (uint32_t)(dt << 5));
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ktop, dsop[qt],
+                                                               acc[dt][qt], 0, 0, 0);
+    }
+    if (!has_next) return true;
+    cur = nxt;
+    return false;
+  };
+  while (true) {
+    if (step(IntC<0>{})) break;
+    if (step(IntC<1>{})) break;
+  }
+
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 o = acc[dt][qt] * p.sm_scale;
+      *(u32x2*)(p.dq + r * HD + dt * 16 + g * 4) =
+          u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. dK, dV: one workgroup per (b, K/V head, key block), BLK/16 waves of 16
+// keys each.  The keys' K and V rows are B operands in registers (rows past
+// the block's valid count zeroed).  For every attending query unit, in
+// 32-row query tiles (Q and dO tiles in LDS with the row swizzle):
+//   S[q][key] = Q K^T                A = Q rows,   B = K^T (registers)
+//   P = 2^(S c - LSE_q),  0 for keys past the count
+//   dP[q][key] = dO V^T              A = dO rows,  B = V^T (registers)
+//   dS = P (dP - delta_q)
+//   dV^T[d][key] += dO^T P           A = dO^T (transposing reads), B = P
+//   dK^T[d][key] += Q^T dS           A = Q^T (transposing reads),  B = dS
+// P and dS are B operands with the query permutation 8g+i <-> 4g+i /
+// 16+4g+(i-4) across the two 16-row query tiles.
+
+template <int BLK>
+__global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
+  constexpr int NW = BLK / 16;
+  constexpr int NT = NW * 64;
+  constexpr int QT_PER_UNIT = BLK / 32;  // 32-row query tiles per unit
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int gq = p.group * p.NQ;  // map entries per key block
+  int* s_n = (int*)(smem + 2 * BSTAGE);
+  uint8_t* map = (uint8_t*)(smem + 2 * BSTAGE + 16);
+  uint32_t* list = (uint32_t*)(map + ((gq + 15) & ~15));
+
+  const int u = remap_unit(blockIdx.x, p.n_units);  // units = B*Hk*NK here
+  const int kb = u % p.NK;
+  const int bkv = u / p.NK;                         // b*Hk + kvh
+  const int kvh = bkv % p.Hk;
+  const int b = bkv / p.Hk;
+  const int64_t kvplane = (int64_t)bkv * p.Sk * HD;
+  const int nv = block_valid<BLK>(p.vbs, kb);
+  const int key = wave * 16 + r16;  // this lane's key within the block
+
+  const int8_t* mrow = p.k2q + (int64_t)u * gq;
+  for (int i = tid; i < gq; i += NT) map[i] = (uint8_t)mrow[i];
+  __syncthreads();
+  if (wave == 0) {
+    const int n = compact_list(map, gq, list, lane);
+    if (lane == 0) *s_n = n;
+  }
+  __syncthreads();
+  const int nunits = nv > 0 ? *s_n : 0;
+  const int ntiles = nunits * QT_PER_UNIT;
+
+  f32x4 dka[8], dva[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) dka[dt] = dva[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (ntiles > 0) {
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
+    // K^T / V^T B operands: column key, rows d = kk*32 + g*8 ..
+    bf16x8 kreg[4], vreg[4];
+    {
+      const int64_t r = kvplane + ((int64_t)kb * BLK + key) * HD;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (key < nv) {
+          kreg[kk] = *(const bf16x8*)(p.k + r + kk * 32 + g * 8);
+          vreg[kk] = *(const bf16x8*)(p.v + r + kk * 32 + g * 8);
+        } else {
+          kreg[kk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+          vreg[kk] = kreg[kk];
+        }
+      }
+    }
+    const int l4 = lane >> 4, pos = lane & 15;
+    uint32_t dko[8 / NW];
+#pragma unroll
+    for (int i = 0; i < 8 / NW; ++i) {
+      const int j = wave + i * NW;
+      dko[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ l4) ^ ((j & 3) << 2)) << 4));
+    }
+    const uint32_t abase = (uint32_t)(r16 * ROWB + ((g ^ r16) << 4));
+    const uint32_t trb = tr_base(lane);
+
+    // query tile t: unit list[t / QT_PER_UNIT], rows (t % QT_PER_UNIT)*32 ..
+    auto tile_rows = [&](int t) -> int64_t {  // first row in [B*H*S]
+      const int e = __builtin_amdgcn_readfirstlane((int)(list[t / QT_PER_UNIT] >> 8));
+      const int hl = e / p.NQ, qb = e % p.NQ;
+      const int64_t bh = (int64_t)b * p.H + (int64_t)kvh * p.group + hl;
+      return bh * p.S + (int64_t)qb * BLK + (t % QT_PER_UNIT) * 32;
+    };
+    auto issue = [&](int64_t r0, int stg) {
+      const uint32_t sl = smem_lds + stg * BSTAGE;
+      issue_rows<NW>((const char*)(p.q + r0 * HD), sl, dko, wave, l4, KT);
+      issue_rows<NW>((const char*)(p.dout + r0 * HD), sl + TILE_BYTES, dko, wave, l4, KT);
+    };
+
+    int64_t r_cur = tile_rows(0);
+    issue(r_cur, 0);
+    int t = 0;
+    auto step = [&](auto stg_c) -> bool {
+      constexpr int STG = decltype(stg_c)::value;
+      // this lane's LSE / delta: query rows g*4 + j and 16 + g*4 + j
+      const f32x4 ls0 = *(const f32x4*)(p.lse + r_cur + g * 4);
+      const f32x4 ls1 = *(const f32x4*)(p.lse + r_cur + 16 + g * 4);
+      const f32x4 de0 = *(const f32x4*)(p.delta + r_cur + g * 4);
+      const f32x4 de1 = *(const f32x4*)(p.delta + r_cur + 16 + g * 4);
+      wait_vm_all();
+      __syncthreads();
+      const bool has_next = t + 1 < ntiles;
+      int64_t r_nxt = 0;
+      if (has_next) {
+        r_nxt = tile_rows(t + 1);
+        issue(r_nxt, STG ^ 1);
+      }
+      const char* qt_ = smem + STG * BSTAGE;
+      const char* dot = qt_ + TILE_BYTES;
+      f32x4 s[2], dp[2];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          const uint32_t a = (abase ^ (kk << 6)) + qh * 16 * ROWB;
+          const bf16x8 qop = *(const bf16x8*)(qt_ + a);
+          const bf16x8 dop = *(const bf16x8*)(dot + a);
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          s[qh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop, kreg[kk],
+                                                          kk == 0 ? z : s[qh], 0, 0, 0);
+          dp[qh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dop, vreg[kk],
+                                                           kk == 0 ? z : dp[qh], 0, 0, 0);
+        }
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int qh = e >> 2, j = e & 3;
+        const float l = qh ? ls1[j] : ls0[j];
+        const float d = qh ? de1[j] : de0[j];
+        const float pr = key < nv ? __builtin_amdgcn_exp2f(
+                                        __builtin_fmaf(s[qh][j], p.c, -l))
+                                  : 0.f;
+        pv[e] = pr;
+        dsv[e] = pr * (dp[qh][j] - d);
+      }
+      const bf16x8 pop = pack8(pv);
+      const bf16x8 dsop = pack8(dsv);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint32_t a = trb ^ (uint32_t)(dt << 5);
+        dva[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_read(dot, a), pop, dva[dt],
+                                                          0, 0, 0);
+        dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_read(qt_, a), dsop, dka[dt],
+                                                          0, 0, 0);
+      }
+      if (!has_next) return true;
+      r_cur = r_nxt;
+      ++t;
+      return false;
+    };
+    while (true) {
+      if (step(IntC<0>{})) break;
+      if (step(IntC<1>{})) break;
+    }
+  }
+
+  // dK^T / dV^T: lane holds d = dt*16 + g*4 + j of its key
+  const int64_t r = kvplane + ((int64_t)kb * BLK + key) * HD;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const f32x4 kd = dka[dt] * p.sm_scale;
+    *(u32x2*)(p.dk + r + dt * 16 + g * 4) =
+        u32x2{pack_bf16x2(kd[0], kd[1]), pack_bf16x2(kd[2], kd[3])};
+    *(u32x2*)(p.dv + r + dt * 16 + g * 4) =
+        u32x2{pack_bf16x2(dva[dt][0], dva[dt][1]), pack_bf16x2(dva[dt][2], dva[dt][3])};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+bool aligned16(const void* x) { return ((uintptr_t)x & 15u) == 0; }
+
+size_t map_bytes(int64_t B, int64_t H, int64_t S, int64_t Sk, int64_t block) {
+  return (size_t)(B * H * (S / block) * (Sk / block));
+}
+
+size_t delta_bytes(int64_t B, int64_t H, int64_t S) {
+  return (size_t)(B * H * S) * sizeof(float);
+}
+
+size_t workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t Sk, int64_t block) {
+  // delta, then the byte map, 256-byte aligned
+  return ((delta_bytes(B, H, S) + 255) & ~(size_t)255) + map_bytes(B, H, S, Sk, block);
+}
+
+bsa_status check_bwd(const void* q, const void* k, const void* v, const void* out,
+                     const void* dout, const float* lse, const void* dq,
+                     const void* dk, const void* dv, const void* ws,
+                     int32_t B, int32_t H, int32_t Hk, int32_t S, int32_t Sk,
+                     int32_t D, int32_t block) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !ws)
+    return BSA_ERR_NULL;
+  if (B <= 0 || H <= 0 || Hk <= 0 || S <= 0 || Sk <= 0 || D <= 0 || block <= 0)
+    return BSA_ERR_SHAPE;
+  if (S % block != 0 || Sk % block != 0 || H % Hk != 0) return BSA_ERR_SHAPE;
+  if (D != HD || (block != 64 && block != 128)) return BSA_ERR_UNSUPPORTED;
+  if (Sk / block > BSA_MAX_KEY_BLOCKS) return BSA_ERR_UNSUPPORTED;
+  if ((int64_t)(H / Hk) * (S / block) > BSA_MAX_KEY_BLOCKS) return BSA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * S > INT32_MAX || (int64_t)B * Hk * Sk > INT32_MAX)
+    return BSA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || ((uintptr_t)ws & 255u) != 0)
+    return BSA_ERR_ALIGN;
+  return BSA_OK;
+}
+
+template <int BLK, bool BITMAP>
+bsa_status run_bwd(BwdParams p, const void* out, float* delta, int8_t* map,
+                   size_t nmap, hipStream_t st) {
+  const int64_t rows = (int64_t)p.n_units * BLK;  // B*H*S
+  hipLaunchKernelGGL(delta_kernel, dim3((uint32_t)((rows + 15) / 16)), dim3(256), 0, st,
+                     (const uint16_t*)out, p.dout, delta, rows);
+  if ((nmap & 15) == 0 && ((uintptr_t)map & 15) == 0)
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, st, (u32x4*)map,
+                       (int64_t)(nmap / 16));
+  else
+    hipLaunchKernelGGL(fill_zero_bytes_kernel, dim3(1024), dim3(256), 0, st, map,
+                       (int64_t)nmap);
+  p.delta = delta;
+  p.k2q = map;
+  hipLaunchKernelGGL(k2q_kernel<BITMAP>, dim3((uint32_t)((p.n_units + 3) / 4)), dim3(256),
+                     0, st, p);
+  {
+    auto kern = dq_kernel<BLK, BITMAP>;
+    const size_t lds = 2 * BSTAGE + 16 + (size_t)((p.NK + 15) & ~15) + (size_t)p.NK * 4;
+    if (lds > 65536 && hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)lds) != hipSuccess)
+      return BSA_ERR_HIP;
+    hipLaunchKernelGGL(kern, dim3(p.n_units), dim3(BLK * 2), lds, st, p);
+  }
+  {
+    auto kern = dkdv_kernel<BLK>;
+    const int gq = p.group * p.NQ;
+    const size_t lds = 2 * BSTAGE + 16 + (size_t)((gq + 15) & ~15) + (size_t)gq * 4;
+    if (lds > 65536 && hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)lds) != hipSuccess)
+      return BSA_ERR_HIP;
+    BwdParams pk = p;
+    pk.n_units = (int32_t)((int64_t)p.n_units / p.H * p.Hk / p.NQ * p.NK);
+    hipLaunchKernelGGL(kern, dim3(pk.n_units), dim3(BLK * 4), lds, st, pk);
+  }
+  return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+BwdParams make_bwd_params(const void* q, const void* k, const void* v,
+                          const void* dout, const float* lse,
+                          const int32_t* vbs, float sm_scale, void* dq, void* dk,
+                          void* dv, int32_t B, int32_t H, int32_t Hk, int32_t S,
+                          int32_t Sk, int32_t block) {
+  BwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.vbs = vbs;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.sm_scale = sm_scale;
+  p.c = sm_scale * LOG2E;
+  p.H = H;
+  p.Hk = Hk;
+  p.group = H / Hk;
+  p.S = S;
+  p.Sk = Sk;
+  p.NQ = S / block;
+  p.NK = Sk / block;
+  p.n_units = B * H * (S / block);
+  return p;
+}
+
+template <bool BITMAP>
+bsa_status dispatch_bwd(const BwdParams& p, int block, const void* out, void* ws,
+                        size_t ws_bytes, int32_t B, int32_t H, int32_t S, int32_t Sk,
+                        hipStream_t st) {
+  const size_t need = workspace_bytes(B, H, S, Sk, block);
+  if (ws_bytes < need) return BSA_ERR_SHAPE;
+  float* delta = (float*)ws;
+  int8_t* map = (int8_t*)ws + ((delta_bytes(B, H, S) + 255) & ~(size_t)255);
+  const size_t nmap = map_bytes(B, H, S, Sk, block);
+  if (block == 64) return run_bwd<64, BITMAP>(p, out, delta, map, nmap, st);
+  return run_bwd<128, BITMAP>(p, out, delta, map, nmap, st);
+}
+
+}  // namespace
+
+extern "C" size_t bsa_bwd_workspace_size(int32_t B, int32_t H, int32_t S, int32_t Sk,
+                                         int32_t block) {
+  if (B <= 0 || H <= 0 || S <= 0 || Sk <= 0 || block <= 0) return 0;
+  return workspace_bytes(B, H, S, Sk, block);
+}
+
+extern "C" bsa_status bsa_bwd_lut(const void* q, const void* k, const void* v,
+                                  const void* out, const void* dout, const float* lse,
+                                  const int32_t* q2k_idx, const int32_t* q2k_num,
+                                  int32_t max_kv, int64_t meta_stride_b,
+                                  int64_t meta_stride_h,
+                                  const int32_t* variable_block_sizes, float sm_scale,
+                                  void* dq, void* dk, void* dv, void* workspace,
+                                  size_t workspace_bytes_, int32_t B, int32_t H,
+                                  int32_t Hk, int32_t S, int32_t Sk, int32_t D,
+                                  int32_t block, void* stream) {
+  bsa_status st = check_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Hk, S,
+                            Sk, D, block);
+  if (st != BSA_OK) return st;
+  if (!q2k_idx || !q2k_num) return BSA_ERR_NULL;
+  if (max_kv < 1 || meta_stride_b < 0 || meta_stride_h < 0) return BSA_ERR_SHAPE;
+  BwdParams p = make_bwd_params(q, k, v, dout, lse, variable_block_sizes, sm_scale, dq,
+                                dk, dv, B, H, Hk, S, Sk, block);
+  p.idx = q2k_idx;
+  p.num = q2k_num;
+  p.max_kv = max_kv;
+  p.meta_sb = meta_stride_b;
+  p.meta_sh = meta_stride_h;
+  return dispatch_bwd<false>(p, block, out, workspace, workspace_bytes_, B, H, S, Sk,
+                             (hipStream_t)stream);
+}
+
+extern "C" bsa_status bsa_bwd_bitmap(const void* q, const void* k, const void* v,
+                                     const void* out, const void* dout,
+                                     const float* lse, const int8_t* mask,
+                                     int64_t mask_stride_b, int64_t mask_stride_h,
+                                     const int32_t* variable_block_sizes, float sm_scale,
+                                     void* dq, void* dk, void* dv, void* workspace,
+                                     size_t workspace_bytes_, int32_t B, int32_t H,
+                                     int32_t Hk, int32_t S, int32_t Sk, int32_t D,
+                                     int32_t block, void* stream) {
+  bsa_status st = check_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Hk, S,
+                            Sk, D, block);
+  if (st != BSA_OK) return st;
+  if (!mask) return BSA_ERR_NULL;
+  if (mask_stride_b < 0 || mask_stride_h < 0) return BSA_ERR_SHAPE;
+  BwdParams p = make_bwd_params(q, k, v, dout, lse, variable_block_sizes, sm_scale, dq,
+                                dk, dv, B, H, Hk, S, Sk, block);
+  p.mask = mask;
+  p.meta_sb = mask_stride_b;
+  p.meta_sh = mask_stride_h;
+  return dispatch_bwd<true>(p, block, out, workspace, workspace_bytes_, B, H, S, Sk,
+                            (hipStream_t)stream);
+}

@@ -23,17 +23,20 @@
 //  A3  Q: each wave keeps its 32 query rows in VGPRs as MFMA operands for
 //      the whole K loop (loaded once with 128-bit loads).
 //  A4  K/V gather: 32-key tiles of the selected blocks, only rows below the
-//      block's valid count are read (coalesced 128-bit loads); rows past it
-//      are written as zeros.  Tiles are double-buffered in LDS: the loads of
-//      tile i+1 are in flight while tile i is computed.  fp8 e4m3 K/V are
-//      widened to bf16 exactly on the way into LDS.
+//      block's valid count are read (direct global->LDS 128-bit loads; the
+//      lanes of rows past the count re-read row 0, fp8 writes zeros there).
+//      Tiles are double-buffered in LDS: the loads of tile i+1 are in flight
+//      while tile i is computed.  fp8 e4m3 K/V are widened to bf16 exactly
+//      on the way into LDS.
 //  A5  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (fp32 accumulate), scaled by
 //      sm_scale*log2(e) (times the block's K scale for fp8); keys at or past
 //      the block's valid count are set to -inf.
-//  A6  online softmax in exp2 form (vLLM "tq_decode" step F shows the same
-//      running-max / rescale scheme): per-row running max m and partial sums
-//      l kept per lane, the max reduced across the four lane groups that
-//      share a query.
+//  A6  softmax in exp2 form.  The reference m of each row is the row
+//      maximum of the unit's first tile and stays fixed (no per-tile max or
+//      rescale); if a weight or sum overflowed, the unit is recomputed with
+//      the running-max / rescale scheme (vLLM "tq_decode" step F shows it).
+//      Partial sums l are kept per lane and reduced across the four lane
+//      groups that share a query once, at the end.
 //  A7  O^T += V^T P^T on the same MFMA; P is the softmax tile rounded to
 //      bf16 (times the block's V scale for fp8), already in the operand
 //      layout; V^T comes from the hardware transposing LDS read
@@ -46,27 +49,12 @@
 #include <stdint.h>
 
 #include "bsa.h"
+#include "bsa_device.h"
 
 namespace {
 
-constexpr int HD = 128;                 // head dimension
-constexpr int KT = 32;                  // keys per pipeline tile
-constexpr int ROWB = HD * 2;            // bytes of one bf16 row in LDS
-constexpr int TILE_BYTES = KT * ROWB;   // one K or V tile (8 KB)
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // one K tile + one V tile
 constexpr int NSTAGE = 2;
-constexpr float LOG2E = 1.4426950408889634f;
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 struct FwdParams {
   const uint16_t* q;
@@ -92,25 +80,6 @@ struct FwdParams {
   int32_t n_units;
 };
 
-__device__ __forceinline__ int clampi(int x, int lo, int hi) {
-  return x < lo ? lo : (x > hi ? hi : x);
-}
-
-// Valid keys of key block kb.
-template <int BLK>
-__device__ __forceinline__ int block_valid(const int32_t* vbs, int kb) {
-  return vbs ? clampi(vbs[kb], 0, BLK) : BLK;
-}
-
-// Workgroups are handed to the 8 XCDs round-robin (id % 8).  Give XCD x the
-// contiguous unit range [x*n/8, (x+1)*n/8) so the units of one head (and of
-// the query heads that share its K/V head), which read the same K/V blocks,
-// meet in the same L2.
-__device__ __forceinline__ int remap_unit(int bid, int n) {
-  if (n % 8 != 0) return bid;
-  return (bid % 8) * (n / 8) + bid / 8;
-}
-
 // LDS tile layout: 32 rows of 256 B, 16-byte chunks XOR-swizzled per row so
 // that the MFMA operand reads are free of bank conflicts without padding.
 // K tiles are read row-wise (16 rows x one chunk per 16 lanes): chunk c of
@@ -124,12 +93,6 @@ __device__ __forceinline__ int v_off(int r, int c) {
   return r * ROWB + ((c ^ ((r & 7) << 1)) << 4);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  f32x2 f = {a, b};
-  bf16x2 r = __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, RNE
-  return __builtin_bit_cast(uint32_t, r);
-}
-
 // 4 fp8 e4m3 codes -> 4 bf16 (exact widening; scale 1).
 __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
   u32x2 r;
@@ -138,99 +101,6 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
   r.y = __builtin_bit_cast(uint32_t,
                            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
   return r;
-}
-
-// Reductions over the four lanes l, l^16, l^32, l^48 (the lanes that hold
-// one query row), with the gfx950 cross-row lane swaps (no LDS traffic).
-__device__ __forceinline__ float group_max(float x) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                            false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                            false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float group_min(float x) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                            false, false);
-  x = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                            false, false);
-  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float group_sum(float x) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                            false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                            false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// Position of one pipeline tile: entry e of the selected-block list, first
-// key t0 within the block, valid keys nv of the block.
-struct Tile {
-  int e, kb, t0, nv;
-};
-
-// Reader of the selected-block list ((kb << 8) | nv per entry, nv = valid
-// keys).  Entries are fetched from LDS 64 at a time into one VGPR (lane i
-// holds entry base + i) and picked out with v_readlane, so moving to the
-// next block costs no LDS round trip on the critical path.
-struct ListCursor {
-  const uint32_t* list;
-  int nsel;
-  int base;
-  uint32_t chunk;
-
-  __device__ __forceinline__ void reset(int lane) {
-    base = 0;
-    chunk = lane < nsel ? list[lane] : 0u;
-  }
-
-  // Entries are visited in increasing order, one at a time.
-  __device__ __forceinline__ Tile at(int e, int lane) {
-    Tile t;
-    t.e = e;
-    t.t0 = 0;
-    t.kb = 0;
-    t.nv = 0;
-    if (e < nsel) {
-      if (e >= base + 64) {
-        base += 64;
-        chunk = base + lane < nsel ? list[base + lane] : 0u;
-      }
-      const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)chunk, e - base);
-      t.kb = (int)(x >> 8);
-      t.nv = (int)(x & 255u);
-    }
-    return t;
-  }
-
-  __device__ __forceinline__ Tile next(const Tile& cur, int lane) {
-    if (cur.t0 + KT < cur.nv) {
-      Tile t = cur;
-      t.t0 += KT;
-      return t;
-    }
-    return at(cur.e + 1, lane);
-  }
-};
-
-// One direct global->LDS load of 16 B per lane (global_load_lds_dwordx4,
-// SGPR base + 32-bit VGPR offset): lane l's 16 bytes land at LDS address
-// lds_base + 16*l.  Issued as inline assembly so that the compiler does not
-// track it; the loop waits for these loads explicitly (vmcnt) before the
-// barrier that publishes a tile, and the reads of the other stage proceed
-// while they are in flight.
-__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff,
-                                      uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds_base), "v"(voff), "s"(gbase)
-      : "memory", "m0");
 }
 
 // fp8 K/V: 16 codes per 16-byte load, widened to bf16 in registers and
@@ -283,25 +153,10 @@ __device__ __forceinline__ void store_tile_fp8(const Fp8Staging<NT>& st,
   }
 }
 
-// Waits until this wave's outstanding global loads (including the ones
-// writing LDS directly) have completed.
-__device__ __forceinline__ void wait_vm_all() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
-}
-
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  return fmaxf(fmaxf(a, b), c);
-}
-
 // Tile shapes of the K loop: FULL = 32 valid keys; PART = 1..31 valid keys
 // (keys past the count masked; the second 16-key half's QK^T is skipped
 // when it holds no valid key).
 enum TileKind { FULL = 0, PART = 1 };
-
-template <int V>
-struct IntC {
-  static constexpr int value = V;
-};
 
 // Accumulator state of one wave: O^T tiles, per-row reference m (log2
 // units, identical in the four lanes of a row) and per-lane partial sums l.

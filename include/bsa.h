@@ -37,6 +37,7 @@
 #define BSA_H
 
 #include <float.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -161,6 +162,64 @@ bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v,
  */
 bsa_status bsa_mask_to_lut(const int8_t* mask, int64_t rows, int32_t nk,
                            int32_t* q2k_idx, int32_t* q2k_num, void* stream);
+
+/*
+ * Backward pass: gradients of sum(O * dout) with respect to q, k, v for the
+ * forward pass with bf16 K/V (the LSE output exists for this pairing:
+ * FastVideo "block_sparse_attn_sm100a.py" keeps the LSE-producing path for
+ * forward/backward pairing).  With t = (q . k) * sm_scale * log2(e) over a
+ * unit's attended keys:
+ *
+ *   P = 2^(t - LSE),  dP = dout V^T,  delta = rowsum(dout * out),
+ *   dS = P * (dP - delta),
+ *   dq = sm_scale * dS K,  dk = sm_scale * dS^T Q,  dv = P^T dout
+ *
+ * (the chain rule of softmax attention; K/V head h/(H/Hk) receives the
+ * gradients of all its query heads).  Rows with no attended key give dq = 0;
+ * keys past a block's valid count and blocks nobody selects give dk = dv = 0.
+ *
+ *  q, k, v, sizes, metadata, variable_block_sizes, sm_scale
+ *               exactly as passed to the forward call (bf16 K/V only).
+ *  out, lse     the forward call's outputs for these inputs (lse must not
+ *               be NULL); 16-byte aligned.
+ *  dout         bf16 [B, H, S, D], 16-byte aligned.
+ *  dq           bf16 [B, H, S, D]; dk, dv bf16 [B, Hk, Sk, D]; 16-byte
+ *               aligned; every element is written.
+ *  workspace    device memory of at least bsa_bwd_workspace_size(...) bytes,
+ *               256-byte aligned, owned by the caller, free for the library
+ *               to overwrite during the call (it holds delta and the
+ *               key-block -> query-block selection map).  Calls that overlap
+ *               on the same workspace race.
+ *  workspace_bytes  its size; a smaller value is BSA_ERR_SHAPE.
+ *
+ * Errors as the forward calls (plus BSA_ERR_UNSUPPORTED when (H/Hk)*S/block
+ * exceeds BSA_MAX_KEY_BLOCKS); on error nothing is launched.  The result is
+ * deterministic: every gradient element is accumulated by one workgroup in a
+ * fixed order (no atomics).
+ */
+size_t bsa_bwd_workspace_size(int32_t B, int32_t H, int32_t S, int32_t Sk,
+                              int32_t block);
+
+bsa_status bsa_bwd_lut(const void* q, const void* k, const void* v,
+                       const void* out, const void* dout, const float* lse,
+                       const int32_t* q2k_idx, const int32_t* q2k_num,
+                       int32_t max_kv, int64_t meta_stride_b,
+                       int64_t meta_stride_h,
+                       const int32_t* variable_block_sizes, float sm_scale,
+                       void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, int32_t B, int32_t H, int32_t Hk,
+                       int32_t S, int32_t Sk, int32_t D, int32_t block,
+                       void* stream);
+
+bsa_status bsa_bwd_bitmap(const void* q, const void* k, const void* v,
+                          const void* out, const void* dout, const float* lse,
+                          const int8_t* mask, int64_t mask_stride_b,
+                          int64_t mask_stride_h,
+                          const int32_t* variable_block_sizes, float sm_scale,
+                          void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, int32_t B, int32_t H,
+                          int32_t Hk, int32_t S, int32_t Sk, int32_t D,
+                          int32_t block, void* stream);
 
 /* Static text of a status code (never NULL). */
 const char* bsa_status_str(int32_t status);

@@ -132,3 +132,42 @@ def mask_lut(**over):
 ])
 def test_mask_to_lut_rejects_invalid_static_arguments(over, status):
     assert mask_lut(**over) == status
+
+
+def bwd_lut(**over):
+    args = dict(q=A, k=A, v=A, out=A, dout=A, lse=A, idx=A, num=A, max_kv=4,
+                sb=8, sh=8, vbs=None, scale=0.1, dq=A, dk=A, dv=A, ws=A,
+                ws_bytes=1 << 30, B=1, H=1, Hk=1, S=512, Sk=512, D=128,
+                block=64, stream=None)
+    args.update(over)
+    return _lib.load().bsa_bwd_lut(*args.values())
+
+
+def test_bwd_workspace_size_covers_delta_and_map():
+    lib = _lib.load()
+    # delta: B*H*S floats (256-aligned), map: B*H*NQ*NK bytes
+    assert lib.bsa_bwd_workspace_size(2, 3, 512, 1024, 64) == \
+        ((2 * 3 * 512 * 4 + 255) // 256) * 256 + 2 * 3 * 8 * 16
+    assert lib.bsa_bwd_workspace_size(0, 3, 512, 512, 64) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), api.BSA_ERR_NULL),
+    (dict(lse=None), api.BSA_ERR_NULL),
+    (dict(dout=None), api.BSA_ERR_NULL),
+    (dict(ws=None), api.BSA_ERR_NULL),
+    (dict(dk=None), api.BSA_ERR_NULL),
+    (dict(idx=None), api.BSA_ERR_NULL),
+    (dict(S=500), api.BSA_ERR_SHAPE),
+    (dict(H=3, Hk=2), api.BSA_ERR_SHAPE),
+    (dict(max_kv=0), api.BSA_ERR_SHAPE),
+    (dict(ws_bytes=100), api.BSA_ERR_SHAPE),       # workspace too small
+    (dict(D=64), api.BSA_ERR_UNSUPPORTED),
+    (dict(block=32), api.BSA_ERR_UNSUPPORTED),
+    (dict(H=64, Hk=1, S=64 * 512), api.BSA_ERR_UNSUPPORTED),  # G*NQ too big
+    (dict(ws=A + 16), api.BSA_ERR_ALIGN),         # workspace needs 256 B
+    (dict(lse=A + 4), api.BSA_ERR_ALIGN),
+    (dict(dq=A + 8), api.BSA_ERR_ALIGN),
+])
+def test_bwd_rejects_invalid_static_arguments(over, status):
+    assert bwd_lut(**over) == status

@@ -1,0 +1,127 @@
+"""GPU parity of the backward pass (bsa_bwd_lut / bsa_bwd_bitmap through the
+C ABI) against the oracle's fp64 gradients on the same seeded inputs.
+
+The GPU path takes the forward pass's own O and LSE (as a training step
+would), so its error is the forward's bf16 rounding of O (through delta)
+plus the bf16 rounding of P and dS as MFMA operands and of the outputs.
+Each of these is a relative 2^-9 per term; the bound checked per gradient
+tensor is max|gpu - ref| <= 2^-6 * max|ref| (four roundings of 2^-9 with a
+factor 2 for cancellation in dS), and the relative L2 error <= 2^-7."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_tile_amd as bsa
+import oracle
+import workloads
+from tests.gpu_helpers import log, run_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 2.0 ** -6
+L2_REL = 2.0 ** -7
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def dout_of(w, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(w.q.shape, generator=g).to(torch.bfloat16)
+
+
+def gpu_bwd(w, dout):
+    d = to_dev(w)
+    out, lse = run_gpu(w, dev_inputs=d)
+    kw = dict(block=w.block, variable_block_sizes=d["vbs"], sm_scale=w.sm_scale)
+    if w.form == "lut":
+        g = bsa.bsa_bwd(d["q"], d["k"], d["v"], out, dout.cuda(), lse,
+                        q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"],
+                        meta_strides=w.meta_strides, **kw)
+    else:
+        g = bsa.bsa_bwd(d["q"], d["k"], d["v"], out, dout.cuda(), lse,
+                        mask=d["mask"], meta_strides=w.mask_strides, **kw)
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy() for t in g]
+
+
+def oracle_bwd(w, dout):
+    kw = dict(block=w.block, vbs=w.vbs, sm_scale=w.sm_scale)
+    if w.form == "lut":
+        return oracle.bwd(w.q, w.k, w.v, dout, q2k_idx=w.q2k_idx,
+                          q2k_num=w.q2k_num, meta_strides=w.meta_strides, **kw)
+    return oracle.bwd(w.q, w.k, w.v, dout, mask=w.mask,
+                      meta_strides=w.mask_strides, **kw)
+
+
+def check_grads(got, ref, label):
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        assert not np.isnan(a).any(), f"{label} {name}: NaN"
+        scale = float(np.abs(r).max())
+        err = float(np.abs(a - r).max())
+        l2 = float(np.linalg.norm(a - r) / max(np.linalg.norm(r), 1e-30))
+        log(f"  {label} {name}: max|ref|={scale:.3e} max|err|={err:.3e} "
+            f"rel_l2={l2:.3e}")
+        if scale == 0.0:
+            assert err == 0.0, f"{label} {name}: must be exactly 0"
+            continue
+        assert err <= MAX_REL * scale, f"{label} {name}: max err {err:.3e}"
+        assert l2 <= L2_REL, f"{label} {name}: rel L2 {l2:.3e}"
+
+
+CASES = [
+    ("lut64_half", dict(seed=201, B=1, H=2, S=512, block=64, density=0.5)),
+    ("lut64_vbs_zero_some", dict(seed=202, B=2, H=2, S=512, block=64,
+                                 count_mode="uniform", vbs_mode="zero_some")),
+    ("lut128_uniform", dict(seed=203, B=1, H=2, S=1024, block=128,
+                            count_mode="uniform", vbs_mode="partial")),
+    ("bitmap64", dict(seed=204, B=1, H=2, S=512, block=64, form="bitmap",
+                      density=0.5, vbs_mode="random")),
+    ("bitmap128_shared", dict(seed=205, B=2, H=2, S=1024, block=128,
+                              form="bitmap", shared_meta=True, density=0.3)),
+    ("gqa_rect_lut64", dict(seed=206, B=2, H=4, Hk=2, S=512, Sk=768, block=64,
+                            count_mode="uniform", vbs_mode="random")),
+    ("gqa_rect_bitmap128", dict(seed=207, B=1, H=6, Hk=1, S=512, Sk=1024,
+                                block=128, form="bitmap", density=0.4,
+                                vbs_mode="partial")),
+    ("lut64_count_zero_some", dict(seed=208, B=1, H=3, S=256, block=64,
+                                   count_mode="uniform", max_kv=2)),
+    ("lut64_one_block", dict(seed=209, B=1, H=2, S=64, block=64, density=1.0,
+                             vbs_mode="partial")),
+    ("lut64_dense", dict(seed=210, B=1, H=2, S=512, block=64, density=1.0)),
+]
+
+
+@pytest.mark.parametrize("label,kw", CASES, ids=[c[0] for c in CASES])
+def test_backward_parity(label, kw):
+    kw = dict(kw)
+    w = workloads.make_random(kw.pop("seed"), **kw)
+    log(f"[bwd] {label} B{w.B} H{w.H} Hk{w.Hk} S{w.S} Sk{w.Sk} blk{w.block} "
+        f"form={w.form}")
+    dout = dout_of(w, 7)
+    got = gpu_bwd(w, dout)
+    ref = oracle_bwd(w, dout)
+    check_grads(got, ref, label)
+
+
+def test_backward_all_rows_empty_gives_zero_gradients():
+    w = workloads.make_random(211, B=1, H=2, S=256, block=64, count_mode="zero")
+    log("[bwd] all rows empty")
+    got = gpu_bwd(w, dout_of(w, 8))
+    for t in got:
+        assert (t == 0).all()
+
+
+def test_backward_is_deterministic():
+    w = workloads.make_random(212, B=1, H=2, S=512, block=64,
+                              count_mode="uniform", vbs_mode="random")
+    dout = dout_of(w, 9)
+    log("[bwd] determinism")
+    a = gpu_bwd(w, dout)
+    b = gpu_bwd(w, dout)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
