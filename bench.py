@@ -247,6 +247,74 @@ def bench_mask_to_lut(args) -> int:
     return 0
 
 
+def bench_bwd(args) -> int:
+    """Times the backward pass (delta pass, selection map, dq, dk/dv kernels)
+    on a named bf16 workload, after one forward pass that supplies O and
+    the LSE.  Algorithmic work: 5 products of 2*D flop per attended pair
+    (S recompute, dP, dV, dK, dQ) = 10*D*P."""
+    progress(f"generating workload {args.workload}")
+    w = workloads.make_config(args.workload)
+    if w.kv_fp8:
+        print("the backward pass takes bf16 K/V", file=sys.stderr)
+        return 2
+    pairs = attended_pairs(w)
+    flop = 10.0 * w.D * pairs
+    dev = torch.device("cuda:0")
+    d = {n: (None if getattr(w, n) is None else getattr(w, n).to(dev))
+         for n in ("q", "k", "v", "q2k_idx", "q2k_num", "mask", "vbs")}
+    d["k_scale"] = d["v_scale"] = None
+    out = torch.empty(tuple(w.q.shape), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    launch(w, d, out, lse)
+    g = torch.Generator().manual_seed(1)
+    dout = torch.randn(tuple(w.q.shape), generator=g).to(torch.bfloat16).to(dev)
+    kw = dict(block=w.block, variable_block_sizes=d["vbs"], sm_scale=w.sm_scale)
+    if w.form == "lut":
+        kw.update(q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"],
+                  meta_strides=w.meta_strides)
+    else:
+        kw.update(mask=d["mask"], meta_strides=w.mask_strides)
+    need = int(bsa._lib.load().bsa_bwd_workspace_size(w.B, w.H, w.S, w.Sk,
+                                                       w.block))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def step():
+        return bsa.bsa_bwd(d["q"], d["k"], d["v"], out, dout, lse,
+                           workspace=ws, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = flop / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "effective TFLOP/s (10*D*attended pairs) + % bf16 MFMA peak, "
+                  "VSA backward",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S,
+                   "D": w.D, "block": w.block, "form": w.form,
+                   "attended_pairs": pairs, "effective_flop_per_step": flop,
+                   "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,9 +330,11 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the "
                          "reference kernel for scaling HBM byte counters)")
-    ap.add_argument("--op", default="fwd", choices=("fwd", "mask_to_lut"),
-                    help="fwd (default): the forward pass; mask_to_lut: the "
-                         "block-map compaction on the workload's selection")
+    ap.add_argument("--op", default="fwd",
+                    choices=("fwd", "bwd", "mask_to_lut"),
+                    help="fwd (default): the forward pass; bwd: the backward "
+                         "pass; mask_to_lut: the block-map compaction on the "
+                         "workload's selection")
     ap.add_argument("--record-traffic", metavar="PMC_DIR",
                     help="no GPU work: read rocprofv3 FETCH_SIZE/WRITE_SIZE "
                          "runs from PMC_DIR and store the workload's HBM "
@@ -285,6 +355,8 @@ def main() -> int:
 
     if args.op == "mask_to_lut":
         return bench_mask_to_lut(args)
+    if args.op == "bwd":
+        return bench_bwd(args)
     if args.copy_calibration:
         n = 1 << 29  # 2**29 bf16 = 1 GiB read + 1 GiB written per copy
         src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
