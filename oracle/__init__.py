@@ -10,10 +10,13 @@ code.  See ``bsa_oracle.h`` for the definition it computes and its citations.
 from .oracle import (  # noqa: F401
     KV_BF16,
     KV_FP8E4M3,
+    KV_I4_CODEBOOK,
+    KV_I8_CODEBOOK,
     LSE_EMPTY,
     bf16_value,
     build,
     bwd,
+    codebook_index,
     fp8e4m3_value,
     fwd_bitmap,
     fwd_lut,

@@ -90,6 +90,8 @@ typedef struct {
   int kv_dtype;
   const float* k_scale;
   const float* v_scale;
+  const float* k_codebook; /* codebook modes: 256 (i8) or 16 (i4) entries */
+  const float* v_codebook;
   const int32_t* vbs;
   double sm_scale;
   int32_t H, Hk;  /* query heads, key/value heads (H a multiple of Hk) */
@@ -97,12 +99,31 @@ typedef struct {
   int32_t D, block;
 } attn_args;
 
+/* Codebook index of element `elem` of a codebook-coded tensor (rocke
+ * "sage_attention.py", codebook-dequant primitives): i8 codes index a
+ * 256-entry table at code + 128; i4 codes are packed two per byte, element
+ * 2i in the low nibble and 2i+1 in the high nibble (two's complement in
+ * [-8, 7]), and index a 16-entry table at code + 8. */
+int bsa_oracle_codebook_index(int kv_dtype, const void* base, int64_t elem) {
+  if (kv_dtype == ORACLE_KV_I8_CODEBOOK)
+    return (int)((const int8_t*)base)[elem] + 128;
+  const uint8_t byte = ((const uint8_t*)base)[elem >> 1];
+  const int nib = (elem & 1) ? (byte >> 4) : (byte & 15);
+  return (nib >= 8 ? nib - 16 : nib) + 8;
+}
+
 static double kv_value(const attn_args* a, const void* base, const float* scale,
-                       int64_t elem, int64_t scale_idx) {
-  if (a->kv_dtype == ORACLE_KV_BF16)
-    return bsa_oracle_bf16_value(((const uint16_t*)base)[elem]);
-  return bsa_oracle_fp8e4m3_value(((const uint8_t*)base)[elem]) *
-         (double)scale[scale_idx];
+                       const float* codebook, int64_t elem, int64_t scale_idx) {
+  switch (a->kv_dtype) {
+    case ORACLE_KV_BF16:
+      return bsa_oracle_bf16_value(((const uint16_t*)base)[elem]);
+    case ORACLE_KV_FP8E4M3:
+      return bsa_oracle_fp8e4m3_value(((const uint8_t*)base)[elem]) *
+             (double)scale[scale_idx];
+    default: /* codebook value times the block scale */
+      return (double)codebook[bsa_oracle_codebook_index(a->kv_dtype, base, elem)] *
+             (double)scale[scale_idx];
+  }
 }
 
 /* Computes the `block` output rows of unit (b, h, qb) given its selected set.
@@ -143,7 +164,8 @@ static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
       const int64_t srow = kvhead * NK + key / block;
       double s = 0.0;
       for (int32_t d = 0; d < D; ++d)
-        s += qd[d] * kv_value(a, a->k, a->k_scale, plane + key * D + d, srow);
+        s += qd[d] * kv_value(a, a->k, a->k_scale, a->k_codebook,
+                              plane + key * D + d, srow);
       t[j] = s * c;
       if (t[j] > m) m = t[j];
     }
@@ -156,7 +178,8 @@ static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
       const double w = exp2(t[j] - m);
       l += w;
       for (int32_t d = 0; d < D; ++d)
-        o[d] += w * kv_value(a, a->v, a->v_scale, plane + key * D + d, srow);
+        o[d] += w * kv_value(a, a->v, a->v_scale, a->v_codebook,
+                             plane + key * D + d, srow);
     }
     for (int32_t d = 0; d < D; ++d) o[d] /= l;
     lse[r] = m + log2(l);
@@ -170,6 +193,16 @@ static int check_dims(int32_t B, int32_t H, int32_t Hk, int32_t Sq,
   if (B <= 0 || H <= 0 || Hk <= 0 || Sq <= 0 || Sk <= 0 || D <= 0 || block <= 0)
     return 1;
   if (H % Hk != 0 || Sq % block != 0 || Sk % block != 0) return 1;
+  return 0;
+}
+
+static int check_kv(int kv_dtype, const float* k_scale, const float* v_scale,
+                    const float* k_codebook, const float* v_codebook,
+                    int32_t D) {
+  if (kv_dtype < ORACLE_KV_BF16 || kv_dtype > ORACLE_KV_I4_CODEBOOK) return 1;
+  if (kv_dtype != ORACLE_KV_BF16 && (!k_scale || !v_scale)) return 1;
+  if (kv_dtype >= ORACLE_KV_I8_CODEBOOK && (!k_codebook || !v_codebook)) return 1;
+  if (kv_dtype == ORACLE_KV_I4_CODEBOOK && D % 2 != 0) return 1;
   return 0;
 }
 
@@ -241,6 +274,7 @@ static int run_fwd(const attn_args* a, const sel_args* s, int32_t B,
 
 int bsa_oracle_fwd_lut(const uint16_t* q, const void* k, const void* v,
                        int kv_dtype, const float* k_scale, const float* v_scale,
+                       const float* k_codebook, const float* v_codebook,
                        const int32_t* q2k_idx, const int32_t* q2k_num,
                        int32_t max_kv, int64_t meta_stride_b,
                        int64_t meta_stride_h, const int32_t* vbs,
@@ -250,11 +284,10 @@ int bsa_oracle_fwd_lut(const uint16_t* q, const void* k, const void* v,
                        double* lse) {
   if (!q || !k || !v || !q2k_idx || !q2k_num || !out || !lse) return 1;
   if (check_dims(B, H, Hk, Sq, Sk, D, block) || max_kv < 1) return 1;
-  if (kv_dtype != ORACLE_KV_BF16 && kv_dtype != ORACLE_KV_FP8E4M3) return 1;
-  if (kv_dtype == ORACLE_KV_FP8E4M3 && (!k_scale || !v_scale)) return 1;
+  if (check_kv(kv_dtype, k_scale, v_scale, k_codebook, v_codebook, D)) return 1;
   if (check_units(units, n_units, (int64_t)B * H * (Sq / block))) return 1;
-  attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, vbs, sm_scale, H, Hk,
-                 Sq, Sk, D, block};
+  attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, k_codebook, v_codebook,
+                 vbs, sm_scale, H, Hk, Sq, Sk, D, block};
   sel_args s = {FORM_LUT, q2k_idx, q2k_num, max_kv, meta_stride_b,
                 meta_stride_h, NULL};
   return run_fwd(&a, &s, B, units, n_units, out, lse);
@@ -262,7 +295,8 @@ int bsa_oracle_fwd_lut(const uint16_t* q, const void* k, const void* v,
 
 int bsa_oracle_fwd_bitmap(const uint16_t* q, const void* k, const void* v,
                           int kv_dtype, const float* k_scale,
-                          const float* v_scale, const int8_t* mask,
+                          const float* v_scale, const float* k_codebook,
+                          const float* v_codebook, const int8_t* mask,
                           int64_t mask_stride_b, int64_t mask_stride_h,
                           const int32_t* vbs, double sm_scale, int32_t B,
                           int32_t H, int32_t Hk, int32_t Sq, int32_t Sk,
@@ -270,11 +304,10 @@ int bsa_oracle_fwd_bitmap(const uint16_t* q, const void* k, const void* v,
                           int64_t n_units, double* out, double* lse) {
   if (!q || !k || !v || !mask || !out || !lse) return 1;
   if (check_dims(B, H, Hk, Sq, Sk, D, block)) return 1;
-  if (kv_dtype != ORACLE_KV_BF16 && kv_dtype != ORACLE_KV_FP8E4M3) return 1;
-  if (kv_dtype == ORACLE_KV_FP8E4M3 && (!k_scale || !v_scale)) return 1;
+  if (check_kv(kv_dtype, k_scale, v_scale, k_codebook, v_codebook, D)) return 1;
   if (check_units(units, n_units, (int64_t)B * H * (Sq / block))) return 1;
-  attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, vbs, sm_scale, H, Hk,
-                 Sq, Sk, D, block};
+  attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, k_codebook, v_codebook,
+                 vbs, sm_scale, H, Hk, Sq, Sk, D, block};
   sel_args s = {FORM_BITMAP, NULL, NULL, 0, mask_stride_b, mask_stride_h,
                 mask};
   return run_fwd(&a, &s, B, units, n_units, out, lse);
@@ -406,8 +439,8 @@ int bsa_oracle_bwd(int form, const uint16_t* q, const uint16_t* k,
   if (form == FORM_LUT && (!q2k_idx || !q2k_num || max_kv < 1)) return 1;
   if (form == FORM_BITMAP && !mask) return 1;
   if (form != FORM_LUT && form != FORM_BITMAP) return 1;
-  attn_args a = {q, k, v, ORACLE_KV_BF16, NULL, NULL, vbs, sm_scale, H, Hk,
-                 Sq, Sk, D, block};
+  attn_args a = {q, k, v, ORACLE_KV_BF16, NULL, NULL, NULL, NULL, vbs,
+                 sm_scale, H, Hk, Sq, Sk, D, block};
   sel_args s;
   if (form == FORM_LUT) {
     sel_args t = {FORM_LUT, q2k_idx, q2k_num, max_kv, meta_stride_b,

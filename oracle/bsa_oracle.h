@@ -58,22 +58,35 @@
 extern "C" {
 #endif
 
-enum { ORACLE_KV_BF16 = 0, ORACLE_KV_FP8E4M3 = 1 };
+enum {
+  ORACLE_KV_BF16 = 0,        /* bf16 values                                  */
+  ORACLE_KV_FP8E4M3 = 1,     /* fp8 e4m3fn code value times the block scale  */
+  ORACLE_KV_I8_CODEBOOK = 2, /* 256-entry f32 codebook[i8 + 128] times scale */
+  ORACLE_KV_I4_CODEBOOK = 3  /* 16-entry f32 codebook[i4 + 8] times scale,
+                                two codes per byte, even element low nibble */
+};
+
+/* Codebook index (0..255 or 0..15) of element `elem` of a codebook-coded
+ * tensor (kv_dtype 2 or 3). */
+int bsa_oracle_codebook_index(int kv_dtype, const void* base, int64_t elem);
 
 /* Value of one bf16 bit pattern (exact). */
 double bsa_oracle_bf16_value(uint16_t bits);
 /* Value of one OCP fp8 e4m3fn byte (exact; NaN for S.1111.111). */
 double bsa_oracle_fp8e4m3_value(uint8_t byte);
 
-/* q: bf16 bits [B,H,Sq,D]; k, v: bf16 bits or fp8 bytes [B,Hk,Sk,D] with
- * H a multiple of Hk (query head h reads K/V head h/(H/Hk));
- * k_scale, v_scale: fp32 [B,Hk,Sk/block] (fp8 only, else ignored);
+/* q: bf16 bits [B,H,Sq,D]; k, v: [B,Hk,Sk,D] bf16 bits, fp8 bytes or i8
+ * codes, or [B,Hk,Sk,D/2] packed i4 codes, per kv_dtype, with H a multiple
+ * of Hk (query head h reads K/V head h/(H/Hk));
+ * k_scale, v_scale: fp32 [B,Hk,Sk/block] (all but bf16, else ignored);
+ * k_codebook, v_codebook: fp32 tables (codebook modes, else ignored);
  * q2k_idx: int32 rows x max_kv, q2k_num: int32 rows, with
  * row = b*meta_stride_b + h*meta_stride_h + qb (qb < Sq/block), entries
  * naming key blocks in [0, Sk/block);
  * vbs: int32 [Sk/block] or NULL (all blocks full). */
 int bsa_oracle_fwd_lut(const uint16_t* q, const void* k, const void* v,
                        int kv_dtype, const float* k_scale, const float* v_scale,
+                       const float* k_codebook, const float* v_codebook,
                        const int32_t* q2k_idx, const int32_t* q2k_num,
                        int32_t max_kv, int64_t meta_stride_b,
                        int64_t meta_stride_h, const int32_t* vbs,
@@ -87,7 +100,8 @@ int bsa_oracle_fwd_lut(const uint16_t* q, const void* k, const void* v,
  * nonzero = attend. */
 int bsa_oracle_fwd_bitmap(const uint16_t* q, const void* k, const void* v,
                           int kv_dtype, const float* k_scale,
-                          const float* v_scale, const int8_t* mask,
+                          const float* v_scale, const float* k_codebook,
+                          const float* v_codebook, const int8_t* mask,
                           int64_t mask_stride_b, int64_t mask_stride_h,
                           const int32_t* vbs, double sm_scale, int32_t B,
                           int32_t H, int32_t Hk, int32_t Sq, int32_t Sk,

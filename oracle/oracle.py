@@ -19,6 +19,8 @@ import torch
 
 KV_BF16 = 0
 KV_FP8E4M3 = 1
+KV_I8_CODEBOOK = 2  # int8 codes, 256-entry codebook at code + 128
+KV_I4_CODEBOOK = 3  # uint8 bytes of two i4 codes (even element low nibble)
 # Finite LSE sentinel of a query row that attends to no key: the lowest finite
 # binary32 value (a stand-in for log(0) that merges with weight 0).
 LSE_EMPTY = float(np.finfo(np.float32).min)
@@ -49,12 +51,14 @@ def _lib():
         lib.bsa_oracle_fp8e4m3_value.restype = f64
         lib.bsa_oracle_fp8e4m3_value.argtypes = [ctypes.c_uint8]
         lib.bsa_oracle_fwd_lut.restype = ctypes.c_int
+        lib.bsa_oracle_codebook_index.restype = ctypes.c_int
+        lib.bsa_oracle_codebook_index.argtypes = [ctypes.c_int, P, i64]
         lib.bsa_oracle_fwd_lut.argtypes = [
-            P, P, P, ctypes.c_int, P, P, P, P, i32, i64, i64, P, f64,
+            P, P, P, ctypes.c_int, P, P, P, P, P, P, i32, i64, i64, P, f64,
             i32, i32, i32, i32, i32, i32, i32, P, i64, P, P]
         lib.bsa_oracle_fwd_bitmap.restype = ctypes.c_int
         lib.bsa_oracle_fwd_bitmap.argtypes = [
-            P, P, P, ctypes.c_int, P, P, P, i64, i64, P, f64,
+            P, P, P, ctypes.c_int, P, P, P, P, P, i64, i64, P, f64,
             i32, i32, i32, i32, i32, i32, i32, P, i64, P, P]
         lib.bsa_oracle_key_counts.restype = ctypes.c_int
         lib.bsa_oracle_key_counts.argtypes = [
@@ -99,7 +103,17 @@ def _kv_bits(t: torch.Tensor):
         return t.view(torch.int16), KV_BF16
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8), KV_FP8E4M3
+    if t.dtype == torch.int8:
+        return t, KV_I8_CODEBOOK
+    if t.dtype == torch.uint8:
+        return t, KV_I4_CODEBOOK
     raise TypeError(f"unsupported K/V dtype {t.dtype}")
+
+
+def codebook_index(kind: int, codes: torch.Tensor, elem: int) -> int:
+    """The oracle's codebook index of one element (kind 2 = i8, 3 = i4)."""
+    c = _cpu(codes)
+    return int(_lib().bsa_oracle_codebook_index(int(kind), _ptr(c), int(elem)))
 
 
 def _units_arg(units, total):
@@ -115,24 +129,34 @@ def _outputs(units, n, B, H, S, D, block):
     return np.empty((n, block, D)), np.empty((n, block))
 
 
-def _common(q, k, v, k_scale, v_scale):
+def _common(q, k, v, k_scale, v_scale, k_codebook=None, v_codebook=None):
     q = _cpu(q)
     assert q.dtype == torch.bfloat16 and q.dim() == 4
-    assert k.dim() == 4 and k.shape == v.shape and k.shape[0] == q.shape[0]
-    assert k.shape[3] == q.shape[3] and q.shape[1] % k.shape[1] == 0
     kb, kdt = _kv_bits(k)
     vb, vdt = _kv_bits(v)
     assert kdt == vdt, "K and V must share a dtype"
-    if kdt == KV_FP8E4M3:
+    width = q.shape[3] // 2 if kdt == KV_I4_CODEBOOK else q.shape[3]
+    assert k.dim() == 4 and k.shape == v.shape and k.shape[0] == q.shape[0]
+    assert k.shape[3] == width and q.shape[1] % k.shape[1] == 0
+    if kdt != KV_BF16:
         k_scale = _cpu(k_scale.to(torch.float32))
         v_scale = _cpu(v_scale.to(torch.float32))
     else:
         k_scale = v_scale = None
-    return q.view(torch.int16), kb, vb, kdt, k_scale, v_scale
+    if kdt in (KV_I8_CODEBOOK, KV_I4_CODEBOOK):
+        n = 256 if kdt == KV_I8_CODEBOOK else 16
+        k_codebook = _cpu(k_codebook.to(torch.float32))
+        v_codebook = _cpu(v_codebook.to(torch.float32))
+        assert k_codebook.numel() == n and v_codebook.numel() == n
+    else:
+        k_codebook = v_codebook = None
+    return (q.view(torch.int16), kb, vb, kdt, k_scale, v_scale, k_codebook,
+            v_codebook)
 
 
 def fwd_lut(q, k, v, q2k_idx, q2k_num, vbs=None, *, block, sm_scale=None,
-            k_scale=None, v_scale=None, meta_strides=None, units=None):
+            k_scale=None, v_scale=None, meta_strides=None, units=None,
+            k_codebook=None, v_codebook=None):
     """Oracle forward, LUT form.  ``q2k_idx`` is ``[..., max_kv]`` int32 and
     ``q2k_num`` the matching per-row counts; ``meta_strides=(sb, sh)`` gives
     the row of (b, h, qb) as ``b*sb + h*sh + qb`` (default: one row per
@@ -141,7 +165,8 @@ def fwd_lut(q, k, v, q2k_idx, q2k_num, vbs=None, *, block, sm_scale=None,
     B, H, S, D = q.shape
     Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
-    qb_, kb_, vb_, kdt, ks, vs = _common(q, k, v, k_scale, v_scale)
+    qb_, kb_, vb_, kdt, ks, vs, kc, vc = _common(q, k, v, k_scale, v_scale,
+                                                 k_codebook, v_codebook)
     idx = _cpu(q2k_idx.to(torch.int32))
     num = _cpu(q2k_num.to(torch.int32))
     max_kv = int(idx.shape[-1])
@@ -152,8 +177,8 @@ def fwd_lut(q, k, v, q2k_idx, q2k_num, vbs=None, *, block, sm_scale=None,
     u, n = _units_arg(units, B * H * NQ)
     out, lse = _outputs(units, n, B, H, S, D, block)
     rc = _lib().bsa_oracle_fwd_lut(
-        _ptr(qb_), _ptr(kb_), _ptr(vb_), kdt, _ptr(ks), _ptr(vs),
-        _ptr(idx), _ptr(num), max_kv, sb, sh, _ptr(vbs_t), float(sm_scale),
+        _ptr(qb_), _ptr(kb_), _ptr(vb_), kdt, _ptr(ks), _ptr(vs), _ptr(kc),
+        _ptr(vc), _ptr(idx), _ptr(num), max_kv, sb, sh, _ptr(vbs_t), float(sm_scale),
         B, H, Hk, S, Sk, D, block, _ptr(u), n,
         out.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p))
     if rc != 0:
@@ -162,14 +187,16 @@ def fwd_lut(q, k, v, q2k_idx, q2k_num, vbs=None, *, block, sm_scale=None,
 
 
 def fwd_bitmap(q, k, v, mask, vbs=None, *, block, sm_scale=None,
-               k_scale=None, v_scale=None, mask_strides=None, units=None):
+               k_scale=None, v_scale=None, mask_strides=None, units=None,
+               k_codebook=None, v_codebook=None):
     """Oracle forward, bitmap form.  ``mask`` is i8 rows of NK bytes;
     ``mask_strides=(sb, sh)`` as for the LUT (``(0, 0)`` = one shared
     ``[NQ, NK]`` mask).  Shapes as for ``fwd_lut``."""
     B, H, S, D = q.shape
     Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
-    qb_, kb_, vb_, kdt, ks, vs = _common(q, k, v, k_scale, v_scale)
+    qb_, kb_, vb_, kdt, ks, vs, kc, vc = _common(q, k, v, k_scale, v_scale,
+                                                 k_codebook, v_codebook)
     m = _cpu(mask.to(torch.int8))
     sb, sh = mask_strides if mask_strides is not None else (H * NQ, NQ)
     vbs_t = None if vbs is None else _cpu(vbs.to(torch.int32))
@@ -178,8 +205,8 @@ def fwd_bitmap(q, k, v, mask, vbs=None, *, block, sm_scale=None,
     u, n = _units_arg(units, B * H * NQ)
     out, lse = _outputs(units, n, B, H, S, D, block)
     rc = _lib().bsa_oracle_fwd_bitmap(
-        _ptr(qb_), _ptr(kb_), _ptr(vb_), kdt, _ptr(ks), _ptr(vs),
-        _ptr(m), sb, sh, _ptr(vbs_t), float(sm_scale),
+        _ptr(qb_), _ptr(kb_), _ptr(vb_), kdt, _ptr(ks), _ptr(vs), _ptr(kc),
+        _ptr(vc), _ptr(m), sb, sh, _ptr(vbs_t), float(sm_scale),
         B, H, Hk, S, Sk, D, block, _ptr(u), n,
         out.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p))
     if rc != 0:
@@ -229,7 +256,7 @@ def bwd(q, k, v, dout, *, block, q2k_idx=None, q2k_num=None, mask=None,
     B, H, S, D = q.shape
     Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
-    qb_, kb_, vb_, kdt, _, _ = _common(q, k, v, None, None)
+    qb_, kb_, vb_, kdt, _, _, _, _ = _common(q, k, v, None, None)
     assert kdt == KV_BF16, "the backward pass takes bf16 K/V"
     do = _cpu(dout)
     assert do.dtype == torch.bfloat16 and tuple(do.shape) == tuple(q.shape)

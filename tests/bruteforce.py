@@ -59,13 +59,33 @@ def dense_mask(w) -> np.ndarray:
     return m
 
 
+def codebook_values(codes: torch.Tensor, codebook: torch.Tensor) -> np.ndarray:
+    """float64 codebook levels of i8 codes (level = code + 128) or of uint8
+    bytes holding two i4 codes (element 2i in the low nibble, level =
+    code + 8), by numpy indexing."""
+    cb = codebook.to(torch.float64).numpy()
+    c = codes.numpy()
+    if c.dtype == np.int8:
+        return cb[c.astype(np.int64) + 128]
+    lo = (c & 15).astype(np.int64)
+    hi = (c >> 4).astype(np.int64)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    idx = np.stack([lo, hi], axis=-1).reshape(*c.shape[:-1], c.shape[-1] * 2)
+    return cb[idx + 8]
+
+
 def kv_f64(w):
     """Decoded K and V as float64 [B,H,Sk,D], one copy per query head
     (query head h uses K/V head h // (H // Hk)); fp8: code value x block
     scale, decoded by torch's float8_e4m3fn."""
-    if w.kv_fp8:
-        k = to_f64(w.k.to(torch.float32))
-        v = to_f64(w.v.to(torch.float32))
+    if w.kv_fp8 or w.kv_codebook:
+        if w.kv_fp8:
+            k = to_f64(w.k.to(torch.float32))
+            v = to_f64(w.v.to(torch.float32))
+        else:
+            k = codebook_values(w.k, w.k_codebook)
+            v = codebook_values(w.v, w.v_codebook)
         ks = np.repeat(to_f64(w.k_scale), w.block, axis=-1)[..., None]
         vs = np.repeat(to_f64(w.v_scale), w.block, axis=-1)[..., None]
         k, v = k * ks, v * vs

@@ -56,7 +56,8 @@ def run_gpu(w, *, need_lse=True, dev_inputs=None, prefill=float("nan")):
 
 def run_oracle(w, units=None):
     kw = dict(block=w.block, sm_scale=w.sm_scale, k_scale=w.k_scale,
-              v_scale=w.v_scale, units=units)
+              v_scale=w.v_scale, units=units,
+              k_codebook=w.k_codebook, v_codebook=w.v_codebook)
     if w.form == "lut":
         return oracle.fwd_lut(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs,
                               meta_strides=w.meta_strides, **kw)

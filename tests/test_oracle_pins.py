@@ -23,7 +23,8 @@ LOG2E = 1.0 / math.log(2.0)
 
 def run_oracle(w, **kw):
     args = dict(block=w.block, sm_scale=w.sm_scale, k_scale=w.k_scale,
-                v_scale=w.v_scale)
+                v_scale=w.v_scale,
+                k_codebook=w.k_codebook, v_codebook=w.v_codebook)
     args.update(kw)
     if w.form == "lut":
         return oracle.fwd_lut(w.q, w.k, w.v, w.q2k_idx, w.q2k_num, w.vbs,
@@ -153,6 +154,11 @@ BRUTE_CASES = [
          density=0.5, vbs_mode="partial"),
     dict(seed=11, block=128, S=256, Sk=512, H=4, Hk=1, kv="fp8",
          count_mode="uniform", vbs_mode="random"),
+    dict(seed=12, block=64, S=256, kv="i8cb", density=0.5, vbs_mode="random"),
+    dict(seed=13, block=64, S=256, kv="i4cb", form="bitmap", density=0.6,
+         vbs_mode="partial"),
+    dict(seed=14, block=128, S=256, Sk=512, H=4, Hk=2, kv="i4cb",
+         count_mode="uniform"),
 ]
 
 
@@ -542,3 +548,35 @@ def test_backward_is_linear_in_dout_and_dv_is_p_transpose_dout():
         np.testing.assert_allclose(b_, -2.0 * a_, atol=1e-12, rtol=1e-12)
     g0 = _oracle_bwd(w, torch.zeros_like(d1))
     assert all(not x.any() for x in g0)
+
+
+# ------------------------------------------------------- codebook K/V
+
+def test_codebook_index_worked_example():
+    """i8: level = code + 128.  i4: two codes per byte, element 2i in the
+    low nibble, two's complement, level = code + 8 (rocke
+    "sage_attention.py", codebook-dequant primitives)."""
+    i8 = torch.tensor([-128, -1, 0, 127], dtype=torch.int8)
+    assert [oracle.codebook_index(oracle.KV_I8_CODEBOOK, i8, e)
+            for e in range(4)] == [0, 127, 128, 255]
+    i4 = torch.tensor([0x9F, 0x70], dtype=torch.uint8)
+    # 0x9F: low 0xF = -1 -> 7, high 0x9 = -7 -> 1; 0x70: low 0 -> 8, high 7 -> 15
+    assert [oracle.codebook_index(oracle.KV_I4_CODEBOOK, i4, e)
+            for e in range(4)] == [7, 1, 8, 15]
+
+
+def test_integer_codebook_equals_bf16_values():
+    """An integer codebook with unit scales is the same attention as bf16
+    K/V holding those integers: bitwise equal oracle results."""
+    w = workloads.make_random(97, B=1, H=2, S=256, block=64, kv="i8cb",
+                              density=0.5, vbs_mode="partial")
+    w.k_codebook = torch.arange(-128, 128, dtype=torch.float32) / 16.0
+    w.v_codebook = torch.arange(-128, 128, dtype=torch.float32) / 32.0
+    w.k_scale = torch.ones_like(w.k_scale)
+    w.v_scale = torch.ones_like(w.v_scale)
+    o, lse = run_oracle(w)
+    kb = torch.from_numpy(bf.codebook_values(w.k, w.k_codebook)).to(torch.bfloat16)
+    vb = torch.from_numpy(bf.codebook_values(w.v, w.v_codebook)).to(torch.bfloat16)
+    o2, l2 = oracle.fwd_lut(w.q, kb, vb, w.q2k_idx, w.q2k_num, w.vbs,
+                            block=w.block, meta_strides=w.meta_strides)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)

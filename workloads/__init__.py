@@ -44,6 +44,8 @@ class Workload:
     mask: Optional[torch.Tensor] = None  # int8 [rows, NK]
     mask_strides: tuple = (0, 0)
     vbs: Optional[torch.Tensor] = None  # int32 [NK] or None (all full)
+    k_codebook: Optional[torch.Tensor] = None  # fp32 [256] (i8) / [16] (i4)
+    v_codebook: Optional[torch.Tensor] = None
     sm_scale: float = 1.0 / (HEAD_DIM ** 0.5)
     extra: dict = field(default_factory=dict)
 
@@ -72,6 +74,11 @@ class Workload:
     @property
     def kv_fp8(self) -> bool:
         return self.k.dtype == torch.float8_e4m3fn
+
+    @property
+    def kv_codebook(self) -> bool:
+        """K/V stored as i8 codes (int8) or packed i4 codes (uint8)."""
+        return self.k.dtype in (torch.int8, torch.uint8)
 
 
 CONFIG_NAMES = [
@@ -112,6 +119,38 @@ def quantize_fp8_per_block(x: torch.Tensor, block: int):
     scale = (amax / 448.0).clamp_min(torch.finfo(torch.float32).tiny)
     codes = (t / scale[..., None]).to(torch.float8_e4m3fn).reshape(B, H, S, D)
     return codes, scale.to(torch.float32).contiguous()
+
+
+def make_codebook(g, n: int) -> torch.Tensor:
+    """A sorted, nonuniform fp32 codebook of n levels whose values are exact
+    in bf16 (seeded normal draws, rounded to bf16)."""
+    cb = torch.randn((n,), generator=g, dtype=torch.float32).sort().values
+    return cb.to(torch.bfloat16).to(torch.float32).contiguous()
+
+
+def quantize_codebook_per_block(x: torch.Tensor, block: int,
+                                codebook: torch.Tensor, bits: int):
+    """Per-(b, h, key block) codebook quantisation of an fp32 [B,H,S,D]
+    tensor: scale = amax / max|codebook| over each [block, D] tile, code =
+    the nearest codebook level of x/scale.  bits 8: int8 codes in [-128, 127]
+    (level = code + 128); bits 4: uint8 bytes of two codes in [-8, 7] (level
+    = code + 8), element 2i in the low nibble.  Returns (codes, scale
+    [B,H,NK])."""
+    B, H, S, D = x.shape
+    t = x.reshape(B, H, S // block, block * D)
+    amax = t.abs().amax(dim=-1)
+    scale = (amax / codebook.abs().max()).clamp_min(torch.finfo(torch.float32).tiny)
+    y = (t / scale[..., None]).reshape(-1)
+    # nearest level: compare with the midpoints of the sorted codebook
+    mids = (codebook[1:] + codebook[:-1]) * 0.5
+    level = torch.searchsorted(mids, y.contiguous())
+    level = level.reshape(B, H, S, D)
+    if bits == 8:
+        codes = (level - 128).to(torch.int8)
+    else:
+        c = (level - 8) & 15  # two's complement nibbles
+        codes = (c[..., 0::2] | (c[..., 1::2] << 4)).to(torch.uint8)
+    return codes.contiguous(), scale.to(torch.float32).contiguous()
 
 
 def make_config(i: int, seed: Optional[int] = None) -> Workload:
@@ -190,8 +229,9 @@ def make_random(seed: int, *, B=1, H=2, S=512, block=64, form="lut",
     count_mode: "fixed" (round(density*NK) per row), "uniform" (U{0..max_kv}),
     "zero" (every row 0).  vbs_mode: "full" (None), "random" (U{0..block}),
     "partial" (U{1..block}), "zero_some" (some blocks 0).  kv: "bf16" or
-    "fp8".  Hk (key/value heads, default H) and Sk (key length, default S)
-    give grouped-query and rectangular cases."""
+    "fp8", or "i8cb" / "i4cb" (codebook-coded K/V with seeded bf16-exact
+    codebooks).  Hk (key/value heads, default H) and Sk (key length, default
+    S) give grouped-query and rectangular cases."""
     g = _gen(seed)
     D = HEAD_DIM
     Hk = H if Hk is None else Hk
@@ -199,15 +239,26 @@ def make_random(seed: int, *, B=1, H=2, S=512, block=64, form="lut",
     NQ = S // block
     NK = Sk // block
     q = _randn(g, (B, H, S, D), std=std)
+    kc = vc = None
     if kv == "bf16":
         k = _randn(g, (B, Hk, Sk, D), std=std)
         v = _randn(g, (B, Hk, Sk, D), std=std)
         ks = vs = None
-    else:
+    elif kv == "fp8":
         k, ks = quantize_fp8_per_block(
             torch.randn((B, Hk, Sk, D), generator=g) * std, block)
         v, vs = quantize_fp8_per_block(
             torch.randn((B, Hk, Sk, D), generator=g) * std, block)
+    elif kv in ("i8cb", "i4cb"):
+        bits = 8 if kv == "i8cb" else 4
+        kc = make_codebook(g, 1 << bits)
+        vc = make_codebook(g, 1 << bits)
+        k, ks = quantize_codebook_per_block(
+            torch.randn((B, Hk, Sk, D), generator=g) * std, block, kc, bits)
+        v, vs = quantize_codebook_per_block(
+            torch.randn((B, Hk, Sk, D), generator=g) * std, block, vc, bits)
+    else:
+        raise ValueError(kv)
     rows = NQ if shared_meta else B * H * NQ
     strides = (0, 0) if shared_meta else (H * NQ, NQ)
     if vbs_mode == "full":
@@ -225,7 +276,8 @@ def make_random(seed: int, *, B=1, H=2, S=512, block=64, form="lut",
         mask = (torch.rand((rows, NK), generator=g) < density).to(torch.int8)
         return Workload(f"random_bitmap_{seed}", B, H, S, D, block, "bitmap",
                         q, k, v, k_scale=ks, v_scale=vs, mask=mask,
-                        mask_strides=strides, vbs=vbs)
+                        mask_strides=strides, vbs=vbs, k_codebook=kc,
+                        v_codebook=vc)
     if max_kv is None:
         max_kv = NK
     take = min(max_kv, NK)
@@ -247,4 +299,5 @@ def make_random(seed: int, *, B=1, H=2, S=512, block=64, form="lut",
     idx = torch.where(padm, torch.full_like(idx, pad_value), idx).contiguous()
     return Workload(f"random_lut_{seed}", B, H, S, D, block, "lut", q, k, v,
                     k_scale=ks, v_scale=vs, q2k_idx=idx, q2k_num=num,
-                    meta_strides=strides, vbs=vbs)
+                    meta_strides=strides, vbs=vbs, k_codebook=kc,
+                    v_codebook=vc)
