@@ -10,12 +10,16 @@ from .api import (  # noqa: F401
     BSA_ERR_NULL,
     BSA_ERR_SHAPE,
     BSA_ERR_UNSUPPORTED,
+    BSA_CODEBOOK_I4,
+    BSA_CODEBOOK_I8,
     BSA_KV_BF16,
+    BSA_KV_BF16_SCALED,
     BSA_KV_FP8E4M3,
     BSA_OK,
     LSE_EMPTY,
     BsaError,
     bsa_bwd,
+    bsa_codebook_dequant,
     bsa_fwd_bitmap,
     bsa_fwd_from_mask,
     bsa_fwd_lut,

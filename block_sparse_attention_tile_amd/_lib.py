@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libbsa.so")
 # The exported C symbols, as declared in include/bsa.h.
 EXPORTS = ("bsa_fwd_lut", "bsa_fwd_bitmap", "bsa_mask_to_lut",
            "bsa_bwd_workspace_size", "bsa_bwd_lut", "bsa_bwd_bitmap",
-           "bsa_status_str")
+           "bsa_codebook_dequant", "bsa_status_str")
 
 _lib = None
 
@@ -51,6 +51,8 @@ def load():
     lib.bsa_bwd_bitmap.argtypes = [
         P, P, P, P, P, P, P, i64, i64, P, f32, P, P, P, P, sz,
         i32, i32, i32, i32, i32, i32, i32, P]
+    lib.bsa_codebook_dequant.restype = ctypes.c_int32
+    lib.bsa_codebook_dequant.argtypes = [P, i32, P, P, i64, P]
     lib.bsa_status_str.restype = ctypes.c_char_p
     lib.bsa_status_str.argtypes = [i32]
     _lib = lib

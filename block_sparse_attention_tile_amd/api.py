@@ -24,6 +24,9 @@ BSA_ERR_ALIGN = 4
 BSA_ERR_HIP = 5
 BSA_KV_BF16 = 0
 BSA_KV_FP8E4M3 = 1
+BSA_KV_BF16_SCALED = 2
+BSA_CODEBOOK_I8 = 0
+BSA_CODEBOOK_I4 = 1
 LSE_EMPTY = -3.4028234663852886e38  # BSA_LSE_EMPTY = -FLT_MAX
 
 
@@ -48,25 +51,66 @@ def _kv_dtype(k: torch.Tensor, v: torch.Tensor) -> int:
         return BSA_KV_BF16
     if k.dtype == torch.float8_e4m3fn:
         return BSA_KV_FP8E4M3
+    if k.dtype in (torch.int8, torch.uint8):
+        return BSA_KV_BF16_SCALED  # codebook codes, dequantised first
     raise TypeError(f"unsupported k/v dtype {k.dtype}")
+
+
+def bsa_codebook_dequant(codes: torch.Tensor, codebook: torch.Tensor,
+                         stream: Optional[torch.cuda.Stream] = None
+                         ) -> torch.Tensor:
+    """bf16 codebook values of codebook-coded K or V: int8 codes
+    ``[..., D]`` (256-entry codebook) or uint8 bytes of packed int4 codes
+    ``[..., D/2]`` (16-entry codebook).  Returns bf16 ``[..., D]``; the
+    per-block scale is not applied."""
+    if codes.dtype == torch.int8:
+        kind, shape = BSA_CODEBOOK_I8, tuple(codes.shape)
+    elif codes.dtype == torch.uint8:
+        kind, shape = BSA_CODEBOOK_I4, tuple(codes.shape[:-1]) + (2 * codes.shape[-1],)
+    else:
+        raise TypeError("codes must be int8 (i8) or uint8 (packed i4)")
+    codes = codes.contiguous()
+    cb = codebook.to(device=codes.device, dtype=torch.float32).contiguous()
+    if cb.numel() != (256 if kind == BSA_CODEBOOK_I8 else 16):
+        raise ValueError("codebook must have 256 (i8) or 16 (i4) entries")
+    out = torch.empty(shape, dtype=torch.bfloat16, device=codes.device)
+    n = out.numel()
+    st = (stream or torch.cuda.current_stream(codes.device)).cuda_stream
+    rc = _lib.load().bsa_codebook_dequant(_ptr(codes), kind, _ptr(cb), _ptr(out),
+                                          n, ctypes.c_void_p(st))
+    if rc != BSA_OK:
+        raise BsaError(rc)
+    return out
 
 
 def _i32(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
     return None if t is None else t.to(torch.int32).contiguous()
 
 
-def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block):
+def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block,
+             k_codebook=None, v_codebook=None, stream=None):
     if q.dtype != torch.bfloat16 or q.dim() != 4:
         raise TypeError("q must be a 4-D bf16 [B, H, S, D] tensor")
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    if k.dtype in (torch.int8, torch.uint8):
+        if k_codebook is None or v_codebook is None:
+            raise ValueError("codebook-coded k/v need k_codebook and v_codebook")
+        if k.dtype != v.dtype:
+            raise TypeError("k and v must have the same dtype")
+        k = bsa_codebook_dequant(k, k_codebook, stream)
+        v = bsa_codebook_dequant(v, v_codebook, stream)
+        kvd = BSA_KV_BF16_SCALED
+    else:
+        kvd = None
     if k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] \
             or k.shape[3] != q.shape[3] or q.shape[1] % k.shape[1] != 0:
         raise ValueError("q must be [B, H, S, D] and k, v [B, Hk, Sk, D] with "
                          "H a multiple of Hk")
-    kvd = _kv_dtype(k, v)
-    if kvd == BSA_KV_FP8E4M3:
+    if kvd is None:
+        kvd = _kv_dtype(k, v)
+    if kvd != BSA_KV_BF16:
         if k_scale is None or v_scale is None:
-            raise ValueError("fp8 k/v need k_scale and v_scale")
+            raise ValueError("fp8 and codebook k/v need k_scale and v_scale")
         k_scale = k_scale.to(torch.float32).contiguous()
         v_scale = v_scale.to(torch.float32).contiguous()
     else:
@@ -90,13 +134,16 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 meta_strides: Optional[Tuple[int, int]] = None,
                 need_lse: bool = True, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None,
-                stream: Optional[torch.cuda.Stream] = None):
+                stream: Optional[torch.cuda.Stream] = None,
+                k_codebook: Optional[torch.Tensor] = None,
+                v_codebook: Optional[torch.Tensor] = None):
     """VSA form.  Returns ``(out, lse)`` (``lse`` is None if not needed).
     ``q`` is ``[B, H, S, D]``, ``k``/``v`` ``[B, Hk, Sk, D]`` (query head h
     reads K/V head h // (H // Hk)).  ``meta_strides=(sb, sh)``: the LUT row
     of (b, h, qb) is ``b*sb + h*sh + qb``; default one row per unit."""
     q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
-                                              lse, need_lse, block)
+                                              lse, need_lse, block, k_codebook,
+                                              v_codebook, stream)
     B, H, S, D = q.shape
     Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
@@ -126,13 +173,16 @@ def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    mask_strides: Optional[Tuple[int, int]] = None,
                    need_lse: bool = True, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None,
-                   stream: Optional[torch.cuda.Stream] = None):
+                   stream: Optional[torch.cuda.Stream] = None,
+                   k_codebook: Optional[torch.Tensor] = None,
+                   v_codebook: Optional[torch.Tensor] = None):
     """Jenga form.  ``mask`` is an int8 (or bool) tensor of rows of S/block
     bytes; ``mask_strides=(sb, sh)`` as in the LUT form ((0, 0) = one
     [NQ, NK] mask shared by all batches and heads).  Shapes as in the LUT
     form."""
     q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
-                                              lse, need_lse, block)
+                                              lse, need_lse, block, k_codebook,
+                                              v_codebook, stream)
     B, H, S, D = q.shape
     Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block

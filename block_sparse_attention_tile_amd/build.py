@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "bsa_fwd.hip"),
            os.path.join(PKG, "csrc", "bsa_mask.hip"),
-           os.path.join(PKG, "csrc", "bsa_bwd.hip")]
+           os.path.join(PKG, "csrc", "bsa_bwd.hip"),
+           os.path.join(PKG, "csrc", "bsa_codebook.hip")]
 LIB = os.path.join(PKG, "libbsa.so")
 
 HIPCC_FLAGS = [

@@ -298,14 +298,18 @@ __device__ __forceinline__ void issue_bf16(const char* kg, const char* vg,
 // waves in 32 KB of LDS, so LDS would allow 4 per SIMD; capping registers
 // at 168 gives 3 (bf16 only: the fp8 staging registers do not fit).  A
 // 64-row unit is held at 2 per SIMD by LDS anyway.
-template <int BLK, bool FP8>
+template <int BLK, int KV>
 constexpr int waves_per_simd() {
-  return (BLK == 128 && !FP8) ? 3 : 2;
+  return (BLK == 128 && KV == BSA_KV_BF16) ? 3 : 2;
 }
 
-template <int BLK, bool FP8, bool BITMAP>
-__global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, FP8>())) void bsa_fwd_kernel(
+// KV: BSA_KV_BF16, BSA_KV_FP8E4M3 or BSA_KV_BF16_SCALED (bf16 values with
+// per-block scales, folded in exactly as for fp8).
+template <int BLK, int KV, bool BITMAP>
+__global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_kernel(
     FwdParams p) {
+  constexpr bool FP8 = KV == BSA_KV_FP8E4M3;  // codes staged through VGPRs
+  constexpr bool SCALED = KV != BSA_KV_BF16;  // per-block K/V scales
   constexpr int NW = BLK / 32;  // waves; each owns 32 query rows
   constexpr int NT = NW * 64;
   // All LDS is dynamic, so the stages start at LDS address 0 and every
@@ -433,13 +437,15 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, FP8>())) void bsa_fwd
     const int nvt = t.nv - t.t0;
     if constexpr (FP8) {
       load_tile_fp8<NT>(st, kplane + key0 * HD, vplane + key0 * HD, nvt, tid);
-      ksc_nxt = p.k_scale[scale_row + t.kb];
-      vsc_nxt = p.v_scale[scale_row + t.kb];
     } else {
       const char* kg = kplane + key0 * ROWB;
       const char* vg = vplane + key0 * ROWB;
       const uint32_t sl = smem_lds + stg * STAGE_BYTES;
       issue_bf16<NW>(kg, vg, sl, sl + TILE_BYTES, dko, dvo, wave, l4, nvt);
+    }
+    if constexpr (SCALED) {
+      ksc_nxt = p.k_scale[scale_row + t.kb];
+      vsc_nxt = p.v_scale[scale_row + t.kb];
     }
   };
 
@@ -462,8 +468,8 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, FP8>())) void bsa_fwd
     cursor.reset(lane);
     Tile cur = cursor.at(0, lane);
     issue(cur, 0);
-    if constexpr (FP8) {
-      store_tile_fp8<NT>(st, smem, tid);
+    if constexpr (FP8) store_tile_fp8<NT>(st, smem, tid);
+    if constexpr (SCALED) {
       ksc_cur = ksc_nxt;
       vsc_cur = vsc_nxt;
     }
@@ -484,7 +490,7 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, FP8>())) void bsa_fwd
       const char* sb = smem + STG * STAGE_BYTES;
       float cs = p.c;
       float vsc = 1.f;
-      if constexpr (FP8) {
+      if constexpr (SCALED) {
         cs *= ksc_cur;
         vsc = vsc_cur;
       }
@@ -510,7 +516,7 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, FP8>())) void bsa_fwd
             acc.m[qt] = mnew;
           }
         }
-        tile_probs<FP8>(sv, cs, vsc, acc, pop);
+        tile_probs<SCALED>(sv, cs, vsc, acc, pop);
       };
       if (nvt >= KT) body(IntC<FULL>{});
       else body(IntC<PART>{});
@@ -519,8 +525,8 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, FP8>())) void bsa_fwd
       tile_pv(sb, vbase, pop, acc);
 
       if (!has_next) return true;
-      if constexpr (FP8) {
-        store_tile_fp8<NT>(st, smem + (STG ^ 1) * STAGE_BYTES, tid);
+      if constexpr (FP8) store_tile_fp8<NT>(st, smem + (STG ^ 1) * STAGE_BYTES, tid);
+      if constexpr (SCALED) {
         ksc_cur = ksc_nxt;
         vsc_cur = vsc_nxt;
       }
@@ -579,9 +585,9 @@ size_t lds_bytes(int NK) {
          (size_t)NK * sizeof(uint32_t);
 }
 
-template <int BLK, bool FP8, bool BITMAP>
+template <int BLK, int KV, bool BITMAP>
 bsa_status launch(const FwdParams& p, hipStream_t stream) {
-  auto kern = bsa_fwd_kernel<BLK, FP8, BITMAP>;
+  auto kern = bsa_fwd_kernel<BLK, KV, BITMAP>;
   const size_t lds = lds_bytes(p.NK);
   if (lds > 65536) {
     if (hipFuncSetAttribute((const void*)kern,
@@ -593,11 +599,19 @@ bsa_status launch(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 
+template <bool BITMAP, int BLK>
+bsa_status dispatch_kv(const FwdParams& p, int kv, hipStream_t s) {
+  switch (kv) {
+    case BSA_KV_FP8E4M3: return launch<BLK, BSA_KV_FP8E4M3, BITMAP>(p, s);
+    case BSA_KV_BF16_SCALED: return launch<BLK, BSA_KV_BF16_SCALED, BITMAP>(p, s);
+    default: return launch<BLK, BSA_KV_BF16, BITMAP>(p, s);
+  }
+}
+
 template <bool BITMAP>
-bsa_status dispatch(const FwdParams& p, int block, bool fp8, hipStream_t s) {
-  if (block == 64)
-    return fp8 ? launch<64, true, BITMAP>(p, s) : launch<64, false, BITMAP>(p, s);
-  return fp8 ? launch<128, true, BITMAP>(p, s) : launch<128, false, BITMAP>(p, s);
+bsa_status dispatch(const FwdParams& p, int block, int kv, hipStream_t s) {
+  if (block == 64) return dispatch_kv<BITMAP, 64>(p, kv, s);
+  return dispatch_kv<BITMAP, 128>(p, kv, s);
 }
 
 bool aligned16(const void* x) { return ((uintptr_t)x & 15u) == 0; }
@@ -614,9 +628,10 @@ bsa_status check_common(const void* q, const void* k, const void* v,
   if (S % block != 0 || Sk % block != 0 || H % Hk != 0) return BSA_ERR_SHAPE;
   if (D != HD) return BSA_ERR_UNSUPPORTED;
   if (block != 64 && block != 128) return BSA_ERR_UNSUPPORTED;
-  if (kv_dtype != BSA_KV_BF16 && kv_dtype != BSA_KV_FP8E4M3)
+  if (kv_dtype != BSA_KV_BF16 && kv_dtype != BSA_KV_FP8E4M3 &&
+      kv_dtype != BSA_KV_BF16_SCALED)
     return BSA_ERR_UNSUPPORTED;
-  if (kv_dtype == BSA_KV_FP8E4M3 && (!k_scale || !v_scale)) return BSA_ERR_NULL;
+  if (kv_dtype != BSA_KV_BF16 && (!k_scale || !v_scale)) return BSA_ERR_NULL;
   if (Sk / block > BSA_MAX_KEY_BLOCKS) return BSA_ERR_UNSUPPORTED;
   const int64_t units = (int64_t)B * H * (S / block);
   if (units > INT32_MAX || (int64_t)B * H * S > INT32_MAX ||
@@ -677,7 +692,7 @@ extern "C" bsa_status bsa_fwd_lut(const void* q, const void* k, const void* v,
   p.max_kv = max_kv;
   p.meta_sb = meta_stride_b;
   p.meta_sh = meta_stride_h;
-  return dispatch<false>(p, block, kv_dtype == BSA_KV_FP8E4M3,
+  return dispatch<false>(p, block, kv_dtype,
                          (hipStream_t)stream);
 }
 
@@ -700,7 +715,7 @@ extern "C" bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v
   p.mask = mask;
   p.meta_sb = mask_stride_b;
   p.meta_sh = mask_stride_h;
-  return dispatch<true>(p, block, kv_dtype == BSA_KV_FP8E4M3,
+  return dispatch<true>(p, block, kv_dtype,
                         (hipStream_t)stream);
 }
 

@@ -66,12 +66,23 @@ typedef enum {
 
 typedef enum {
   BSA_KV_BF16 = 0,   /* K and V are bf16 [B, H, S, D]                          */
-  BSA_KV_FP8E4M3 = 1 /* K and V are OCP fp8 e4m3 ("fn") bytes [B, H, S, D],
+  BSA_KV_FP8E4M3 = 1, /* K and V are OCP fp8 e4m3 ("fn") bytes [B, H, S, D],
                         each key block dequantised as code value times its
                         fp32 scale (rocke "sage_attention.py", module
                         docstring: K/V dequantised per block before the score
                         and the PV product)                                   */
+  BSA_KV_BF16_SCALED = 2 /* K and V are bf16 values [B, H, S, D] times their
+                        per-block fp32 scale: the form the codebook modes of
+                        the same page take after bsa_codebook_dequant (value
+                        = codebook[code], scale applied here, exactly as for
+                        fp8: folded into the score scale and into P)          */
 } bsa_kv_dtype;
+
+typedef enum {
+  BSA_CODEBOOK_I8 = 0, /* int8 codes, 256-entry table at code + 128           */
+  BSA_CODEBOOK_I4 = 1  /* two int4 codes per byte (element 2i in the low
+                          nibble, two's complement), 16 entries at code + 8 */
+} bsa_codebook_kind;
 
 /*
  * bsa_fwd_lut -- VSA (look-up-table) form.
@@ -220,6 +231,29 @@ bsa_status bsa_bwd_bitmap(const void* q, const void* k, const void* v,
                           size_t workspace_bytes, int32_t B, int32_t H,
                           int32_t Hk, int32_t S, int32_t Sk, int32_t D,
                           int32_t block, void* stream);
+
+/*
+ * bsa_codebook_dequant -- codebook K/V codes to bf16 values (rocke
+ * "sage_attention.py": K/V stored as i8 or i4 codes of an f32 codebook,
+ * dequantised as codebook[code] times the per-block scale).  Writes
+ * out[i] = bf16(codebook[level(i)]) (round to nearest even); the per-block
+ * scale is applied by the forward call with kv_dtype BSA_KV_BF16_SCALED.
+ *
+ *  codes     device memory: n_values int8 codes (kind BSA_CODEBOOK_I8,
+ *            16-byte aligned) or n_values/2 bytes of packed int4 codes
+ *            (BSA_CODEBOOK_I4, 8-byte aligned).
+ *  codebook  fp32 device table of 256 (i8) or 16 (i4) entries.
+ *  out       bf16 device buffer of n_values elements, 16-byte aligned.
+ *  n_values  number of values, a multiple of 16 (0 launches nothing).
+ *  stream    hipStream_t (void*), NULL = null stream.
+ *
+ * Exact given the bf16 rounding of the table.  Errors: BSA_ERR_UNSUPPORTED
+ * (unknown kind), BSA_ERR_SHAPE, BSA_ERR_NULL, BSA_ERR_ALIGN, BSA_ERR_HIP;
+ * on error nothing is launched.
+ */
+bsa_status bsa_codebook_dequant(const void* codes, int32_t kind,
+                                const float* codebook, void* out,
+                                int64_t n_values, void* stream);
 
 /* Static text of a status code (never NULL). */
 const char* bsa_status_str(int32_t status);

@@ -171,3 +171,22 @@ def test_bwd_workspace_size_covers_delta_and_map():
 ])
 def test_bwd_rejects_invalid_static_arguments(over, status):
     assert bwd_lut(**over) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, 0, A, A, 15, None), api.BSA_ERR_SHAPE),      # not a multiple of 16
+    ((A, 0, A, A, -16, None), api.BSA_ERR_SHAPE),
+    ((A, 5, A, A, 16, None), api.BSA_ERR_UNSUPPORTED),
+    ((None, 0, A, A, 16, None), api.BSA_ERR_NULL),
+    ((A, 1, None, A, 16, None), api.BSA_ERR_NULL),
+    ((A + 8, 0, A, A, 16, None), api.BSA_ERR_ALIGN),  # i8 codes need 16 B
+    ((A, 0, A, A + 8, 16, None), api.BSA_ERR_ALIGN),
+    ((None, 0, None, None, 0, None), api.BSA_OK),      # empty: no launch
+])
+def test_codebook_dequant_rejects_invalid_static_arguments(args, status):
+    assert _lib.load().bsa_codebook_dequant(*args) == status
+
+
+def test_lut_accepts_scaled_bf16_mode_only_with_scales():
+    assert lut(kv=2) == api.BSA_ERR_NULL
+    assert lut(kv=2, ks=A) == api.BSA_ERR_NULL

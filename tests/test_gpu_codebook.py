@@ -1,0 +1,126 @@
+"""Codebook K/V on the GPU: bsa_codebook_dequant bit-exact against torch
+indexing of the bf16-rounded codebook, and the forward pass on
+codebook-coded K/V (dequantisation + BSA_KV_BF16_SCALED) against the
+oracle's codebook modes."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_tile_amd as bsa
+import workloads
+from tests.gpu_helpers import check, log, run_oracle, scaled_input_bounds
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def levels(codes: torch.Tensor) -> torch.Tensor:
+    """Codebook levels by numpy (i8: code + 128; i4: nibbles, low first)."""
+    c = codes.numpy()
+    if c.dtype == np.int8:
+        return torch.from_numpy(c.astype(np.int64) + 128)
+    lo = (c & 15).astype(np.int64)
+    hi = (c >> 4).astype(np.int64)
+    lv = np.stack([np.where(lo >= 8, lo - 16, lo), np.where(hi >= 8, hi - 16, hi)],
+                  axis=-1).reshape(*c.shape[:-1], 2 * c.shape[-1]) + 8
+    return torch.from_numpy(lv)
+
+
+@pytest.mark.parametrize("kind,n", [("i8", 16), ("i8", 4096 * 48), ("i4", 16),
+                                    ("i4", 4096 * 32), ("i8", 0)])
+def test_dequant_bit_exact(kind, n):
+    g = torch.Generator().manual_seed(n + len(kind))
+    ent = 256 if kind == "i8" else 16
+    cb = torch.randn((ent,), generator=g) * 3.0  # not bf16-exact: RNE path
+    if kind == "i8":
+        codes = torch.randint(-128, 128, (n,), generator=g, dtype=torch.int8)
+    else:
+        codes = torch.randint(0, 256, (n // 2,), generator=g,
+                              dtype=torch.int32).to(torch.uint8)
+    log(f"[dequant] {kind} n={n}")
+    got = bsa.bsa_codebook_dequant(codes.cuda(), cb.cuda())
+    torch.cuda.synchronize()
+    ref = cb.to(torch.bfloat16)[levels(codes)]
+    assert got.shape == ref.shape
+    assert torch.equal(got.cpu().view(torch.int16), ref.view(torch.int16))
+
+
+CASES = [
+    ("i8_lut64", dict(seed=401, B=1, H=2, S=512, block=64, kv="i8cb",
+                      density=0.5, vbs_mode="partial")),
+    ("i4_lut64_uniform", dict(seed=402, B=2, H=2, S=512, block=64, kv="i4cb",
+                              count_mode="uniform", vbs_mode="random")),
+    ("i4_bitmap128", dict(seed=403, B=1, H=2, S=1024, block=128, kv="i4cb",
+                          form="bitmap", density=0.4)),
+    ("i8_gqa_rect", dict(seed=404, B=1, H=4, Hk=2, S=512, Sk=768, block=64,
+                         kv="i8cb", count_mode="uniform", vbs_mode="zero_some")),
+    ("i4_gqa128", dict(seed=405, B=1, H=6, Hk=3, S=512, Sk=1024, block=128,
+                       kv="i4cb", density=0.5, vbs_mode="partial")),
+]
+
+
+def vmax(w) -> float:
+    """Largest dequantised |V| (codebook level times block scale): the
+    codebook levels span each block's range, so the bound derived for
+    inputs beyond N(0, 1) applies (P rounded to bf16 moves O by at most
+    2^-9 max|V|)."""
+    return float(w.v_codebook.abs().max() * w.v_scale.max())
+
+
+def run_codebook_gpu(w):
+    d = {n: (None if getattr(w, n) is None else getattr(w, n).cuda())
+         for n in ("q", "k", "v", "k_scale", "v_scale", "q2k_idx", "q2k_num",
+                   "mask", "vbs", "k_codebook", "v_codebook")}
+    out = torch.full(tuple(w.q.shape), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.full((w.B, w.H, w.S), float("nan"), dtype=torch.float32,
+                     device="cuda")
+    kw = dict(block=w.block, sm_scale=w.sm_scale, k_scale=d["k_scale"],
+              v_scale=d["v_scale"], k_codebook=d["k_codebook"],
+              v_codebook=d["v_codebook"], out=out, lse=lse)
+    if w.form == "lut":
+        bsa.bsa_fwd_lut(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"],
+                        d["vbs"], meta_strides=w.meta_strides, **kw)
+    else:
+        bsa.bsa_fwd_bitmap(d["q"], d["k"], d["v"], d["mask"], d["vbs"],
+                           mask_strides=w.mask_strides, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("label,kw", CASES, ids=[c[0] for c in CASES])
+def test_codebook_forward_parity(label, kw):
+    kw = dict(kw)
+    w = workloads.make_random(kw.pop("seed"), **kw)
+    log(f"[codebook fwd] {label} {w.k.dtype} B{w.B} H{w.H} Hk{w.Hk} S{w.S} "
+        f"Sk{w.Sk} blk{w.block}")
+    out, lse = run_codebook_gpu(w)
+    o_ref, l_ref = run_oracle(w)
+    o_abs, o_rel = scaled_input_bounds(vmax(w))
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, label,
+          o_rel=o_rel, o_abs=o_abs)
+
+
+def test_codebook_not_bf16_exact_uses_rounded_table():
+    """With an fp32 codebook that bf16 cannot hold, the GPU result is the
+    attention over the bf16-rounded table (the operand precision): parity
+    against the oracle run on that rounded table."""
+    w = workloads.make_random(406, B=1, H=2, S=512, block=64, kv="i8cb",
+                              density=0.5)
+    g = torch.Generator().manual_seed(9)
+    w.k_codebook = (w.k_codebook + torch.randn(256, generator=g) * 1e-3)
+    w.v_codebook = (w.v_codebook + torch.randn(256, generator=g) * 1e-3)
+    log("[codebook fwd] fp32 codebook")
+    out, lse = run_codebook_gpu(w)
+    w.k_codebook = w.k_codebook.to(torch.bfloat16).float()
+    w.v_codebook = w.v_codebook.to(torch.bfloat16).float()
+    o_ref, l_ref = run_oracle(w)
+    o_abs, o_rel = scaled_input_bounds(vmax(w))
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref,
+          "fp32 codebook", o_rel=o_rel, o_abs=o_abs)
