@@ -86,18 +86,39 @@ def attended_pairs(w, units=None) -> int:
     return int((sel.long() * nv[None, :]).sum()) * w.block
 
 
+def codebook_recode(w, kind: str):
+    """The workload with its K/V re-coded as codebook codes (seeded
+    bf16-exact codebooks of 256 (i8) or 16 (i4) levels, per-block scales)."""
+    g = torch.Generator().manual_seed(1000)
+    bits = 8 if kind == "i8cb" else 4
+    kc = workloads.make_codebook(g, 1 << bits)
+    vc = workloads.make_codebook(g, 1 << bits)
+    src_k = w.k.float() * (w.k_scale.repeat_interleave(w.block, -1)[..., None]
+                           if w.k_scale is not None else 1.0)
+    src_v = w.v.float() * (w.v_scale.repeat_interleave(w.block, -1)[..., None]
+                           if w.v_scale is not None else 1.0)
+    w.k, w.k_scale = workloads.quantize_codebook_per_block(src_k, w.block, kc, bits)
+    del src_k
+    w.v, w.v_scale = workloads.quantize_codebook_per_block(src_v, w.block, vc, bits)
+    w.k_codebook, w.v_codebook = kc, vc
+    w.name = f"{w.name}_{kind}"
+    return w
+
+
 def launch(w, d, out, lse):
-    """One forward pass; lse=None is the inference route (no LSE store)."""
+    """One forward pass; lse=None is the inference route (no LSE store).
+    Codebook-coded K/V are dequantised inside the call."""
+    cb = dict(k_codebook=d.get("k_codebook"), v_codebook=d.get("v_codebook"))
     if w.form == "lut":
         bsa.bsa_fwd_lut(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"],
                         d["vbs"], block=w.block, sm_scale=w.sm_scale,
-                        k_scale=d["k_scale"], v_scale=d["v_scale"],
+                        k_scale=d["k_scale"], v_scale=d["v_scale"], **cb,
                         meta_strides=w.meta_strides, out=out, lse=lse,
                         need_lse=lse is not None)
     else:
         bsa.bsa_fwd_bitmap(d["q"], d["k"], d["v"], d["mask"], d["vbs"],
                            block=w.block, sm_scale=w.sm_scale,
-                           k_scale=d["k_scale"], v_scale=d["v_scale"],
+                           k_scale=d["k_scale"], v_scale=d["v_scale"], **cb,
                            mask_strides=w.mask_strides, out=out, lse=lse,
                            need_lse=lse is not None)
 
@@ -176,7 +197,8 @@ def cpu_baseline(w, target_s: float):
     g = np.random.default_rng(1234)
     order = g.permutation(w.n_units)
     kw = dict(block=w.block, sm_scale=w.sm_scale, k_scale=w.k_scale,
-              v_scale=w.v_scale)
+              v_scale=w.v_scale, k_codebook=w.k_codebook,
+              v_codebook=w.v_codebook)
 
     def run(units):
         t0 = time.perf_counter()
@@ -323,6 +345,10 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2,
                     help="named workload index (default 2: video-shaped VSA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv", default=None, choices=("i8cb", "i4cb"),
+                    help="re-code the workload's K/V as i8 / packed-i4 "
+                         "codebook codes (each step then includes the "
+                         "dequantisation pass)")
     ap.add_argument("--no-lse", action="store_true",
                     help="inference route: the forward pass without the LSE "
                          "output")
@@ -369,12 +395,15 @@ def main() -> int:
 
     progress(f"generating workload {args.workload}")
     w = workloads.make_config(args.workload)
+    if args.kv:
+        progress(f"re-coding K/V as {args.kv}")
+        w = codebook_recode(w, args.kv)
     pairs = attended_pairs(w)
     flop = 4.0 * w.D * pairs
     dev = torch.device("cuda:0")
     d = {n: (None if getattr(w, n) is None else getattr(w, n).to(dev))
          for n in ("q", "k", "v", "k_scale", "v_scale", "q2k_idx", "q2k_num",
-                   "mask", "vbs")}
+                   "mask", "vbs", "k_codebook", "v_codebook")}
     out = torch.empty(tuple(w.q.shape), dtype=torch.bfloat16, device=dev)
     lse = None if args.no_lse else torch.empty((w.B, w.H, w.S),
                                                dtype=torch.float32, device=dev)
@@ -412,7 +441,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3-kv/bf16" if w.kv_fp8 else "bf16",
+        "dtype": ("fp8e4m3-kv/bf16" if w.kv_fp8 else
+                  f"{args.kv}-kv/bf16" if args.kv else "bf16"),
         "data": "synthetic",
         "config": {
             "workload": w.name,
