@@ -463,23 +463,35 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
       issue_rows<NW>((const char*)(p.dout + r0 * HD), sl + TILE_BYTES, dko, wave, l4, KT);
     };
 
+    // this lane's LSE / delta of a tile: query rows g*4 + j and 16 + g*4 + j,
+    // loaded one tile ahead together with the tile's Q / dO
+    f32x4 ls0, ls1, de0, de1;
+    auto load_rows = [&](int64_t r0) {
+      ls0 = *(const f32x4*)(p.lse + r0 + g * 4);
+      ls1 = *(const f32x4*)(p.lse + r0 + 16 + g * 4);
+      de0 = *(const f32x4*)(p.delta + r0 + g * 4);
+      de1 = *(const f32x4*)(p.delta + r0 + 16 + g * 4);
+    };
     int64_t r_cur = tile_rows(0);
     issue(r_cur, 0);
+    f32x4 nls0, nls1, nde0, nde1;
+    load_rows(r_cur);
+    nls0 = ls0; nls1 = ls1; nde0 = de0; nde1 = de1;
     int t = 0;
     auto step = [&](auto stg_c) -> bool {
       constexpr int STG = decltype(stg_c)::value;
-      // this lane's LSE / delta: query rows g*4 + j and 16 + g*4 + j
-      const f32x4 ls0 = *(const f32x4*)(p.lse + r_cur + g * 4);
-      const f32x4 ls1 = *(const f32x4*)(p.lse + r_cur + 16 + g * 4);
-      const f32x4 de0 = *(const f32x4*)(p.delta + r_cur + g * 4);
-      const f32x4 de1 = *(const f32x4*)(p.delta + r_cur + 16 + g * 4);
       wait_vm_all();
       __syncthreads();
+      ls0 = nls0; ls1 = nls1; de0 = nde0; de1 = nde1;
       const bool has_next = t + 1 < ntiles;
       int64_t r_nxt = 0;
       if (has_next) {
         r_nxt = tile_rows(t + 1);
         issue(r_nxt, STG ^ 1);
+        nls0 = *(const f32x4*)(p.lse + r_nxt + g * 4);
+        nls1 = *(const f32x4*)(p.lse + r_nxt + 16 + g * 4);
+        nde0 = *(const f32x4*)(p.delta + r_nxt + g * 4);
+        nde1 = *(const f32x4*)(p.delta + r_nxt + 16 + g * 4);
       }
       const char* qt_ = smem + STG * BSTAGE;
       const char* dot = qt_ + TILE_BYTES;
