@@ -413,6 +413,14 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
   __syncthreads();
   if (wave == 0) {
     const int n = compact_list(map, gq, list, lane);
+    // entry -> first query row (in [B*H*S]) of the listed unit, so the tile
+    // walk needs no division
+    for (int i = lane; i < n; i += 64) {
+      const int e = (int)(list[i] >> 8);
+      const int hl = e / p.NQ, qb = e - hl * p.NQ;
+      const int64_t bh = (int64_t)b * p.H + (int64_t)kvh * p.group + hl;
+      list[i] = (uint32_t)(bh * p.S + (int64_t)qb * BLK);
+    }
     if (lane == 0) *s_n = n;
   }
   __syncthreads();
@@ -452,10 +460,9 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
 
     // query tile t: unit list[t / QT_PER_UNIT], rows (t % QT_PER_UNIT)*32 ..
     auto tile_rows = [&](int t) -> int64_t {  // first row in [B*H*S]
-      const int e = __builtin_amdgcn_readfirstlane((int)(list[t / QT_PER_UNIT] >> 8));
-      const int hl = e / p.NQ, qb = e % p.NQ;
-      const int64_t bh = (int64_t)b * p.H + (int64_t)kvh * p.group + hl;
-      return bh * p.S + (int64_t)qb * BLK + (t % QT_PER_UNIT) * 32;
+      const uint32_t r0 =
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)list[t / QT_PER_UNIT]);
+      return (int64_t)r0 + (t % QT_PER_UNIT) * 32;
     };
     auto issue = [&](int64_t r0, int stg) {
       const uint32_t sl = smem_lds + stg * BSTAGE;
