@@ -373,7 +373,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
 // 4. dK, dV: one workgroup per (b, K/V head, key block), BLK/16 waves of 16
 // keys each.  The keys' K and V rows are B operands in registers (rows past
 // the block's valid count zeroed).  For every attending query unit, in
-// 32-row query tiles (Q and dO tiles in LDS with the row swizzle):
+// 64-row query steps (Q and dO as two 32-row tiles each in LDS with the row
+// swizzle, the rows' LSE and delta beside them):
 //   S[q][key] = Q K^T                A = Q rows,   B = K^T (registers)
 //   P = 2^(S c - LSE_q),  0 for keys past the count
 //   dP[q][key] = dO V^T              A = dO rows,  B = V^T (registers)
@@ -381,13 +382,18 @@ __global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
 //   dV^T[d][key] += dO^T P           A = dO^T (transposing reads), B = P
 //   dK^T[d][key] += Q^T dS           A = Q^T (transposing reads),  B = dS
 // P and dS are B operands with the query permutation 8g+i <-> 4g+i /
-// 16+4g+(i-4) across the two 16-row query tiles.
+// 16+4g+(i-4) across two 16-row query sub-tiles.
+
+constexpr int QSTEP = 64;                                 // query rows per step
+constexpr int DSTAGE = 4 * TILE_BYTES + 1024;             // Q, dO, LSE, delta
+constexpr int LSE_OFF = 4 * TILE_BYTES;                   // 64 floats
+constexpr int DLT_OFF = 4 * TILE_BYTES + 256;             // 64 floats
 
 template <int BLK>
 __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
   constexpr int NW = BLK / 16;
   constexpr int NT = NW * 64;
-  constexpr int QT_PER_UNIT = BLK / 32;  // 32-row query tiles per unit
+  constexpr int QT_PER_UNIT = BLK / QSTEP;  // query steps per unit
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -395,8 +401,8 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
   const int g = lane >> 4;
   const int r16 = lane & 15;
   const int gq = p.group * p.NQ;  // map entries per key block
-  int* s_n = (int*)(smem + 2 * BSTAGE);
-  uint8_t* map = (uint8_t*)(smem + 2 * BSTAGE + 16);
+  int* s_n = (int*)(smem + 2 * DSTAGE);
+  uint8_t* map = (uint8_t*)(smem + 2 * DSTAGE + 16);
   uint32_t* list = (uint32_t*)(map + ((gq + 15) & ~15));
 
   const int u = remap_unit(blockIdx.x, p.n_units);  // units = B*Hk*NK here
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
   __syncthreads();
   if (wave == 0) {
     const int n = compact_list(map, gq, list, lane);
-    // entry -> first query row (in [B*H*S]) of the listed unit, so the tile
+    // entry -> first query row (in [B*H*S]) of the listed unit, so the step
     // walk needs no division
     for (int i = lane; i < n; i += 64) {
       const int e = (int)(list[i] >> 8);
@@ -425,13 +431,13 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
   }
   __syncthreads();
   const int nunits = nv > 0 ? *s_n : 0;
-  const int ntiles = nunits * QT_PER_UNIT;
+  const int nsteps = nunits * QT_PER_UNIT;
 
   f32x4 dka[8], dva[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) dka[dt] = dva[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (ntiles > 0) {
+  if (nsteps > 0) {
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
     // K^T / V^T B operands: column key, rows d = kk*32 + g*8 ..
     bf16x8 kreg[4], vreg[4];
@@ -458,88 +464,90 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
     const uint32_t abase = (uint32_t)(r16 * ROWB + ((g ^ r16) << 4));
     const uint32_t trb = tr_base(lane);
 
-    // query tile t: unit list[t / QT_PER_UNIT], rows (t % QT_PER_UNIT)*32 ..
-    auto tile_rows = [&](int t) -> int64_t {  // first row in [B*H*S]
+    // query step t: unit list[t / QT_PER_UNIT], rows (t % QT_PER_UNIT)*64 ..
+    auto step_rows = [&](int t) -> int64_t {  // first row in [B*H*S]
       const uint32_t r0 =
           (uint32_t)__builtin_amdgcn_readfirstlane((int)list[t / QT_PER_UNIT]);
-      return (int64_t)r0 + (t % QT_PER_UNIT) * 32;
+      return (int64_t)r0 + (t % QT_PER_UNIT) * QSTEP;
     };
+    // Q rows r0..r0+63 -> two tiles, dO likewise, LSE and delta (64 floats
+    // each, lanes 0..15 of waves 0 and 1)
     auto issue = [&](int64_t r0, int stg) {
-      const uint32_t sl = smem_lds + stg * BSTAGE;
-      issue_rows<NW>((const char*)(p.q + r0 * HD), sl, dko, wave, l4, KT);
-      issue_rows<NW>((const char*)(p.dout + r0 * HD), sl + TILE_BYTES, dko, wave, l4, KT);
+      const uint32_t sl = smem_lds + stg * DSTAGE;
+      const char* qg = (const char*)(p.q + r0 * HD);
+      const char* dg = (const char*)(p.dout + r0 * HD);
+      issue_rows<NW>(qg, sl, dko, wave, l4, KT);
+      issue_rows<NW>(qg + TILE_BYTES, sl + TILE_BYTES, dko, wave, l4, KT);
+      issue_rows<NW>(dg, sl + 2 * TILE_BYTES, dko, wave, l4, KT);
+      issue_rows<NW>(dg + TILE_BYTES, sl + 3 * TILE_BYTES, dko, wave, l4, KT);
+      if (wave < 2 && lane < 16) {
+        const float* src = wave == 0 ? p.lse : p.delta;
+        dma16u((const char*)(src + r0), (uint32_t)lane * 16u,
+               sl + (wave == 0 ? LSE_OFF : DLT_OFF));
+      }
     };
 
-    // this lane's LSE / delta of a tile: query rows g*4 + j and 16 + g*4 + j,
-    // loaded one tile ahead together with the tile's Q / dO
-    f32x4 ls0, ls1, de0, de1;
-    auto load_rows = [&](int64_t r0) {
-      ls0 = *(const f32x4*)(p.lse + r0 + g * 4);
-      ls1 = *(const f32x4*)(p.lse + r0 + 16 + g * 4);
-      de0 = *(const f32x4*)(p.delta + r0 + g * 4);
-      de1 = *(const f32x4*)(p.delta + r0 + 16 + g * 4);
-    };
-    int64_t r_cur = tile_rows(0);
-    issue(r_cur, 0);
-    f32x4 nls0, nls1, nde0, nde1;
-    load_rows(r_cur);
-    nls0 = ls0; nls1 = ls1; nde0 = de0; nde1 = de1;
+    issue(step_rows(0), 0);
     int t = 0;
     auto step = [&](auto stg_c) -> bool {
       constexpr int STG = decltype(stg_c)::value;
       wait_vm_all();
       __syncthreads();
-      ls0 = nls0; ls1 = nls1; de0 = nde0; de1 = nde1;
-      const bool has_next = t + 1 < ntiles;
-      int64_t r_nxt = 0;
-      if (has_next) {
-        r_nxt = tile_rows(t + 1);
-        issue(r_nxt, STG ^ 1);
-        nls0 = *(const f32x4*)(p.lse + r_nxt + g * 4);
-        nls1 = *(const f32x4*)(p.lse + r_nxt + 16 + g * 4);
-        nde0 = *(const f32x4*)(p.delta + r_nxt + g * 4);
-        nde1 = *(const f32x4*)(p.delta + r_nxt + 16 + g * 4);
-      }
-      const char* qt_ = smem + STG * BSTAGE;
-      const char* dot = qt_ + TILE_BYTES;
-      f32x4 s[2], dp[2];
+      const bool has_next = t + 1 < nsteps;
+      if (has_next) issue(step_rows(t + 1), STG ^ 1);
+      const char* qtile = smem + STG * DSTAGE;
+      const char* dtile = qtile + 2 * TILE_BYTES;
+      // S and dP for four 16-row query sub-tiles qs (rows qs*16 ..)
+      f32x4 s[4], dp[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
-          const uint32_t a = (abase ^ (kk << 6)) + qh * 16 * ROWB;
-          const bf16x8 qop = *(const bf16x8*)(qt_ + a);
-          const bf16x8 dop = *(const bf16x8*)(dot + a);
+        for (int qs = 0; qs < 4; ++qs) {
+          const uint32_t a =
+              (abase ^ (kk << 6)) + (qs & 1) * 16 * ROWB + (qs >> 1) * TILE_BYTES;
+          const bf16x8 qop = *(const bf16x8*)(qtile + a);
+          const bf16x8 dop = *(const bf16x8*)(dtile + a);
           const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          s[qh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop, kreg[kk],
-                                                          kk == 0 ? z : s[qh], 0, 0, 0);
-          dp[qh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dop, vreg[kk],
-                                                           kk == 0 ? z : dp[qh], 0, 0, 0);
+          s[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop, kreg[kk],
+                                                          kk == 0 ? z : s[qs], 0, 0, 0);
+          dp[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dop, vreg[kk],
+                                                           kk == 0 ? z : dp[qs], 0, 0, 0);
         }
-      float pv[8], dsv[8];
+      // P and dS as B operands, one pair per 32-row half
+      bf16x8 pop[2], dsop[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int qh = e >> 2, j = e & 3;
-        const float l = qh ? ls1[j] : ls0[j];
-        const float d = qh ? de1[j] : de0[j];
-        const float pr = key < nv ? __builtin_amdgcn_exp2f(
-                                        __builtin_fmaf(s[qh][j], p.c, -l))
-                                  : 0.f;
-        pv[e] = pr;
-        dsv[e] = pr * (dp[qh][j] - d);
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 l0 = *(const f32x4*)(qtile + LSE_OFF + (hf * 32 + g * 4) * 4);
+        const f32x4 l1 = *(const f32x4*)(qtile + LSE_OFF + (hf * 32 + 16 + g * 4) * 4);
+        const f32x4 d0 = *(const f32x4*)(qtile + DLT_OFF + (hf * 32 + g * 4) * 4);
+        const f32x4 d1 = *(const f32x4*)(qtile + DLT_OFF + (hf * 32 + 16 + g * 4) * 4);
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int qs = hf * 2 + (e >> 2), j = e & 3;
+          const float l = (e >> 2) ? l1[j] : l0[j];
+          const float d = (e >> 2) ? d1[j] : d0[j];
+          const float pr = key < nv ? __builtin_amdgcn_exp2f(
+                                          __builtin_fmaf(s[qs][j], p.c, -l))
+                                    : 0.f;
+          pv[e] = pr;
+          dsv[e] = pr * (dp[qs][j] - d);
+        }
+        pop[hf] = pack8(pv);
+        dsop[hf] = pack8(dsv);
       }
-      const bf16x8 pop = pack8(pv);
-      const bf16x8 dsop = pack8(dsv);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const uint32_t a = trb ^ (uint32_t)(dt << 5);
-        dva[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_read(dot, a), pop, dva[dt],
-                                                          0, 0, 0);
-        dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_read(qt_, a), dsop, dka[dt],
-                                                          0, 0, 0);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          dva[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              tr_read(dtile + hf * TILE_BYTES, a), pop[hf], dva[dt], 0, 0, 0);
+          dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              tr_read(qtile + hf * TILE_BYTES, a), dsop[hf], dka[dt], 0, 0, 0);
+        }
       }
       if (!has_next) return true;
-      r_cur = r_nxt;
       ++t;
       return false;
     };
@@ -629,7 +637,7 @@ bsa_status run_bwd(BwdParams p, const void* out, float* delta, int8_t* map,
   {
     auto kern = dkdv_kernel<BLK>;
     const int gq = p.group * p.NQ;
-    const size_t lds = 2 * BSTAGE + 16 + (size_t)((gq + 15) & ~15) + (size_t)gq * 4;
+    const size_t lds = 2 * DSTAGE + 16 + (size_t)((gq + 15) & ~15) + (size_t)gq * 4;
     if (lds > 65536 && hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)lds) != hipSuccess)
