@@ -22,10 +22,15 @@
 //      padding and repetitions.
 //  A3  Q: each wave keeps its 32 query rows in VGPRs as MFMA operands for
 //      the whole K loop (loaded once with 128-bit loads).
-//  A4  K/V gather: 32-key tiles of the selected blocks, only rows below the
-//      block's valid count are read (direct global->LDS 128-bit loads; the
-//      lanes of rows past the count re-read row 0, fp8 writes zeros there).
-//      Tiles are double-buffered in LDS: the loads of tile i+1 are in flight
+//  A4  K/V gather in 32-key tiles, only rows below a block's valid count
+//      are read (direct global->LDS 128-bit loads).  bf16 K/V: the valid
+//      keys of the selected blocks, in list order, are cut into tiles as
+//      one stream, so a tile may draw rows from several blocks and only the
+//      unit's last tile is partial (with valid counts below the block size
+//      this removes the padded tail of every block).  With per-block scales
+//      (fp8, scaled bf16) each tile stays inside one block.  Lanes of rows
+//      past a tile's count re-read row 0 (fp8 writes zeros there).  Tiles
+//      are double-buffered in LDS: the loads of tile i+1 are in flight
 //      while tile i is computed.  fp8 e4m3 K/V are widened to bf16 exactly
 //      on the way into LDS.
 //  A5  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (fp32 accumulate), scaled by
@@ -157,6 +162,12 @@ __device__ __forceinline__ void store_tile_fp8(const Fp8Staging<NT>& st,
 // (keys past the count masked; the second 16-key half's QK^T is skipped
 // when it holds no valid key).
 enum TileKind { FULL = 0, PART = 1 };
+
+// Position in the stream of a unit's valid keys: entry e of the selected
+// list, key o of that entry's block.
+struct Walk {
+  int e, o;
+};
 
 // Accumulator state of one wave: O^T tiles, per-row reference m (log2
 // units, identical in the four lanes of a row) and per-lane partial sums l.
@@ -407,10 +418,14 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
                                     ((2 * ((lane >> 2) & 7) + ((lane & 3) >> 1)) << 4) +
                                     (lane & 1) * 8);
   const int l4 = lane >> 4, pos = lane & 15;
-  // DMA source offsets of this lane for its wave's slices (see issue_bf16)
-  [[maybe_unused]] uint32_t dko[8 / NW], dvo[8 / NW];
+  // DMA source offsets of this lane for its wave's slices (see issue_bf16).
+  // With 4 waves the two slices of a wave share their swizzle, so the
+  // stream path keeps one offset per tensor and reaches the second slice
+  // 4 KB further through the scalar base (fewer live registers).
+  constexpr int KP = (SCALED || NW != 4) ? 8 / NW : 1;
+  [[maybe_unused]] uint32_t dko[KP], dvo[KP];
 #pragma unroll
-  for (int i = 0; i < 8 / NW; ++i) {
+  for (int i = 0; i < KP; ++i) {
     const int j = wave + i * NW;
     dko[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ l4) ^ ((j & 3) << 2)) << 4));
     dvo[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ (2 * l4)) ^ ((j & 1) << 3)) << 4));
@@ -437,7 +452,7 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
     const int nvt = t.nv - t.t0;
     if constexpr (FP8) {
       load_tile_fp8<NT>(st, kplane + key0 * HD, vplane + key0 * HD, nvt, tid);
-    } else {
+    } else if constexpr (SCALED) {
       const char* kg = kplane + key0 * ROWB;
       const char* vg = vplane + key0 * ROWB;
       const uint32_t sl = smem_lds + stg * STAGE_BYTES;
@@ -447,6 +462,74 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
       ksc_nxt = p.k_scale[scale_row + t.kb];
       vsc_nxt = p.v_scale[scale_row + t.kb];
     }
+  };
+
+  // bf16 K/V without scales: the valid keys of the selected blocks, in
+  // list order, form one stream that is cut into 32-row tiles, so a tile
+  // may span several blocks and only the unit's last tile is partial.
+  // Starts the loads of the tile that begins at stream position w (entry
+  // w.e, key w.o of that block) into stage `stg`, moves w past it and
+  // returns the tile's row count (1..32).  A tile inside one block loads
+  // like a block tile; a tile that spans blocks adds, per lane, the offset
+  // of the run of rows its row falls in.  Rows past the count re-read row
+  // 0's chunk.
+  auto issue_stream = [&](Walk& w, int stg) -> int {
+    const Tile t = cursor.at(w.e, lane);
+    const int avail = t.nv - w.o;
+    const int64_t key0 = (int64_t)t.kb * BLK + w.o;  // key of row 0
+    const char* kg = kplane + key0 * ROWB;
+    const char* vg = vplane + key0 * ROWB;
+    const uint32_t sl = smem_lds + stg * STAGE_BYTES;
+    if (avail >= KT) {
+      // the whole tile lies in one block
+      w.o += KT;
+      if (w.o >= t.nv) {
+        ++w.e;
+        w.o = 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 8 / NW; ++i) {
+        const uint32_t j = (uint32_t)(wave + i * NW);
+        const int xb = (i / KP) * KP * NW * 1024;  // slice bytes past dko
+        dma16(kg + xb, dko[i % KP], sl + j * 1024u);
+        dma16(vg + xb, dvo[i % KP], sl + TILE_BYTES + j * 1024u);
+      }
+      return KT;
+    }
+    // Rows [0, avail) come from this block; later runs of rows from the
+    // following entries.  Row rr of a run that starts at row r0 in block kb
+    // holds key kb*BLK + rr - r0, i.e. it lies (kb*BLK - r0 - key0) rows
+    // past where a single-block tile would put it (>= 0: keys ascend).
+    int row = avail;
+    ++w.e;
+    w.o = 0;
+    uint32_t ex[8 / NW];
+#pragma unroll
+    for (int i = 0; i < 8 / NW; ++i) ex[i] = 0u;
+    while (row < KT && w.e < nsel) {
+      const Tile u = cursor.at(w.e, lane);
+      const int take = min(u.nv, KT - row);
+      const uint32_t d = (uint32_t)((int64_t)u.kb * BLK - row - key0) << 8;
+#pragma unroll
+      for (int i = 0; i < 8 / NW; ++i)
+        ex[i] = l4 >= row - 4 * (wave + i * NW) ? d : ex[i];
+      row += take;
+      if (take == u.nv) {
+        ++w.e;
+      } else {
+        w.o = take;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8 / NW; ++i) {
+      const int j = wave + i * NW;
+      const bool ok = 4 * j + l4 < row;
+      const uint32_t xb = (uint32_t)((i / KP) * KP * NW * 1024);
+      const uint32_t ko = dko[i % KP], vo = dvo[i % KP];
+      dma16(kg, ok ? ko + xb + ex[i] : (ko & 0xFFu), sl + (uint32_t)j * 1024u);
+      dma16(vg, ok ? vo + xb + ex[i] : (vo & 0xFFu), sl + TILE_BYTES + (uint32_t)j * 1024u);
+    }
+    return row;
   };
 
   // One pass of the K loop over every selected tile.
@@ -466,8 +549,15 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
     acc.l[0] = acc.l[1] = 0.f;
 
     cursor.reset(lane);
-    Tile cur = cursor.at(0, lane);
-    issue(cur, 0);
+    [[maybe_unused]] Tile cur{};
+    [[maybe_unused]] Walk walk{0, 0};
+    [[maybe_unused]] int cur_rows = 0;
+    if constexpr (SCALED) {
+      cur = cursor.at(0, lane);
+      issue(cur, 0);
+    } else {
+      cur_rows = issue_stream(walk, 0);
+    }
     if constexpr (FP8) store_tile_fp8<NT>(st, smem, tid);
     if constexpr (SCALED) {
       ksc_cur = ksc_nxt;
@@ -481,11 +571,20 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
       // tile `cur` complete in LDS for every wave; stage STG^1 free again
       wait_vm_all();
       __syncthreads();
-      const Tile nxt = cursor.next(cur, lane);
-      const bool has_next = nxt.e < nsel;
-      if (has_next) issue(nxt, STG ^ 1);
-
-      const int nvt = cur.nv - cur.t0;  // valid keys of this tile (>= 1)
+      [[maybe_unused]] Tile nxt{};
+      [[maybe_unused]] int nxt_rows = 0;
+      bool has_next;
+      int nvt;  // valid keys of this tile (>= 1)
+      if constexpr (SCALED) {
+        nxt = cursor.next(cur, lane);
+        has_next = nxt.e < nsel;
+        if (has_next) issue(nxt, STG ^ 1);
+        nvt = cur.nv - cur.t0;
+      } else {
+        has_next = walk.e < nsel;
+        if (has_next) nxt_rows = issue_stream(walk, STG ^ 1);
+        nvt = cur_rows;
+      }
       const int lim = nvt - 4 * g;
       const char* sb = smem + STG * STAGE_BYTES;
       float cs = p.c;
@@ -529,8 +628,10 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
       if constexpr (SCALED) {
         ksc_cur = ksc_nxt;
         vsc_cur = vsc_nxt;
+        cur = nxt;
+      } else {
+        cur_rows = nxt_rows;
       }
-      cur = nxt;
       return false;
     };
 

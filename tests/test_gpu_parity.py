@@ -70,6 +70,18 @@ SMALL = [
                           kv="fp8", density=0.5, vbs_mode="random")),
     ("gqa_rect128_shared", dict(seed=123, B=2, H=4, Hk=4, S=512, Sk=1536,
                                 block=128, shared_meta=True, density=0.3)),
+    # valid counts around tile and half-tile edges, and runs of very short
+    # blocks: 32-row tiles of the key stream span many blocks
+    ("lut64_vbs_edges", dict(seed=124, B=1, H=2, S=2048, block=64,
+                             density=0.6, vbs_mode="edges")),
+    ("lut64_vbs_tiny", dict(seed=125, B=1, H=2, S=4096, block=64,
+                            density=0.9, vbs_mode="tiny")),
+    ("lut128_vbs_edges", dict(seed=126, B=1, H=2, S=2048, block=128,
+                              count_mode="uniform", vbs_mode="edges")),
+    ("bitmap128_vbs_tiny", dict(seed=127, B=1, H=2, S=4096, block=128,
+                                form="bitmap", density=0.7, vbs_mode="tiny")),
+    ("gqa_rect64_vbs_edges", dict(seed=128, B=2, H=4, Hk=2, S=512, Sk=2048,
+                                  block=64, density=0.5, vbs_mode="edges")),
 ]
 
 

@@ -228,7 +228,9 @@ def make_random(seed: int, *, B=1, H=2, S=512, block=64, form="lut",
 
     count_mode: "fixed" (round(density*NK) per row), "uniform" (U{0..max_kv}),
     "zero" (every row 0).  vbs_mode: "full" (None), "random" (U{0..block}),
-    "partial" (U{1..block}), "zero_some" (some blocks 0).  kv: "bf16" or
+    "partial" (U{1..block}), "zero_some" (some blocks 0), "edges" (counts
+    at and around multiples of 16, and 0), "tiny" (U{1..4}: runs of many
+    short blocks).  kv: "bf16" or
     "fp8", or "i8cb" / "i4cb" (codebook-coded K/V with seeded bf16-exact
     codebooks).  Hk (key/value heads, default H) and Sk (key length, default
     S) give grouped-query and rectangular cases."""
@@ -270,6 +272,13 @@ def make_random(seed: int, *, B=1, H=2, S=512, block=64, form="lut",
     elif vbs_mode == "zero_some":
         vbs = torch.randint(0, block + 1, (NK,), generator=g, dtype=torch.int32)
         vbs[torch.rand((NK,), generator=g) < 0.3] = 0
+    elif vbs_mode == "edges":
+        vals = sorted({v for m in range(0, block + 1, 16) for v in (m - 1, m, m + 1)
+                       if 0 <= v <= block} | {2, 3})
+        pick = torch.randint(0, len(vals), (NK,), generator=g)
+        vbs = torch.tensor(vals, dtype=torch.int32)[pick]
+    elif vbs_mode == "tiny":
+        vbs = torch.randint(1, 5, (NK,), generator=g, dtype=torch.int32)
     else:
         raise ValueError(vbs_mode)
     if form == "bitmap":
