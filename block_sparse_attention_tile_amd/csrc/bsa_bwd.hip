@@ -17,9 +17,10 @@
 //                       query block) that attends it (1 = attends, the key
 //                       block has >= 1 valid key).  Duplicate stores write
 //                       the same 1, so no atomics are needed.
-//   3. dq_kernel        one workgroup per query unit, the same selected-block
-//                       walk as the forward pass; dQ accumulates in
-//                       registers and is written once.
+//   3. dq_kernel        one workgroup per query unit, the same walk as the
+//                       forward pass (32-row tiles cut from the stream of
+//                       the unit's valid keys); dQ accumulates in registers
+//                       and is written once.
 //   4. dkdv_kernel      one workgroup per (b, K/V head, key block): its keys
 //                       stay in registers while it walks every query unit
 //                       that attends the block (from the byte map), so dK and
@@ -283,25 +284,34 @@ __global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
   for (int dt = 0; dt < 8; ++dt)
     acc[dt][0] = acc[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Tiles are cut from the stream of the unit's valid keys (a tile may
+  // span blocks; only the last one is partial).
   ListCursor cursor{list, nsel, 0, 0u};
   cursor.reset(lane);
-  auto issue = [&](const Tile& t, int stg) {
-    const int64_t off = ((int64_t)t.kb * BLK + t.t0) * ROWB;
+  Walk walk{0, 0};
+  auto issue = [&](int stg) -> int {
     const uint32_t sl = smem_lds + stg * BSTAGE;
-    issue_rows<NW>(kplane + off, sl, dko, wave, l4, t.nv - t.t0);
-    issue_rows<NW>(vplane + off, sl + TILE_BYTES, dko, wave, l4, t.nv - t.t0);
+    return next_stream_tile<BLK, NW>(
+        cursor, walk, nsel, wave, l4, lane,
+        [&](int64_t key0) {
+          issue_rows<NW>(kplane + key0 * ROWB, sl, dko, wave, l4, KT);
+          issue_rows<NW>(vplane + key0 * ROWB, sl + TILE_BYTES, dko, wave, l4, KT);
+        },
+        [&](int64_t key0, int rows, const uint32_t (&ex)[8 / NW]) {
+          issue_split_rows<NW>(kplane + key0 * ROWB, sl, dko, ex, rows, wave, l4);
+          issue_split_rows<NW>(vplane + key0 * ROWB, sl + TILE_BYTES, dko, ex, rows, wave,
+                               l4);
+        });
   };
 
-  Tile cur = cursor.at(0, lane);
-  issue(cur, 0);
+  int cur_rows = issue(0);
   auto step = [&](auto stg_c) -> bool {
     constexpr int STG = decltype(stg_c)::value;
     wait_vm_all();
     __syncthreads();
-    const Tile nxt = cursor.next(cur, lane);
-    const bool has_next = nxt.e < nsel;
-    if (has_next) issue(nxt, STG ^ 1);
-    const int lim = cur.nv - cur.t0 - 4 * g;  // valid keys of this lane's group
+    const bool has_next = walk.e < nsel;
+    const int nxt_rows = has_next ? issue(STG ^ 1) : 0;
+    const int lim = cur_rows - 4 * g;  // valid keys of this lane's group
     const char* kt = smem + STG * BSTAGE;
     const char* vt = kt + TILE_BYTES;
 
@@ -349,7 +359,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
                                                                acc[dt][qt], 0, 0, 0);
     }
     if (!has_next) return true;
-    cur = nxt;
+    cur_rows = nxt_rows;
     return false;
   };
   while (true) {

@@ -138,6 +138,62 @@ struct ListCursor {
   }
 };
 
+// Position in the stream of a unit's valid keys (each selected block's
+// valid keys, blocks in list order): entry e of the list, key o of that
+// entry's block.
+struct Walk {
+  int e, o;
+};
+
+// Cuts the 32-row tile that starts at stream position w (w.e < nsel),
+// moves w past it and returns its row count (1..32).  When all 32 rows lie
+// in one block, row rr holds key key0 + rr and full(key0) issues the loads.
+// Otherwise rows [0, rows) hold the next `rows` keys of the stream, which
+// may come from several blocks: a run of rows that starts at tile row r0 in
+// block kb holds keys kb*BLK + rr - r0, so a lane whose row rr (rows
+// 4j .. 4j+3 of slice i, j = wave + i*NW) falls in that run sits
+// ex[i] = (kb*BLK - r0 - key0) rows past key0 + rr (>= 0: keys ascend along
+// the stream); split(key0, rows, ex) issues the loads.
+template <int BLK, int NW, class Full, class Split>
+__device__ __forceinline__ int next_stream_tile(ListCursor& cursor, Walk& w, int nsel,
+                                                int wave, int l4, int lane, Full&& full,
+                                                Split&& split) {
+  const Tile t = cursor.at(w.e, lane);
+  const int avail = t.nv - w.o;
+  const int64_t key0 = (int64_t)t.kb * BLK + w.o;
+  if (avail >= KT) {
+    w.o += KT;
+    if (w.o >= t.nv) {
+      ++w.e;
+      w.o = 0;
+    }
+    full(key0);
+    return KT;
+  }
+  int row = avail;
+  ++w.e;
+  w.o = 0;
+  uint32_t ex[8 / NW];
+#pragma unroll
+  for (int i = 0; i < 8 / NW; ++i) ex[i] = 0u;
+  while (row < KT && w.e < nsel) {
+    const Tile u = cursor.at(w.e, lane);
+    const int take = min(u.nv, KT - row);
+    const uint32_t d = (uint32_t)((int64_t)u.kb * BLK - row - key0) << 8;
+#pragma unroll
+    for (int i = 0; i < 8 / NW; ++i)
+      ex[i] = l4 >= row - 4 * (wave + i * NW) ? d : ex[i];
+    row += take;
+    if (take == u.nv) {
+      ++w.e;
+    } else {
+      w.o = take;
+    }
+  }
+  split(key0, row, ex);
+  return row;
+}
+
 // One direct global->LDS load of 16 B per lane (global_load_lds_dwordx4,
 // SGPR base + 32-bit VGPR offset): lane l's 16 bytes land at LDS address
 // lds_base + 16*l.  Issued as inline assembly so that the compiler does not
@@ -195,6 +251,21 @@ __device__ __forceinline__ void issue_rows(const char* g, uint32_t dst,
       const int j = wave + i * NW;
       dma16u(g, 4 * j + l4 < nv ? off[i] : (off[i] & 0xFFu), dst + (uint32_t)j * 1024u);
     }
+  }
+}
+
+// issue_rows for a tile of the key stream that spans blocks or is partial
+// (see next_stream_tile): g is key0's row; lanes of rows past the count
+// re-read row 0's chunk.
+template <int NW>
+__device__ __forceinline__ void issue_split_rows(const char* g, uint32_t dst,
+                                                 const uint32_t (&off)[8 / NW],
+                                                 const uint32_t (&ex)[8 / NW], int rows,
+                                                 int wave, int l4) {
+#pragma unroll
+  for (int i = 0; i < 8 / NW; ++i) {
+    const int j = wave + i * NW;
+    dma16u(g, 4 * j + l4 < rows ? off[i] + ex[i] : (off[i] & 0xFFu), dst + (uint32_t)j * 1024u);
   }
 }
 

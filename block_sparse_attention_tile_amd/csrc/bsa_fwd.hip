@@ -163,12 +163,6 @@ __device__ __forceinline__ void store_tile_fp8(const Fp8Staging<NT>& st,
 // when it holds no valid key).
 enum TileKind { FULL = 0, PART = 1 };
 
-// Position in the stream of a unit's valid keys: entry e of the selected
-// list, key o of that entry's block.
-struct Walk {
-  int e, o;
-};
-
 // Accumulator state of one wave: O^T tiles, per-row reference m (log2
 // units, identical in the four lanes of a row) and per-lane partial sums l.
 struct Acc {
@@ -467,69 +461,40 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   // bf16 K/V without scales: the valid keys of the selected blocks, in
   // list order, form one stream that is cut into 32-row tiles, so a tile
   // may span several blocks and only the unit's last tile is partial.
-  // Starts the loads of the tile that begins at stream position w (entry
-  // w.e, key w.o of that block) into stage `stg`, moves w past it and
-  // returns the tile's row count (1..32).  A tile inside one block loads
-  // like a block tile; a tile that spans blocks adds, per lane, the offset
-  // of the run of rows its row falls in.  Rows past the count re-read row
-  // 0's chunk.
+  // Starts the loads of the tile that begins at stream position w into
+  // stage `stg`, moves w past it and returns the tile's row count (1..32).
+  // A tile inside one block loads like a block tile; a tile that spans
+  // blocks adds, per lane, the offset of the run of rows its row falls in.
+  // Rows past the count re-read row 0's chunk.
   auto issue_stream = [&](Walk& w, int stg) -> int {
-    const Tile t = cursor.at(w.e, lane);
-    const int avail = t.nv - w.o;
-    const int64_t key0 = (int64_t)t.kb * BLK + w.o;  // key of row 0
-    const char* kg = kplane + key0 * ROWB;
-    const char* vg = vplane + key0 * ROWB;
     const uint32_t sl = smem_lds + stg * STAGE_BYTES;
-    if (avail >= KT) {
-      // the whole tile lies in one block
-      w.o += KT;
-      if (w.o >= t.nv) {
-        ++w.e;
-        w.o = 0;
-      }
+    return next_stream_tile<BLK, NW>(
+        cursor, w, nsel, wave, l4, lane,
+        [&](int64_t key0) {
+          const char* kg = kplane + key0 * ROWB;
+          const char* vg = vplane + key0 * ROWB;
 #pragma unroll
-      for (int i = 0; i < 8 / NW; ++i) {
-        const uint32_t j = (uint32_t)(wave + i * NW);
-        const int xb = (i / KP) * KP * NW * 1024;  // slice bytes past dko
-        dma16(kg + xb, dko[i % KP], sl + j * 1024u);
-        dma16(vg + xb, dvo[i % KP], sl + TILE_BYTES + j * 1024u);
-      }
-      return KT;
-    }
-    // Rows [0, avail) come from this block; later runs of rows from the
-    // following entries.  Row rr of a run that starts at row r0 in block kb
-    // holds key kb*BLK + rr - r0, i.e. it lies (kb*BLK - r0 - key0) rows
-    // past where a single-block tile would put it (>= 0: keys ascend).
-    int row = avail;
-    ++w.e;
-    w.o = 0;
-    uint32_t ex[8 / NW];
+          for (int i = 0; i < 8 / NW; ++i) {
+            const uint32_t j = (uint32_t)(wave + i * NW);
+            const int xb = (i / KP) * KP * NW * 1024;  // slice bytes past dko
+            dma16(kg + xb, dko[i % KP], sl + j * 1024u);
+            dma16(vg + xb, dvo[i % KP], sl + TILE_BYTES + j * 1024u);
+          }
+        },
+        [&](int64_t key0, int rows, const uint32_t (&ex)[8 / NW]) {
+          const char* kg = kplane + key0 * ROWB;
+          const char* vg = vplane + key0 * ROWB;
 #pragma unroll
-    for (int i = 0; i < 8 / NW; ++i) ex[i] = 0u;
-    while (row < KT && w.e < nsel) {
-      const Tile u = cursor.at(w.e, lane);
-      const int take = min(u.nv, KT - row);
-      const uint32_t d = (uint32_t)((int64_t)u.kb * BLK - row - key0) << 8;
-#pragma unroll
-      for (int i = 0; i < 8 / NW; ++i)
-        ex[i] = l4 >= row - 4 * (wave + i * NW) ? d : ex[i];
-      row += take;
-      if (take == u.nv) {
-        ++w.e;
-      } else {
-        w.o = take;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8 / NW; ++i) {
-      const int j = wave + i * NW;
-      const bool ok = 4 * j + l4 < row;
-      const uint32_t xb = (uint32_t)((i / KP) * KP * NW * 1024);
-      const uint32_t ko = dko[i % KP], vo = dvo[i % KP];
-      dma16(kg, ok ? ko + xb + ex[i] : (ko & 0xFFu), sl + (uint32_t)j * 1024u);
-      dma16(vg, ok ? vo + xb + ex[i] : (vo & 0xFFu), sl + TILE_BYTES + (uint32_t)j * 1024u);
-    }
-    return row;
+          for (int i = 0; i < 8 / NW; ++i) {
+            const int j = wave + i * NW;
+            const bool ok = 4 * j + l4 < rows;
+            const uint32_t xb = (uint32_t)((i / KP) * KP * NW * 1024);
+            const uint32_t ko = dko[i % KP], vo = dvo[i % KP];
+            dma16(kg, ok ? ko + xb + ex[i] : (ko & 0xFFu), sl + (uint32_t)j * 1024u);
+            dma16(vg, ok ? vo + xb + ex[i] : (vo & 0xFFu),
+                  sl + TILE_BYTES + (uint32_t)j * 1024u);
+          }
+        });
   };
 
   // One pass of the K loop over every selected tile.
