@@ -381,7 +381,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // 4. dK, dV: one workgroup per (b, K/V head, key block), BLK/16 waves of 16
-// keys each.  The keys' K and V rows are B operands in registers (rows past
+// keys each (blocks with at most BLK/2 valid keys: two waves per 16 keys,
+// each on half the query rows).  The keys' K and V rows are B operands in registers (rows past
 // the block's valid count zeroed).  For every attending query unit, in
 // 64-row query steps (Q and dO as two 32-row tiles each in LDS with the row
 // swizzle, the rows' LSE and delta beside them):
@@ -422,7 +423,7 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
   const int b = bkv / p.Hk;
   const int64_t kvplane = (int64_t)bkv * p.Sk * HD;
   const int nv = block_valid<BLK>(p.vbs, kb);
-  const int key = wave * 16 + r16;  // this lane's key within the block
+  const int key = wave * 16 + r16;  // this lane's key within the block (output)
 
   const int8_t* mrow = p.k2q + (int64_t)u * gq;
   for (int i = tid; i < gq; i += NT) map[i] = (uint8_t)mrow[i];
@@ -447,15 +448,24 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) dka[dt] = dva[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // A block with at most BLK/2 valid keys would leave the second half of
+  // the waves on keys past the count.  Instead those waves take the first
+  // half's keys and the second 32 rows of every 64-row query step (the
+  // first half keeps rows 0..31); their partial dK, dV are added to the
+  // first half's through LDS at the end.  Fixed split, so deterministic.
+  const bool halves = 2 * nv <= BLK;
+  const int rep = halves && wave >= NW / 2 ? 1 : 0;       // row half (halves)
+  const int ckey = (halves ? wave % (NW / 2) : wave) * 16 + r16;  // key computed
+
   if (nsteps > 0) {
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
     // K^T / V^T B operands: column key, rows d = kk*32 + g*8 ..
     bf16x8 kreg[4], vreg[4];
     {
-      const int64_t r = kvplane + ((int64_t)kb * BLK + key) * HD;
+      const int64_t r = kvplane + ((int64_t)kb * BLK + ckey) * HD;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        if (key < nv) {
+        if (ckey < nv) {
           kreg[kk] = *(const bf16x8*)(p.k + r + kk * 32 + g * 8);
           vreg[kk] = *(const bf16x8*)(p.v + r + kk * 32 + g * 8);
         } else {
@@ -497,73 +507,108 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
       }
     };
 
-    issue(step_rows(0), 0);
-    int t = 0;
-    auto step = [&](auto stg_c) -> bool {
-      constexpr int STG = decltype(stg_c)::value;
-      wait_vm_all();
-      __syncthreads();
-      const bool has_next = t + 1 < nsteps;
-      if (has_next) issue(step_rows(t + 1), STG ^ 1);
-      const char* qtile = smem + STG * DSTAGE;
-      const char* dtile = qtile + 2 * TILE_BYTES;
-      // S and dP for four 16-row query sub-tiles qs (rows qs*16 ..)
-      f32x4 s[4], dp[4];
+    // NHF: 32-row halves of each step this wave computes (2, or 1 with
+    // `halves`: half hf0 = rep)
+    auto run = [&](auto nhf_c) {
+      constexpr int NHF = decltype(nhf_c)::value;
+      const int hf0 = NHF == 2 ? 0 : rep;
+      issue(step_rows(0), 0);
+      int t = 0;
+      auto step = [&](auto stg_c) -> bool {
+        constexpr int STG = decltype(stg_c)::value;
+        wait_vm_all();
+        __syncthreads();
+        const bool has_next = t + 1 < nsteps;
+        if (has_next) issue(step_rows(t + 1), STG ^ 1);
+        const char* stage = smem + STG * DSTAGE;
+        const char* qtile = stage + hf0 * TILE_BYTES;          // Q rows of half hf0
+        const char* dtile = stage + (2 + hf0) * TILE_BYTES;    // dO rows of half hf0
+        const char* ltab = stage + LSE_OFF + hf0 * 128;
+        const char* dtab = stage + DLT_OFF + hf0 * 128;
+        // S and dP for the 16-row query sub-tiles qs (rows qs*16 .. of the
+        // wave's halves)
+        f32x4 s[2 * NHF], dp[2 * NHF];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int qs = 0; qs < 4; ++qs) {
-          const uint32_t a =
-              (abase ^ (kk << 6)) + (qs & 1) * 16 * ROWB + (qs >> 1) * TILE_BYTES;
-          const bf16x8 qop = *(const bf16x8*)(qtile + a);
-          const bf16x8 dop = *(const bf16x8*)(dtile + a);
-          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          s[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop, kreg[kk],
-                                                          kk == 0 ? z : s[qs], 0, 0, 0);
-          dp[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dop, vreg[kk],
-                                                           kk == 0 ? z : dp[qs], 0, 0, 0);
+          for (int qs = 0; qs < 2 * NHF; ++qs) {
+            const uint32_t a =
+                (abase ^ (kk << 6)) + (qs & 1) * 16 * ROWB + (qs >> 1) * TILE_BYTES;
+            const bf16x8 qop = *(const bf16x8*)(qtile + a);
+            const bf16x8 dop = *(const bf16x8*)(dtile + a);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            s[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop, kreg[kk],
+                                                            kk == 0 ? z : s[qs], 0, 0, 0);
+            dp[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dop, vreg[kk],
+                                                             kk == 0 ? z : dp[qs], 0, 0, 0);
+          }
+        // P and dS as B operands, one pair per 32-row half
+        bf16x8 pop[NHF], dsop[NHF];
+#pragma unroll
+        for (int hf = 0; hf < NHF; ++hf) {
+          const f32x4 l0 = *(const f32x4*)(ltab + (hf * 32 + g * 4) * 4);
+          const f32x4 l1 = *(const f32x4*)(ltab + (hf * 32 + 16 + g * 4) * 4);
+          const f32x4 d0 = *(const f32x4*)(dtab + (hf * 32 + g * 4) * 4);
+          const f32x4 d1 = *(const f32x4*)(dtab + (hf * 32 + 16 + g * 4) * 4);
+          float pv[8], dsv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int qs = hf * 2 + (e >> 2), j = e & 3;
+            const float l = (e >> 2) ? l1[j] : l0[j];
+            const float d = (e >> 2) ? d1[j] : d0[j];
+            const float pr = ckey < nv ? __builtin_amdgcn_exp2f(
+                                             __builtin_fmaf(s[qs][j], p.c, -l))
+                                       : 0.f;
+            pv[e] = pr;
+            dsv[e] = pr * (dp[qs][j] - d);
+          }
+          pop[hf] = pack8(pv);
+          dsop[hf] = pack8(dsv);
         }
-      // P and dS as B operands, one pair per 32-row half
-      bf16x8 pop[2], dsop[2];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const f32x4 l0 = *(const f32x4*)(qtile + LSE_OFF + (hf * 32 + g * 4) * 4);
-        const f32x4 l1 = *(const f32x4*)(qtile + LSE_OFF + (hf * 32 + 16 + g * 4) * 4);
-        const f32x4 d0 = *(const f32x4*)(qtile + DLT_OFF + (hf * 32 + g * 4) * 4);
-        const f32x4 d1 = *(const f32x4*)(qtile + DLT_OFF + (hf * 32 + 16 + g * 4) * 4);
-        float pv[8], dsv[8];
+        for (int dt = 0; dt < 8; ++dt) {
+          const uint32_t a = trb ^ (uint32_t)(dt << 5);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int qs = hf * 2 + (e >> 2), j = e & 3;
-          const float l = (e >> 2) ? l1[j] : l0[j];
-          const float d = (e >> 2) ? d1[j] : d0[j];
-          const float pr = key < nv ? __builtin_amdgcn_exp2f(
-                                          __builtin_fmaf(s[qs][j], p.c, -l))
-                                    : 0.f;
-          pv[e] = pr;
-          dsv[e] = pr * (dp[qs][j] - d);
+          for (int hf = 0; hf < NHF; ++hf) {
+            dva[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                tr_read(dtile + hf * TILE_BYTES, a), pop[hf], dva[dt], 0, 0, 0);
+            dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                tr_read(qtile + hf * TILE_BYTES, a), dsop[hf], dka[dt], 0, 0, 0);
+          }
         }
-        pop[hf] = pack8(pv);
-        dsop[hf] = pack8(dsv);
+        if (!has_next) return true;
+        ++t;
+        return false;
+      };
+      while (true) {
+        if (step(IntC<0>{})) break;
+        if (step(IntC<1>{})) break;
       }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const uint32_t a = trb ^ (uint32_t)(dt << 5);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          dva[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              tr_read(dtile + hf * TILE_BYTES, a), pop[hf], dva[dt], 0, 0, 0);
-          dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              tr_read(qtile + hf * TILE_BYTES, a), dsop[hf], dka[dt], 0, 0, 0);
-        }
-      }
-      if (!has_next) return true;
-      ++t;
-      return false;
     };
-    while (true) {
-      if (step(IntC<0>{})) break;
-      if (step(IntC<1>{})) break;
+    if (halves) {
+      run(IntC<1>{});
+      // second-half waves hand their partial sums to the first half
+      __syncthreads();  // every wave is done with the stages
+      f32x4* red = (f32x4*)smem;  // [key group][16][64 lanes]
+      const int kg = wave % (NW / 2);
+      if (rep == 1) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          red[(kg * 16 + dt) * 64 + lane] = dka[dt];
+          red[(kg * 16 + 8 + dt) * 64 + lane] = dva[dt];
+          dka[dt] = dva[dt] = f32x4{0.f, 0.f, 0.f, 0.f};  // own keys: past the count
+        }
+      }
+      __syncthreads();
+      if (rep == 0) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          dka[dt] += red[(kg * 16 + dt) * 64 + lane];
+          dva[dt] += red[(kg * 16 + 8 + dt) * 64 + lane];
+        }
+      }
+    } else {
+      run(IntC<2>{});
     }
   }
 

@@ -93,6 +93,16 @@ CASES = [
     ("lut64_one_block", dict(seed=209, B=1, H=2, S=64, block=64, density=1.0,
                              vbs_mode="partial")),
     ("lut64_dense", dict(seed=210, B=1, H=2, S=512, block=64, density=1.0)),
+    # valid counts around 16-row edges (blocks with at most half their keys
+    # valid split their query rows over two waves) and runs of 1-4-key
+    # blocks (dq tiles spanning many blocks)
+    ("lut64_vbs_edges", dict(seed=211, B=1, H=2, S=1024, block=64,
+                             density=0.6, vbs_mode="edges")),
+    ("lut128_vbs_edges", dict(seed=212, B=1, H=2, S=2048, block=128,
+                              count_mode="uniform", vbs_mode="edges")),
+    ("gqa_bitmap64_vbs_tiny", dict(seed=213, B=1, H=4, Hk=2, S=512, Sk=2048,
+                                   block=64, form="bitmap", density=0.8,
+                                   vbs_mode="tiny")),
 ]
 
 
