@@ -353,6 +353,9 @@ def main() -> int:
                     help="inference route: the forward pass without the LSE "
                          "output")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--flush-cache", action="store_true",
+                    help="forward only: overwrite 512 MB before every timed "
+                         "launch and time each launch alone (cold L2 and MALL)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (the "
                          "reference kernel for scaling HBM byte counters)")
@@ -419,13 +422,29 @@ def main() -> int:
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        launch(w, d, out, lse)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    if args.flush_cache:
+        # cold caches: a 512 MB write (twice the MALL) before every launch,
+        # outside the timed interval of that launch
+        scrub = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        pairs_ev = [(torch.cuda.Event(enable_timing=True),
+                     torch.cuda.Event(enable_timing=True))
+                    for _ in range(args.steps)]
+        for i in range(args.steps):
+            scrub.fill_(float(i))
+            pairs_ev[i][0].record(stream)
+            launch(w, d, out, lse)
+            pairs_ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in pairs_ev) / args.steps
+        del scrub
+    else:
+        ev0.record(stream)
+        for _ in range(args.steps):
+            launch(w, d, out, lse)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.steps
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
     progress(f"timed {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)")
 
     tflops = flop / (ms * 1e-3) / 1e12
@@ -448,6 +467,7 @@ def main() -> int:
             "workload": w.name,
             "B": w.B, "H": w.H, "S": w.S, "D": w.D, "block": w.block,
             "form": w.form, "need_lse": not args.no_lse,
+            "caches": "flushed before each launch" if args.flush_cache else "warm",
             "attended_pairs": pairs,
             "effective_flop_per_step": flop,
             "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
