@@ -103,6 +103,8 @@ CASES = [
     ("gqa_bitmap64_vbs_tiny", dict(seed=213, B=1, H=4, Hk=2, S=512, Sk=2048,
                                    block=64, form="bitmap", density=0.8,
                                    vbs_mode="tiny")),
+    ("lut64_many_tiny", dict(seed=214, B=1, H=1, S=1024, Sk=16384, block=64,
+                             density=0.9, vbs_mode="tiny")),
 ]
 
 

@@ -82,6 +82,10 @@ SMALL = [
                                 form="bitmap", density=0.7, vbs_mode="tiny")),
     ("gqa_rect64_vbs_edges", dict(seed=128, B=2, H=4, Hk=2, S=512, Sk=2048,
                                   block=64, density=0.5, vbs_mode="edges")),
+    # ~230 selected blocks of 1-4 keys: tiles span many blocks and cross
+    # the 64-entry list chunks in the middle of a tile
+    ("lut64_many_tiny", dict(seed=129, B=1, H=1, S=1024, Sk=16384, block=64,
+                             density=0.9, vbs_mode="tiny")),
 ]
 
 
