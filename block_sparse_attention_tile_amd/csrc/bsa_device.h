@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bsa.h"
+
 namespace {
 
 constexpr int HD = 128;                 // head dimension
@@ -154,6 +156,11 @@ struct Walk {
 // 4j .. 4j+3 of slice i, j = wave + i*NW) falls in that run sits
 // ex[i] = (kb*BLK - r0 - key0) rows past key0 + rr (>= 0: keys ascend along
 // the stream); split(key0, rows, ex) issues the loads.
+// Lane offsets are 32-bit byte offsets from key0's row; they stay below
+// one head's K/V plane, at most BSA_MAX_KEY_BLOCKS blocks of 128 keys.
+static_assert((int64_t)BSA_MAX_KEY_BLOCKS * 128 * ROWB < ((int64_t)1 << 32),
+              "stream-tile lane offsets must fit 32 bits");
+
 template <int BLK, int NW, class Full, class Split>
 __device__ __forceinline__ int next_stream_tile(ListCursor& cursor, Walk& w, int nsel,
                                                 int wave, int l4, int lane, Full&& full,

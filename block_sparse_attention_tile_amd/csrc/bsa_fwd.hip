@@ -406,7 +406,7 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   // Per-lane constant byte offsets (the XOR swizzles make every address a
   // per-lane base XORed with a constant): K operand kbase ^ (kk << 6),
   // keys 16..31 at +16 rows; V^T transposing reads vbase ^ (dt << 5), rows
-  // 16..31 at +16 rows; DMA offsets within a 4-row slice dmak / dmav.
+  // 16..31 at +16 rows; DMA offsets within a 4-row slice dko / dvo.
   const uint32_t kbase = (uint32_t)(r16 * ROWB + ((g ^ r16) << 4));
   const uint32_t vbase = (uint32_t)(TILE_BYTES + (lane >> 2) * ROWB +
                                     ((2 * ((lane >> 2) & 7) + ((lane & 3) >> 1)) << 4) +
@@ -440,7 +440,9 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   [[maybe_unused]] Fp8Staging<NT> st;
   [[maybe_unused]] float ksc_cur = 1.f, vsc_cur = 1.f, ksc_nxt = 1.f, vsc_nxt = 1.f;
 
-  // Starts the loads of tile t into stage `stg` (bf16: DMA; fp8: registers).
+  // Per-block tiles (K/V with per-block scales): starts the loads of tile t
+  // into stage `stg` (scaled bf16: DMA; fp8: registers) and fetches the
+  // block's scales.
   auto issue = [&](const Tile& t, int stg) {
     const int64_t key0 = (int64_t)t.kb * BLK + t.t0;
     const int nvt = t.nv - t.t0;
