@@ -1,15 +1,19 @@
 """Thin Python binding of the C ABI in ``include/bsa.h``.
 
 Argument marshalling only: every step of the forward pass runs in the HIP
-kernels of ``libbsa.so``.  PyTorch supplies device memory and the stream
-(``torch.cuda.current_stream()``); outputs are allocated here with
+kernels of ``libbsa.so``.  PyTorch supplies device memory and the stream:
+``torch.cuda.current_stream()``, or the stream given as the keyword
+``stream=`` (every entry point takes it; the whole call then runs under
+``torch.cuda.stream(stream)``); outputs are allocated here with
 ``torch.empty`` when not passed in.  Integer metadata is cast to contiguous
 int32 as the FastVideo wrapper does (``block_sparse_attn_sm100a``).
 """
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 from typing import Optional, Tuple
 
 import torch
@@ -44,6 +48,23 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _on_stream(fn):
+    """Runs the whole call under ``torch.cuda.stream(stream)`` when a stream
+    is given, so the temporaries it makes (int32 and contiguous copies,
+    dequantised K/V, the workspace) are produced on, ordered before and
+    owned by the stream the kernels are launched on."""
+    @functools.wraps(fn)
+    def wrapped(*args, stream: Optional[torch.cuda.Stream] = None, **kw):
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            return fn(*args, **kw)
+    return wrapped
+
+
+def _cur_stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
 def _kv_dtype(k: torch.Tensor, v: torch.Tensor) -> int:
     if k.dtype != v.dtype:
         raise TypeError("k and v must have the same dtype")
@@ -56,8 +77,8 @@ def _kv_dtype(k: torch.Tensor, v: torch.Tensor) -> int:
     raise TypeError(f"unsupported k/v dtype {k.dtype}")
 
 
-def bsa_codebook_dequant(codes: torch.Tensor, codebook: torch.Tensor,
-                         stream: Optional[torch.cuda.Stream] = None
+@_on_stream
+def bsa_codebook_dequant(codes: torch.Tensor, codebook: torch.Tensor
                          ) -> torch.Tensor:
     """bf16 codebook values of codebook-coded K or V: int8 codes
     ``[..., D]`` (256-entry codebook) or uint8 bytes of packed int4 codes
@@ -75,9 +96,8 @@ def bsa_codebook_dequant(codes: torch.Tensor, codebook: torch.Tensor,
         raise ValueError("codebook must have 256 (i8) or 16 (i4) entries")
     out = torch.empty(shape, dtype=torch.bfloat16, device=codes.device)
     n = out.numel()
-    st = (stream or torch.cuda.current_stream(codes.device)).cuda_stream
     rc = _lib.load().bsa_codebook_dequant(_ptr(codes), kind, _ptr(cb), _ptr(out),
-                                          n, ctypes.c_void_p(st))
+                                          n, _cur_stream(codes))
     if rc != BSA_OK:
         raise BsaError(rc)
     return out
@@ -88,7 +108,7 @@ def _i32(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
 
 
 def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block,
-             k_codebook=None, v_codebook=None, stream=None):
+             k_codebook=None, v_codebook=None):
     if q.dtype != torch.bfloat16 or q.dim() != 4:
         raise TypeError("q must be a 4-D bf16 [B, H, S, D] tensor")
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
@@ -97,8 +117,8 @@ def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block,
             raise ValueError("codebook-coded k/v need k_codebook and v_codebook")
         if k.dtype != v.dtype:
             raise TypeError("k and v must have the same dtype")
-        k = bsa_codebook_dequant(k, k_codebook, stream)
-        v = bsa_codebook_dequant(v, v_codebook, stream)
+        k = bsa_codebook_dequant(k, k_codebook)
+        v = bsa_codebook_dequant(v, v_codebook)
         kvd = BSA_KV_BF16_SCALED
     else:
         kvd = None
@@ -125,6 +145,7 @@ def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block,
     return q, k, v, kvd, k_scale, v_scale, out, lse
 
 
+@_on_stream
 def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 q2k_idx: torch.Tensor, q2k_num: torch.Tensor,
                 variable_block_sizes: Optional[torch.Tensor] = None, *,
@@ -134,7 +155,6 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 meta_strides: Optional[Tuple[int, int]] = None,
                 need_lse: bool = True, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None,
-                stream: Optional[torch.cuda.Stream] = None,
                 k_codebook: Optional[torch.Tensor] = None,
                 v_codebook: Optional[torch.Tensor] = None):
     """VSA form.  Returns ``(out, lse)`` (``lse`` is None if not needed).
@@ -143,7 +163,7 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     of (b, h, qb) is ``b*sb + h*sh + qb``; default one row per unit."""
     q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
                                               lse, need_lse, block, k_codebook,
-                                              v_codebook, stream)
+                                              v_codebook)
     B, H, S, D = q.shape
     Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
@@ -153,17 +173,17 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     sb, sh = meta_strides if meta_strides is not None else (H * NQ, NQ)
     if sm_scale is None:
         sm_scale = 1.0 / (D ** 0.5)
-    st = (stream or torch.cuda.current_stream(q.device)).cuda_stream
     rc = _lib.load().bsa_fwd_lut(
         _ptr(q), _ptr(k), _ptr(v), kvd, _ptr(ks), _ptr(vs), _ptr(idx),
         _ptr(num), int(idx.shape[-1]), int(sb), int(sh), _ptr(vbs),
         float(sm_scale), _ptr(out), _ptr(lse), B, H, Hk, S, Sk, D, int(block),
-        ctypes.c_void_p(st))
+        _cur_stream(q))
     if rc != BSA_OK:
         raise BsaError(rc)
     return out, lse
 
 
+@_on_stream
 def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    mask: torch.Tensor,
                    variable_block_sizes: Optional[torch.Tensor] = None, *,
@@ -173,7 +193,6 @@ def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    mask_strides: Optional[Tuple[int, int]] = None,
                    need_lse: bool = True, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None,
-                   stream: Optional[torch.cuda.Stream] = None,
                    k_codebook: Optional[torch.Tensor] = None,
                    v_codebook: Optional[torch.Tensor] = None):
     """Jenga form.  ``mask`` is an int8 (or bool) tensor of rows of S/block
@@ -182,7 +201,7 @@ def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     form."""
     q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
                                               lse, need_lse, block, k_codebook,
-                                              v_codebook, stream)
+                                              v_codebook)
     B, H, S, D = q.shape
     Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
@@ -191,18 +210,17 @@ def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     sb, sh = mask_strides if mask_strides is not None else (H * NQ, NQ)
     if sm_scale is None:
         sm_scale = 1.0 / (D ** 0.5)
-    st = (stream or torch.cuda.current_stream(q.device)).cuda_stream
     rc = _lib.load().bsa_fwd_bitmap(
         _ptr(q), _ptr(k), _ptr(v), kvd, _ptr(ks), _ptr(vs), _ptr(m),
         int(sb), int(sh), _ptr(vbs), float(sm_scale), _ptr(out), _ptr(lse),
-        B, H, Hk, S, Sk, D, int(block), ctypes.c_void_p(st))
+        B, H, Hk, S, Sk, D, int(block), _cur_stream(q))
     if rc != BSA_OK:
         raise BsaError(rc)
     return out, lse
 
 
-def bsa_mask_to_lut(mask: torch.Tensor,
-                    stream: Optional[torch.cuda.Stream] = None):
+@_on_stream
+def bsa_mask_to_lut(mask: torch.Tensor):
     """Compacts a block map ``mask [..., NK]`` (nonzero = selected) on the
     GPU into ``(q2k_idx [..., NK] int32, q2k_num [...] int32)``: ascending
     selected key blocks, then -1 padding."""
@@ -213,14 +231,14 @@ def bsa_mask_to_lut(mask: torch.Tensor,
     rows = m.numel() // nk if nk > 0 else 0
     idx = torch.empty(m.shape, dtype=torch.int32, device=m.device)
     num = torch.empty(m.shape[:-1], dtype=torch.int32, device=m.device)
-    st = (stream or torch.cuda.current_stream(m.device)).cuda_stream
     rc = _lib.load().bsa_mask_to_lut(_ptr(m), int(rows), nk, _ptr(idx),
-                                     _ptr(num), ctypes.c_void_p(st))
+                                     _ptr(num), _cur_stream(m))
     if rc != BSA_OK:
         raise BsaError(rc)
     return idx, num
 
 
+@_on_stream
 def bsa_fwd_from_mask(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                       mask: torch.Tensor,
                       variable_block_sizes: Optional[torch.Tensor] = None, *,
@@ -229,13 +247,14 @@ def bsa_fwd_from_mask(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """The from-mask route: compaction on the GPU, then the LUT form.  Gives
     the same result as ``bsa_fwd_bitmap`` on the same mask; also returns the
     look-up table for reuse.  Returns ``(out, lse, q2k_idx, q2k_num)``."""
-    idx, num = bsa_mask_to_lut(mask, stream=kw.get("stream"))
+    idx, num = bsa_mask_to_lut(mask)
     out, lse = bsa_fwd_lut(q, k, v, idx.reshape(-1, idx.shape[-1]),
                            num.reshape(-1), variable_block_sizes, block=block,
                            meta_strides=mask_strides, **kw)
     return out, lse, idx, num
 
 
+@_on_stream
 def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, *,
             block: int, q2k_idx: Optional[torch.Tensor] = None,
@@ -244,8 +263,7 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             variable_block_sizes: Optional[torch.Tensor] = None,
             sm_scale: Optional[float] = None,
             meta_strides: Optional[Tuple[int, int]] = None,
-            workspace: Optional[torch.Tensor] = None,
-            stream: Optional[torch.cuda.Stream] = None):
+            workspace: Optional[torch.Tensor] = None):
     """Gradients ``(dq, dk, dv)`` of ``sum(out * dout)`` for the forward pass
     that produced ``out`` and ``lse`` from the same inputs (bf16 K/V).  LUT
     form if ``q2k_idx`` is given, else bitmap form (``mask``);
@@ -272,7 +290,7 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     sb, sh = meta_strides if meta_strides is not None else (H * NQ, NQ)
     if sm_scale is None:
         sm_scale = 1.0 / (D ** 0.5)
-    st = ctypes.c_void_p((stream or torch.cuda.current_stream(q.device)).cuda_stream)
+    st = _cur_stream(q)
     common_tail = (float(sm_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                    int(workspace.numel()), B, H, Hk, S, Sk, D, int(block), st)
     if q2k_idx is not None:
