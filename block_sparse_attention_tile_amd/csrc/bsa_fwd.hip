@@ -9,11 +9,12 @@
 //      "sparse_attention.py" keeps separate query and KV head counts and
 //      query and key lengths, both supported here).
 //  A2  selected-set decode into LDS.  LUT form: the row's first
-//      clamp(num, 0, max_kv) entries are scattered into a byte bitmap
-//      (duplicate stores write the same 1, out-of-range entries are dropped),
-//      as in rocke "sparse_attention.py" `_stage_vsa_bitmap_to_lds`.  Bitmap
-//      form: the mask row is copied into the same LDS bitmap
-//      (`_stage_jenga_mask_to_lds` on the same page).  One wave then
+//      clamp(num, 0, max_kv) entries are scattered into a byte map
+//      (duplicate stores write the same value, out-of-range entries are
+//      dropped), as in rocke "sparse_attention.py" `_stage_vsa_bitmap_to_lds`;
+//      a selected block's byte holds its valid key count.  Bitmap form: the
+//      mask row is copied into the same LDS map (`_stage_jenga_mask_to_lds`
+//      on the same page).  One wave then
 //      compacts the bitmap into an ascending list of selected key blocks that
 //      have at least one valid key (ballot + popcount), so the K loop runs
 //      over selected tiles only and never touches an unselected one (the
@@ -21,7 +22,8 @@
 //      -inf).  Ascending order makes the result independent of LUT order,
 //      padding and repetitions.
 //  A3  Q: each wave keeps its 32 query rows in VGPRs as MFMA operands for
-//      the whole K loop (loaded once with 128-bit loads).
+//      the whole K loop (loaded once with 128-bit loads, issued before the
+//      decode so that they arrive during it).
 //  A4  K/V gather in 32-key tiles, only rows below a block's valid count
 //      are read (direct global->LDS 128-bit loads).  bf16 K/V: the valid
 //      keys of the selected blocks, in list order, are cut into tiles as
@@ -29,7 +31,8 @@
 //      unit's last tile is partial (with valid counts below the block size
 //      this removes the padded tail of every block).  With per-block scales
 //      (fp8, scaled bf16) each tile stays inside one block.  Lanes of rows
-//      past a tile's count re-read row 0 (fp8 writes zeros there).  Tiles
+//      past a tile's count re-read row 0 (fp8 writes zeros there), so every
+//      row of every staged tile is written before it is read.  Tiles
 //      are double-buffered in LDS: the loads of tile i+1 are in flight
 //      while tile i is computed.  fp8 e4m3 K/V are widened to bf16 exactly
 //      on the way into LDS.
@@ -345,15 +348,27 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   const int64_t kvplane = kvh * p.Sk * HD;       // element offset of K/V
   const int64_t row = (int64_t)b * p.meta_sb + (int64_t)h * p.meta_sh + qb;
 
-  // Zero both stages once: rows that are never loaded must hold finite data.
-  for (int i = tid; i < NSTAGE * STAGE_BYTES / 16; i += NT)
-    *(u32x4*)(smem + i * 16) = u32x4{0, 0, 0, 0};
+  const int qrow0 = qb * BLK + wave * 32;  // first query row of this wave
+
+  // ---- A3: Q operands (B operand of S^T = K Q^T): Q[row r16][d kk*32+g*8..],
+  // loaded first so that they arrive while the selected set is decoded.
+  bf16x8 qreg[2][4];
+  {
+    const uint16_t* qg = p.q + plane + (int64_t)qrow0 * HD;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qreg[qt][kk] = *(const bf16x8*)(qg + (qt * 16 + r16) * HD + kk * 32 + g * 8);
+  }
   if (tid == 0) *s_redo = 0;
 
-  // ---- A2: selected set -> LDS bitmap
+  // ---- A2: selected set -> LDS byte map: bmp[kb] = valid keys of kb if
+  // selected, else 0 (every thread reads the valid counts of its entries)
   if constexpr (BITMAP) {
     const int8_t* mrow = p.mask + row * NK;
-    for (int i = tid; i < NK; i += NT) bmp[i] = mrow[i] != 0;
+    for (int i = tid; i < NK; i += NT)
+      bmp[i] = mrow[i] != 0 ? (uint8_t)block_valid<BLK>(p.vbs, i) : (uint8_t)0;
   } else {
     for (int i = tid; i < NK; i += NT) bmp[i] = 0;
     __syncthreads();
@@ -361,17 +376,18 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
     const int32_t* irow = p.idx + row * p.max_kv;
     for (int j = tid; j < n; j += NT) {
       const int kb = irow[j];
-      if (kb >= 0 && kb < NK) bmp[kb] = 1;  // duplicates store the same 1
+      // duplicates store the same value
+      if (kb >= 0 && kb < NK) bmp[kb] = (uint8_t)block_valid<BLK>(p.vbs, kb);
     }
   }
   __syncthreads();
-  // bitmap -> ascending list of selected blocks with >= 1 valid key
+  // byte map -> ascending list of selected blocks with >= 1 valid key
   if (wave == 0) {
     int base = 0;
     for (int c0 = 0; c0 < NK; c0 += 64) {
       const int kb = c0 + lane;
-      const int nv = kb < NK ? block_valid<BLK>(p.vbs, kb) : 0;
-      const bool f = kb < NK && bmp[kb] != 0 && nv > 0;
+      const int nv = kb < NK ? (int)bmp[kb] : 0;
+      const bool f = nv > 0;
       const uint64_t bal = __ballot(f);
       const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
       if (f) list[pos] = ((uint32_t)kb << 8) | (uint32_t)nv;
@@ -381,8 +397,6 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   }
   __syncthreads();
   const int nsel = *s_nsel;
-
-  const int qrow0 = qb * BLK + wave * 32;  // first query row of this wave
 
   if (nsel == 0) {
     // A8 for a unit with no attended key: exact zeros and the sentinel
@@ -423,17 +437,6 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
     const int j = wave + i * NW;
     dko[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ l4) ^ ((j & 3) << 2)) << 4));
     dvo[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ (2 * l4)) ^ ((j & 1) << 3)) << 4));
-  }
-
-  // ---- A3: Q operands (B operand of S^T = K Q^T): Q[row r16][d kk*32+g*8..]
-  bf16x8 qreg[2][4];
-  {
-    const uint16_t* qg = p.q + plane + (int64_t)qrow0 * HD;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        qreg[qt][kk] = *(const bf16x8*)(qg + (qt * 16 + r16) * HD + kk * 32 + g * 8);
   }
 
   ListCursor cursor{list, nsel, 0, 0u};
