@@ -155,13 +155,24 @@ __device__ __forceinline__ int compact_list(const uint8_t* map, int n,
   return base;
 }
 
-// Address of this lane's transposing read (ds_read_b64_tr_b16) of a tile
-// stored with the row swizzle c ^ (r & 15): rows lane/4 (and +16), the
-// 4-element column group (lane & 3) of 16-column group dt: base ^ (dt << 5).
+// Tiles of the backward kernels are read both row-wise (MFMA A operands: 16
+// rows x one 16-byte chunk per 16 lanes) and through the transposing read
+// (8 rows x two chunks per 32 lanes).  Chunk c of row r sits at position
+// c ^ bswz(r) with bswz(r) = (r ^ 2r) mod 16: a permutation of the 16 rows
+// (row reads hit 16 distinct positions) whose values shifted right by one
+// are distinct within each group of 8 rows (transposing reads hit 16
+// distinct positions), so both are free of bank conflicts.  (The row
+// swizzle c ^ r of the forward's K tiles costs the transposing read a
+// 2-way conflict.)
+__device__ __forceinline__ int bswz(int r) { return (r ^ (r << 1)) & 15; }
+
+// Address of this lane's transposing read (ds_read_b64_tr_b16) of a tile:
+// rows lane/4 (and +16), the 4-element column group (lane & 3) of 16-column
+// group dt: base ^ (dt << 5).
 __device__ __forceinline__ uint32_t tr_base(int lane) {
   const int row = lane >> 2;
   const int hb = (lane & 3) >> 1;
-  return (uint32_t)(row * ROWB + ((hb ^ (row & 15)) << 4) + (lane & 1) * 8);
+  return (uint32_t)(row * ROWB + ((hb ^ bswz(row)) << 4) + (lane & 1) * 8);
 }
 
 __device__ __forceinline__ bf16x8 tr_read(const char* tile, uint32_t addr) {
@@ -180,7 +191,7 @@ __device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
 // ---------------------------------------------------------------------------
 // 3. dQ: one workgroup per query unit, BLK/32 waves of 32 query rows.
 //
-// Per 32-key tile (K and V tiles in LDS, both stored with the row swizzle):
+// Per 32-key tile (K and V tiles in LDS, both stored with bswz):
 //   S^T[key][q] = K Q^T              A = K rows,   B = Q (registers)
 //   P^T = 2^(S^T c - LSE_q)          keys past the block's count -> 0
 //   dP^T[key][q] = V dO^T            A = V rows,   B = dO (registers)
@@ -274,9 +285,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < 8 / NW; ++i) {
     const int j = wave + i * NW;
-    dko[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ l4) ^ ((j & 3) << 2)) << 4));
+    dko[i] = (uint32_t)(j * 1024 + l4 * ROWB + ((pos ^ bswz(4 * j + l4)) << 4));
   }
-  const uint32_t kbase = (uint32_t)(r16 * ROWB + ((g ^ r16) << 4));
+  const uint32_t kbase = (uint32_t)(r16 * ROWB + ((g ^ bswz(r16)) << 4));
   const uint32_t trb = tr_base(lane);
 
   f32x4 acc[8][2];
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
 // each on half the query rows).  The keys' K and V rows are B operands in registers (rows past
 // the block's valid count zeroed).  For every attending query unit, in
 // 64-row query steps (Q and dO as two 32-row tiles each in LDS with the row
-// swizzle, the rows' LSE and delta beside them):
+// swizzle bswz, the rows' LSE and delta beside them):
 //   S[q][key] = Q K^T                A = Q rows,   B = K^T (registers)
 //   P = 2^(S c - LSE_q),  0 for keys past the count
 //   dP[q][key] = dO V^T              A = dO rows,  B = V^T (registers)
@@ -479,9 +490,9 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 8 / NW; ++i) {
       const int j = wave + i * NW;
-      dko[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ l4) ^ ((j & 3) << 2)) << 4));
+      dko[i] = (uint32_t)(j * 1024 + l4 * ROWB + ((pos ^ bswz(4 * j + l4)) << 4));
     }
-    const uint32_t abase = (uint32_t)(r16 * ROWB + ((g ^ r16) << 4));
+    const uint32_t abase = (uint32_t)(r16 * ROWB + ((g ^ bswz(r16)) << 4));
     const uint32_t trb = tr_base(lane);
 
     // query step t: unit list[t / QT_PER_UNIT], rows (t % QT_PER_UNIT)*64 ..
