@@ -227,6 +227,22 @@ __global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
   const int64_t row = (int64_t)b * p.meta_sb + (int64_t)h * p.meta_sh + qb;
   const int qrow0 = qb * BLK + wave * 32;
 
+  // Q and dO as B operands: row r16 (+16 qt), columns kk*32 + g*8 ..; loaded
+  // first so that they arrive while the selected set is decoded.
+  bf16x8 qreg[2][4], doreg[2][4];
+  float lse[2], dlt[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      qreg[qt][kk] = *(const bf16x8*)(p.q + r * HD + kk * 32 + g * 8);
+      doreg[qt][kk] = *(const bf16x8*)(p.dout + r * HD + kk * 32 + g * 8);
+    }
+    lse[qt] = p.lse[r];
+    dlt[qt] = p.delta[r];
+  }
+
   // selected set -> bmp[kb] = valid keys of kb if selected, else 0
   if constexpr (BITMAP) {
     const int8_t* mrow = p.mask + row * NK;
@@ -264,21 +280,6 @@ __global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
   const char* kplane = (const char*)(p.k + kvplane);
   const char* vplane = (const char*)(p.v + kvplane);
-
-  // Q and dO as B operands: row r16 (+16 qt), columns kk*32 + g*8 ..
-  bf16x8 qreg[2][4], doreg[2][4];
-  float lse[2], dlt[2];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      qreg[qt][kk] = *(const bf16x8*)(p.q + r * HD + kk * 32 + g * 8);
-      doreg[qt][kk] = *(const bf16x8*)(p.dout + r * HD + kk * 32 + g * 8);
-    }
-    lse[qt] = p.lse[r];
-    dlt[qt] = p.delta[r];
-  }
 
   const int l4 = lane >> 4, pos = lane & 15;
   uint32_t dko[8 / NW];
