@@ -11,7 +11,7 @@ import torch
 import block_sparse_attention_tile_amd as bsa
 import oracle
 
-# Spec tolerances for bf16 inputs: O max-abs 1e-2, LSE (base 2) 1e-3.
+# Target tolerances for bf16 inputs: O max-abs 1e-2, LSE (base 2) 1e-3.
 O_TOL = 1e-2
 LSE_TOL = 1e-3
 
@@ -89,7 +89,7 @@ def check(o_gpu, l_gpu, o_ref, l_ref, label="", o_rel=0.0, o_abs=O_TOL):
     """Asserts parity: no NaN, O within o_abs (+ o_rel*|O|), LSE within
     LSE_TOL, and empty rows bit-exact (+0 output, the finite sentinel).
 
-    The defaults are the benchmark spec's bound (max-abs 1e-2).  For inputs scaled
+    The defaults are the target bound (max-abs 1e-2).  For inputs scaled
     beyond N(0, 1) the bound is derived from the arithmetic (see
     scaled_input_bounds)."""
     o_gpu = np.asarray(o_gpu, dtype=np.float64)
