@@ -17,48 +17,70 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "bsa.h"
 #include "bsa_device.h"
 
 namespace {
 
-// One thread turns 16 consecutive codes into 16 bf16 values (32 bytes).
-// The table is the codebook rounded to bf16, staged in LDS.  The level of
-// an i8 code is (code + 128) = byte ^ 0x80; of an i4 nibble (code + 8) =
+// One workgroup turns 8192 consecutive codes into bf16 values: each thread
+// takes four groups of 8 codes, 256 groups apart, so that every load and
+// every 16-byte store of a wave covers one contiguous span, and all four
+// loads are in flight before the first lookup.  The bf16-rounded codebook
+// sits in LDS: for i8 one 16-bit entry per level, where the level of a code
+// byte is (code + 128) = byte ^ 0x80; for i4 one 32-bit entry per code byte
+// holding both of its values, the level of a nibble being (code + 8) =
 // nibble ^ 8.
+constexpr int DQ_R = 4;                 // groups of 8 codes per thread
+constexpr int DQ_GROUPS = 256 * DQ_R;   // groups per workgroup
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const f32x2 f = {x, 0.f};
+  const bf16x2 r = __builtin_convertvector(f, bf16x2);  // RNE
+  return (uint16_t)(__builtin_bit_cast(uint32_t, r) & 0xFFFFu);
+}
+
 template <int KIND>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const float* __restrict__ codebook,
                                                       uint16_t* __restrict__ out,
                                                       int64_t groups) {
-  constexpr int NENT = KIND == BSA_CODEBOOK_I8 ? 256 : 16;
-  __shared__ uint16_t tab[NENT];
-  for (int i = threadIdx.x; i < NENT; i += 256) {
-    const f32x2 f = {codebook[i], 0.f};
-    const bf16x2 r = __builtin_convertvector(f, bf16x2);  // RNE
-    tab[i] = (uint16_t)(__builtin_bit_cast(uint32_t, r) & 0xFFFFu);
+  constexpr bool I8 = KIND == BSA_CODEBOOK_I8;
+  using Word = std::conditional_t<I8, u32x2, uint32_t>;  // 8 codes
+  __shared__ std::conditional_t<I8, uint16_t, uint32_t> tab[256];
+  const int tid = threadIdx.x;
+  const int64_t g0 = (int64_t)blockIdx.x * DQ_GROUPS + tid;
+  Word w[DQ_R];
+#pragma unroll
+  for (int r = 0; r < DQ_R; ++r) {
+    const int64_t gi = g0 + r * 256;
+    if (gi < groups) w[r] = ((const Word*)codes)[gi];
+  }
+  if constexpr (I8) {
+    tab[tid] = bf16_rne(codebook[tid]);
+  } else {
+    tab[tid] = (uint32_t)bf16_rne(codebook[(tid & 15) ^ 8]) |
+               ((uint32_t)bf16_rne(codebook[(tid >> 4) ^ 8]) << 16);
   }
   __syncthreads();
-  for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < groups;
-       gi += (int64_t)gridDim.x * 256) {
-    uint32_t lv[16];  // table levels of the 16 codes
-    if constexpr (KIND == BSA_CODEBOOK_I8) {
-      const u32x4 w = ((const u32x4*)codes)[gi];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) lv[i] = ((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) ^ 0x80u;
+  for (int r = 0; r < DQ_R; ++r) {
+    const int64_t gi = g0 + r * 256;
+    if (gi >= groups) break;
+    u32x4 o;
+    if constexpr (I8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t x = w[r][i >> 1] >> (16 * (i & 1));
+        o[i] = (uint32_t)tab[(x & 0xFFu) ^ 0x80u] |
+               ((uint32_t)tab[((x >> 8) & 0xFFu) ^ 0x80u] << 16);
+      }
     } else {
-      const u32x2 w = ((const u32x2*)codes)[gi];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) lv[i] = ((w[i >> 3] >> (4 * (i & 7))) & 0xFu) ^ 0x8u;
+      for (int i = 0; i < 4; ++i) o[i] = tab[(w[r] >> (8 * i)) & 0xFFu];
     }
-    u32x4 o0, o1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o0[i] = (uint32_t)tab[lv[2 * i]] | ((uint32_t)tab[lv[2 * i + 1]] << 16);
-      o1[i] = (uint32_t)tab[lv[8 + 2 * i]] | ((uint32_t)tab[lv[8 + 2 * i + 1]] << 16);
-    }
-    ((u32x4*)out)[2 * gi] = o0;
-    ((u32x4*)out)[2 * gi + 1] = o1;
+    ((u32x4*)out)[gi] = o;
   }
 }
 
@@ -74,15 +96,16 @@ extern "C" bsa_status bsa_codebook_dequant(const void* codes, int32_t kind,
   const uintptr_t calign = kind == BSA_CODEBOOK_I8 ? 15u : 7u;
   if (((uintptr_t)codes & calign) != 0 || ((uintptr_t)out & 15u) != 0)
     return BSA_ERR_ALIGN;
-  const int64_t groups = n_values / 16;
-  const int64_t want = (groups + 255) / 256;
-  const uint32_t grid = (uint32_t)(want < 8192 ? want : 8192);
+  const int64_t groups = n_values / 8;
+  const int64_t blocks = (groups + DQ_GROUPS - 1) / DQ_GROUPS;
+  if (blocks > INT32_MAX) return BSA_ERR_UNSUPPORTED;
+  const dim3 grid((uint32_t)blocks);
   if (kind == BSA_CODEBOOK_I8)
-    hipLaunchKernelGGL(dequant_kernel<BSA_CODEBOOK_I8>, dim3(grid), dim3(256), 0,
+    hipLaunchKernelGGL(dequant_kernel<BSA_CODEBOOK_I8>, grid, dim3(256), 0,
                        (hipStream_t)stream, (const uint8_t*)codes, codebook,
                        (uint16_t*)out, groups);
   else
-    hipLaunchKernelGGL(dequant_kernel<BSA_CODEBOOK_I4>, dim3(grid), dim3(256), 0,
+    hipLaunchKernelGGL(dequant_kernel<BSA_CODEBOOK_I4>, grid, dim3(256), 0,
                        (hipStream_t)stream, (const uint8_t*)codes, codebook,
                        (uint16_t*)out, groups);
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;

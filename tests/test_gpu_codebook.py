@@ -33,7 +33,9 @@ def levels(codes: torch.Tensor) -> torch.Tensor:
 
 
 @pytest.mark.parametrize("kind,n", [("i8", 16), ("i8", 4096 * 48), ("i4", 16),
-                                    ("i4", 4096 * 32), ("i8", 0)])
+                                    ("i4", 4096 * 32), ("i8", 0),
+                                    # ragged: the last workgroup is partial
+                                    ("i8", 16 * 12345), ("i4", 16 * 9999)])
 def test_dequant_bit_exact(kind, n):
     g = torch.Generator().manual_seed(n + len(kind))
     ent = 256 if kind == "i8" else 16
