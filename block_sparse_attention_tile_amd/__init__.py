@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     BSA_KV_BF16,
     BSA_KV_BF16_SCALED,
     BSA_KV_FP8E4M3,
+    BSA_MAX_KEY_BLOCKS,
     BSA_OK,
     LSE_EMPTY,
     BsaError,

@@ -32,6 +32,7 @@ BSA_KV_BF16_SCALED = 2
 BSA_CODEBOOK_I8 = 0
 BSA_CODEBOOK_I4 = 1
 LSE_EMPTY = -3.4028234663852886e38  # BSA_LSE_EMPTY = -FLT_MAX
+BSA_MAX_KEY_BLOCKS = 16384
 
 
 class BsaError(RuntimeError):

@@ -34,6 +34,17 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
 
 
+def test_header_constants_match_the_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define BSA_MAX_KEY_BLOCKS (\d+)", text).group(1)) == \
+        api.BSA_MAX_KEY_BLOCKS
+    for name in ("OK", "ERR_NULL", "ERR_SHAPE", "ERR_UNSUPPORTED", "ERR_ALIGN",
+                 "ERR_HIP", "KV_BF16", "KV_FP8E4M3", "KV_BF16_SCALED",
+                 "CODEBOOK_I8", "CODEBOOK_I4"):
+        m = re.search(r"\bBSA_%s\s*=\s*(\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(api, "BSA_" + name), name
+
+
 def test_status_strings():
     for s in range(6):
         assert api.bsa_status_str(s)

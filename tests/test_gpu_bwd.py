@@ -120,6 +120,22 @@ def test_backward_parity(label, kw):
     check_grads(got, ref, label)
 
 
+def test_backward_longest_key_block_list():
+    """Key block 0 selected by every query unit of its K/V head: the dK/dV
+    workgroup's map row and unit list hold BSA_MAX_KEY_BLOCKS entries (the
+    largest LDS footprint) and it walks 16384 query steps."""
+    w = workloads.make_random(216, B=1, H=4, Hk=1, S=4096 * 64, Sk=64 * 64,
+                              block=64, density=2 / 64, max_kv=2,
+                              vbs_mode="tiny")
+    w.q2k_idx[:, 0] = 0
+    assert w.Hk and (w.H // w.Hk) * w.NQ == bsa.BSA_MAX_KEY_BLOCKS
+    log(f"[bwd] longest list H{w.H} Hk{w.Hk} S{w.S} Sk{w.Sk}")
+    dout = dout_of(w, 10)
+    got = gpu_bwd(w, dout)
+    ref = oracle_bwd(w, dout)
+    check_grads(got, ref, "longest_list")
+
+
 def test_backward_all_rows_empty_gives_zero_gradients():
     w = workloads.make_random(211, B=1, H=2, S=256, block=64, count_mode="zero")
     log("[bwd] all rows empty")

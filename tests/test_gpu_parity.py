@@ -113,6 +113,38 @@ def test_small_random_parity(label, kw):
         check(o_gpu, l_gpu, o_ref, l_ref, label)
 
 
+# BSA_MAX_KEY_BLOCKS key blocks: the LDS byte map and block list at their
+# largest, the list walked in 64-entry chunks to its end and per-lane load
+# offsets up to the last block (512 MB into the K/V plane at block 128).
+# Every row selects the first and the last block, both fully valid.
+MAX_NK = [
+    ("lut64_max_key_blocks", dict(seed=130, B=1, H=1, S=128, Sk=64 * 16384,
+                                  block=64, density=300 / 16384,
+                                  vbs_mode="partial")),
+    ("bitmap128_max_key_blocks", dict(seed=131, B=1, H=2, Hk=1, S=256,
+                                      Sk=128 * 16384, block=128, form="bitmap",
+                                      density=0.01, vbs_mode="edges")),
+]
+
+
+@pytest.mark.parametrize("label,kw", MAX_NK, ids=[c[0] for c in MAX_NK])
+def test_max_key_blocks_parity(label, kw):
+    kw = dict(kw)
+    w = workloads.make_random(kw.pop("seed"), **kw)
+    assert w.NK == bsa.BSA_MAX_KEY_BLOCKS
+    w.vbs[0] = w.vbs[-1] = w.block
+    if w.form == "lut":
+        w.q2k_idx[:, 0] = w.NK - 1
+        w.q2k_idx[:, 1] = 0
+    else:
+        w.mask[:, 0] = 1
+        w.mask[:, -1] = 1
+    log(f"[parity] {label} H{w.H} Hk{w.Hk} S{w.S} Sk{w.Sk} blk{w.block} form={w.form}")
+    out, lse = run_gpu(w)
+    o_ref, l_ref = run_oracle(w)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, label)
+
+
 def test_tiny_named_workload_full_parity():
     w = workloads.make_config(0)
     log(f"[parity] {w.name} (every element)")
