@@ -86,6 +86,54 @@ def attended_pairs(w, units=None) -> int:
     return int((sel.long() * nv[None, :]).sum()) * w.block
 
 
+def _valid_counts(w) -> torch.Tensor:
+    return torch.full((w.NK,), w.block, dtype=torch.long) if w.vbs is None \
+        else w.vbs.long().clamp(0, w.block)
+
+
+def issued_tile_flop(w) -> float:
+    """Matrix-core work the forward kernel issues, counted in whole 32-key
+    tiles (4*D*block*32 per tile): bf16 K/V tiles are cut from each unit's
+    stream of valid keys, fp8 and scaled (codebook) K/V tiles from one block
+    at a time."""
+    sel = selected_matrix(w).long()
+    nv = _valid_counts(w)
+    if w.kv_fp8 or w.kv_codebook:
+        tiles = int((sel * ((nv + 31) // 32)[None, :]).sum())
+    else:
+        tiles = int(((sel * nv[None, :]).sum(1) + 31).div(32, rounding_mode="floor").sum())
+    return 4.0 * w.D * w.block * 32 * tiles
+
+
+def compulsory_bytes(w) -> int:
+    """Bytes every forward pass must move at least once: Q, O and the LSE,
+    the valid K/V rows of every block some unit selects (with their scales),
+    and the selection metadata."""
+    sel = selected_matrix(w).view(w.B, w.Hk, (w.H // w.Hk) * w.NQ, w.NK).any(2)
+    rows = int((sel.long() * _valid_counts(w)[None, None, :]).sum())
+    row_bytes = w.k.shape[-1] * w.k.element_size()
+    kv = 2 * rows * row_bytes
+    if w.k_scale is not None:
+        kv += 2 * int(sel.sum()) * 4
+    q = w.q.numel() * w.q.element_size()
+    meta = (w.q2k_idx.numel() * 4 + w.q2k_num.numel() * 4) if w.form == "lut" \
+        else w.mask.numel()
+    if w.vbs is not None:
+        meta += w.vbs.numel() * 4
+    return 2 * q + w.B * w.H * w.S * 4 + kv + meta
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def codebook_recode(w, kind: str):
     """The workload with its K/V re-coded as codebook codes (seeded
     bf16-exact codebooks of 256 (i8) or 16 (i4) levels, per-block scales)."""
@@ -224,6 +272,8 @@ def cpu_baseline(w, target_s: float):
         "value": 4.0 * w.D * pairs / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": (f"{n} of {w.n_units} work units (b,h,q-block) of "
                    f"{w.name}, drawn at random (seed 1234); {pairs} attended "
@@ -448,6 +498,8 @@ def main() -> int:
     progress(f"timed {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)")
 
     tflops = flop / (ms * 1e-3) / 1e12
+    traffic = stored_traffic(w.name)
+    compulsory = compulsory_bytes(w)
     result = {
         "metric": "effective TFLOP/s (4*D*attended pairs) + % bf16 MFMA peak, "
                   "VSA fwd",
@@ -471,6 +523,11 @@ def main() -> int:
             "attended_pairs": pairs,
             "effective_flop_per_step": flop,
             "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+            "issued_tile_flop_per_step": issued_tile_flop(w),
+            "compulsory_bytes": compulsory,
+            "compulsory_gbs": round(compulsory / (ms * 1e-3) / 1e9, 1),
+            "fabric_gbs": (None if traffic is None else
+                           round(traffic / (ms * 1e-3) / 1e9, 1)),
         },
         "roofline": {
             "bound": "mfma",
@@ -478,7 +535,7 @@ def main() -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": stored_traffic(w.name),
+            "traffic": traffic,
         },
     }
     if not args.no_cpu_baseline:
