@@ -44,6 +44,36 @@ def test_tiny_named_workload_pair_count_closed_form():
     assert bench.attended_pairs(w) == want == _oracle_pairs(w)
 
 
+def test_tiny_named_workload_issued_tiles_and_compulsory_bytes():
+    w = workloads.make_config(0)
+    sel = bench.selected_matrix(w).numpy()
+    # stream tiles: each unit's valid keys cut into 32-key tiles
+    tiles = sum(-(-sum(40 if kb == 7 else 64 for kb in range(8) if sel[u, kb])
+                  // 32) for u in range(8))
+    assert bench.issued_tile_flop(w) == 4.0 * 128 * 64 * 32 * tiles
+    # Q and O bf16, the LSE, the valid rows of every selected block of K and
+    # V once (bf16 rows of 256 bytes), the LUT (8 x 8 int32), counts, vbs
+    used = [kb for kb in range(8) if sel[:, kb].any()]
+    kv_rows = sum(40 if kb == 7 else 64 for kb in used)
+    want = 2 * 512 * 128 * 2 + 512 * 4 + 2 * kv_rows * 256 + 8 * 8 * 4 + 8 * 4 + 8 * 4
+    assert bench.compulsory_bytes(w) == want
+
+
+def test_fp8_tiles_are_per_block():
+    w = workloads.make_random(5, B=1, H=2, S=512, block=64, kv="fp8",
+                              vbs_mode="random", density=0.5)
+    sel = bench.selected_matrix(w).numpy()
+    nv = w.vbs.tolist()
+    # one block per tile: a block with 1-32 valid keys is one tile, 33-64 two
+    tiles = 0
+    for u in range(w.n_units):
+        for kb in range(w.NK):
+            if sel[u, kb] and nv[kb] > 0:
+                tiles += 1 if nv[kb] <= 32 else 2
+    assert bench.issued_tile_flop(w) == 4.0 * 128 * 64 * 32 * tiles
+    assert bench.issued_tile_flop(w) >= 4.0 * 128 * bench.attended_pairs(w)
+
+
 def test_multi_gpu_request_exits_with_message(monkeypatch, capsys):
     monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
     assert bench.main() == 2
