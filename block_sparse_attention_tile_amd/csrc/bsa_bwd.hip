@@ -468,6 +468,9 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
   const bool halves = 2 * nv <= BLK;
   const int rep = halves && wave >= NW / 2 ? 1 : 0;       // row half (halves)
   const int ckey = (halves ? wave % (NW / 2) : wave) * 16 + r16;  // key computed
+  // A wave whose 16 keys all lie past the count only loads and synchronises
+  // (its dK, dV stay zero), which leaves its SIMD to the other workgroup.
+  const bool active = ckey - r16 < nv;
 
   if (nsteps > 0) {
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
@@ -532,6 +535,11 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
         __syncthreads();
         const bool has_next = t + 1 < nsteps;
         if (has_next) issue(step_rows(t + 1), STG ^ 1);
+        if (!active) {
+          if (!has_next) return true;
+          ++t;
+          return false;
+        }
         const char* stage = smem + STG * DSTAGE;
         const char* qtile = stage + hf0 * TILE_BYTES;          // Q rows of half hf0
         const char* dtile = stage + (2 + hf0) * TILE_BYTES;    // dO rows of half hf0
