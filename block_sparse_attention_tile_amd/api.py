@@ -66,6 +66,57 @@ def _cur_stream(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _need_device(device: torch.device, **tensors) -> None:
+    """Every tensor the kernels read or write must be GPU memory on the
+    device of ``q``: the library dereferences the raw pointers on the GPU."""
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != device):
+            raise ValueError(f"{name} must be a tensor on {device}, got {t.device}")
+
+
+def _need_elems(name: str, t: Optional[torch.Tensor], n: int) -> None:
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements; the call reads {n}")
+
+
+def _need_out(name: str, t: torch.Tensor, shape, dtype) -> None:
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape "
+                         f"{tuple(shape)}")
+
+
+def _meta_rows(B: int, H: int, NQ: int, sb: int, sh: int) -> int:
+    """Metadata rows the kernels address: row(b, h, qb) = b*sb + h*sh + qb."""
+    return (B - 1) * max(sb, 0) + (H - 1) * max(sh, 0) + NQ
+
+
+def _check_meta(q, k, block, sb, sh, *, idx=None, num=None, mask=None,
+                vbs=None, k_scale=None, v_scale=None) -> None:
+    """Device and size checks of the metadata against what the kernels read
+    (the C ABI takes raw pointers and cannot see buffer sizes)."""
+    B, H, S, _ = q.shape
+    Hk, Sk = int(k.shape[1]), int(k.shape[2])
+    _need_device(q.device, q2k_idx=idx, q2k_num=num, mask=mask,
+                 variable_block_sizes=vbs, k_scale=k_scale, v_scale=v_scale)
+    if block not in (64, 128) or S % block or Sk % block:
+        return  # the library rejects these shapes before any launch
+    NQ, NK = S // block, Sk // block
+    rows = _meta_rows(B, H, NQ, sb, sh)
+    if idx is not None:
+        width = int(idx.shape[-1]) if idx.dim() > 0 else 0
+        if width > 0 and idx.numel() // width < rows:
+            raise ValueError(f"q2k_idx has {idx.numel() // width} rows; the "
+                             f"strides address {rows}")
+        _need_elems("q2k_num", num, rows)
+    if mask is not None:
+        if mask.dim() < 1 or int(mask.shape[-1]) != NK:
+            raise ValueError(f"mask rows must hold Sk/block = {NK} bytes")
+        _need_elems("mask", mask, rows * NK)
+    _need_elems("variable_block_sizes", vbs, NK)
+    _need_elems("k_scale", k_scale, B * Hk * NK)
+    _need_elems("v_scale", v_scale, B * Hk * NK)
+
+
 def _kv_dtype(k: torch.Tensor, v: torch.Tensor) -> int:
     if k.dtype != v.dtype:
         raise TypeError("k and v must have the same dtype")
@@ -91,6 +142,8 @@ def bsa_codebook_dequant(codes: torch.Tensor, codebook: torch.Tensor
         kind, shape = BSA_CODEBOOK_I4, tuple(codes.shape[:-1]) + (2 * codes.shape[-1],)
     else:
         raise TypeError("codes must be int8 (i8) or uint8 (packed i4)")
+    if not codes.is_cuda:
+        raise ValueError(f"codes must be a GPU tensor, got {codes.device}")
     codes = codes.contiguous()
     cb = codebook.to(device=codes.device, dtype=torch.float32).contiguous()
     if cb.numel() != (256 if kind == BSA_CODEBOOK_I8 else 16):
@@ -112,6 +165,9 @@ def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block,
              k_codebook=None, v_codebook=None):
     if q.dtype != torch.bfloat16 or q.dim() != 4:
         raise TypeError("q must be a 4-D bf16 [B, H, S, D] tensor")
+    if not q.is_cuda:
+        raise ValueError(f"q must be a GPU tensor, got {q.device}")
+    _need_device(q.device, k=k, v=v, out=out, lse=lse)
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
     if k.dtype in (torch.int8, torch.uint8):
         if k_codebook is None or v_codebook is None:
@@ -139,10 +195,13 @@ def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block,
     B, H, S, D = q.shape
     if out is None:
         out = torch.empty_like(q)
+    _need_out("out", out, q.shape, torch.bfloat16)
     if need_lse and lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     if not need_lse:
         lse = None
+    if lse is not None:
+        _need_out("lse", lse, (B, H, S), torch.float32)
     return q, k, v, kvd, k_scale, v_scale, out, lse
 
 
@@ -172,6 +231,8 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     num = _i32(q2k_num)
     vbs = _i32(variable_block_sizes)
     sb, sh = meta_strides if meta_strides is not None else (H * NQ, NQ)
+    _check_meta(q, k, block, int(sb), int(sh), idx=idx, num=num, vbs=vbs,
+                k_scale=ks, v_scale=vs)
     if sm_scale is None:
         sm_scale = 1.0 / (D ** 0.5)
     rc = _lib.load().bsa_fwd_lut(
@@ -209,6 +270,8 @@ def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     m = mask.to(torch.int8).contiguous()
     vbs = _i32(variable_block_sizes)
     sb, sh = mask_strides if mask_strides is not None else (H * NQ, NQ)
+    _check_meta(q, k, block, int(sb), int(sh), mask=m, vbs=vbs, k_scale=ks,
+                v_scale=vs)
     if sm_scale is None:
         sm_scale = 1.0 / (D ** 0.5)
     rc = _lib.load().bsa_fwd_bitmap(
@@ -225,6 +288,8 @@ def bsa_mask_to_lut(mask: torch.Tensor):
     """Compacts a block map ``mask [..., NK]`` (nonzero = selected) on the
     GPU into ``(q2k_idx [..., NK] int32, q2k_num [...] int32)``: ascending
     selected key blocks, then -1 padding."""
+    if not mask.is_cuda:
+        raise ValueError(f"mask must be a GPU tensor, got {mask.device}")
     m = mask.to(torch.int8).contiguous()
     if m.dim() < 1:
         raise ValueError("mask must have a key-block dimension")
@@ -274,16 +339,30 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or \
             v.dtype != torch.bfloat16:
         raise TypeError("the backward pass takes bf16 q, k, v")
+    if not q.is_cuda:
+        raise ValueError(f"q must be a GPU tensor, got {q.device}")
+    _need_device(q.device, k=k, v=v, out=out, dout=dout, lse=lse,
+                 workspace=workspace)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or \
+            k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3] or \
+            q.shape[1] % k.shape[1] != 0:
+        raise ValueError("q must be [B, H, S, D] and k, v [B, Hk, Sk, D] with "
+                         "H a multiple of Hk")
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
     out, dout = out.contiguous(), dout.to(torch.bfloat16).contiguous()
     lse = lse.to(torch.float32).contiguous()
     B, H, S, D = q.shape
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != torch.bfloat16 or \
+            tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, S):
+        raise ValueError("out and dout must be bf16 like q, lse [B, H, S]")
     Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
     lib = _lib.load()
     need = int(lib.bsa_bwd_workspace_size(B, H, S, Sk, int(block)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -296,11 +375,15 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    int(workspace.numel()), B, H, Hk, S, Sk, D, int(block), st)
     if q2k_idx is not None:
         idx, num = _i32(q2k_idx), _i32(q2k_num)
+        _check_meta(q, k, block, int(sb), int(sh), idx=idx, num=num, vbs=vbs)
         rc = lib.bsa_bwd_lut(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
                              _ptr(lse), _ptr(idx), _ptr(num), int(idx.shape[-1]),
                              int(sb), int(sh), _ptr(vbs), *common_tail)
     else:
+        if mask is None:
+            raise ValueError("give q2k_idx and q2k_num, or mask")
         m = mask.to(torch.int8).contiguous()
+        _check_meta(q, k, block, int(sb), int(sh), mask=m, vbs=vbs)
         rc = lib.bsa_bwd_bitmap(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
                                 _ptr(lse), _ptr(m), int(sb), int(sh), _ptr(vbs),
                                 *common_tail)

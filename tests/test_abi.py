@@ -125,6 +125,25 @@ def test_python_binding_checks_dtypes_before_calling():
                         torch.zeros((1,), dtype=torch.int32), block=64)
 
 
+def test_python_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16)
+    idx = torch.zeros((1, 1), dtype=torch.int32)
+    num = torch.ones((1,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        api.bsa_fwd_lut(q, q, q, idx, num, block=64)
+    with pytest.raises(ValueError, match="GPU"):
+        api.bsa_fwd_bitmap(q, q, q, idx.to(torch.int8), block=64)
+    with pytest.raises(ValueError, match="GPU"):
+        api.bsa_bwd(q, q, q, q, q, torch.zeros((1, 1, 64)), block=64,
+                    q2k_idx=idx, q2k_num=num)
+    with pytest.raises(ValueError, match="GPU"):
+        api.bsa_mask_to_lut(idx.to(torch.int8))
+    with pytest.raises(ValueError, match="GPU"):
+        api.bsa_codebook_dequant(torch.zeros((16,), dtype=torch.int8),
+                                 torch.zeros((256,)))
+
+
 def mask_lut(**over):
     args = dict(mask=A, rows=4, nk=8, idx=A, num=A, stream=None)
     args.update(over)

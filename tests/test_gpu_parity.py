@@ -276,3 +276,40 @@ def test_invalid_static_arguments_raise_and_write_nothing():
     assert e.value.status == bsa.BSA_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert (out.float() == 7.0).all().item() and (lse == 7.0).all().item()
+
+
+def test_binding_rejects_misplaced_or_short_buffers_before_launch():
+    """The C ABI sees raw pointers only; the binding checks devices and
+    sizes against what the kernels would read or write."""
+    w = workloads.make_random(206, B=1, H=2, S=256, block=64,
+                              vbs_mode="partial")
+    d = to_dev(w)
+    args = (d["q"], d["k"], d["v"])
+    log("[binding] misplaced and short buffers")
+    bad = [
+        dict(q2k_idx=w.q2k_idx),                       # metadata on the host
+        dict(q2k_idx=d["q2k_idx"][:3]),                # fewer rows than units
+        dict(q2k_num=d["q2k_num"][:3]),
+        dict(vbs=d["vbs"][:2]),                        # fewer than NK entries
+        dict(out=torch.empty((1, 2, 128, 128), dtype=torch.bfloat16,
+                             device="cuda")),          # wrong output shape
+        dict(lse=torch.empty((1, 2, 256), dtype=torch.float16,
+                             device="cuda")),          # wrong LSE dtype
+    ]
+    for over in bad:
+        kw = dict(q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"], vbs=d["vbs"],
+                  out=None, lse=None)
+        kw.update(over)
+        with pytest.raises(ValueError):
+            bsa.bsa_fwd_lut(*args, kw["q2k_idx"], kw["q2k_num"], kw["vbs"],
+                            block=64, out=kw["out"], lse=kw["lse"])
+    mask = torch.ones((2 * 4, 3), dtype=torch.int8, device="cuda")  # NK is 4
+    with pytest.raises(ValueError):
+        bsa.bsa_fwd_bitmap(*args, mask, block=64)
+    out, lse = bsa.bsa_fwd_lut(*args, d["q2k_idx"], d["q2k_num"], d["vbs"],
+                               block=64)
+    with pytest.raises(ValueError):
+        bsa.bsa_bwd(*args, out, out[:, :1].contiguous(), lse, block=64,
+                    q2k_idx=d["q2k_idx"], q2k_num=d["q2k_num"])
+    torch.cuda.synchronize()
+
