@@ -171,18 +171,23 @@ def launch(w, d, out, lse):
                            need_lse=lse is not None)
 
 
-def stored_traffic(workload_name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
+def stored_counters(workload_name: str) -> dict:
+    """The committed rocprofv3 counter record of the forward kernel on a
+    workload, if it was taken on the current kernel source; else {}."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     e = t.get(workload_name)
     if not e or e.get("kernel_sha256_16") != kernel_hash():
-        return None
-    return e.get("hbm_bytes_per_launch")
+        return {}
+    return e
+
+
+def stored_traffic(workload_name: str):
+    """HBM bytes per launch from the committed counter record, or None."""
+    return stored_counters(workload_name).get("hbm_bytes_per_launch")
 
 
 def _counter_means(csv_path: str, counter: str, kernel_substr: str):
@@ -204,7 +209,8 @@ def record_traffic(pmc_dir: str, workload: int) -> int:
     workload) into HBM bytes per launch of the forward kernel, each counter
     scaled by what it reads for a copy of exactly 1 GiB read + 1 GiB
     written, and stores them in the traffic file under the workload name,
-    keyed to the current kernel source."""
+    keyed to the current kernel source.  A fifth run under ``hit``
+    (TCC_HIT_sum, TCC_MISS_sum), when present, adds the L2 hit rate."""
     csv_of = lambda n: os.path.join(pmc_dir, n, "run_counter_collection.csv")
     gib = float(1 << 30)
     cf, _ = _counter_means(csv_of("copy_fetch"), "FETCH_SIZE", "copyBuffer")
@@ -214,6 +220,12 @@ def record_traffic(pmc_dir: str, workload: int) -> int:
     kw, nw = _counter_means(csv_of("write"), "WRITE_SIZE", "bsa_fwd_kernel")
     fetch = kf * 1024.0 * f_fac
     write = kw * 1024.0 * w_fac
+    hit_rate = None
+    if os.path.exists(csv_of("hit")):
+        # optional fifth run: TCC_HIT_sum and TCC_MISS_sum on the workload
+        hit, _ = _counter_means(csv_of("hit"), "TCC_HIT_sum", "bsa_fwd_kernel")
+        miss, _ = _counter_means(csv_of("hit"), "TCC_MISS_sum", "bsa_fwd_kernel")
+        hit_rate = round(hit / (hit + miss), 4) if hit + miss > 0 else None
     name = workloads.CONFIG_NAMES[workload]
     try:
         with open(TRAFFIC_FILE) as f:
@@ -229,6 +241,8 @@ def record_traffic(pmc_dir: str, workload: int) -> int:
         "write_scale": round(w_fac, 4),
         "dispatches_averaged": [nf, nw],
     }
+    if hit_rate is not None:
+        table[name]["l2_hit_rate"] = hit_rate
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(table, f, indent=1, sort_keys=True)
         f.write("\n")
@@ -498,7 +512,8 @@ def main() -> int:
     progress(f"timed {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)")
 
     tflops = flop / (ms * 1e-3) / 1e12
-    traffic = stored_traffic(w.name)
+    counters = stored_counters(w.name)
+    traffic = counters.get("hbm_bytes_per_launch")
     compulsory = compulsory_bytes(w)
     result = {
         "metric": "effective TFLOP/s (4*D*attended pairs) + % bf16 MFMA peak, "
@@ -528,6 +543,7 @@ def main() -> int:
             "compulsory_gbs": round(compulsory / (ms * 1e-3) / 1e9, 1),
             "fabric_gbs": (None if traffic is None else
                            round(traffic / (ms * 1e-3) / 1e9, 1)),
+            "l2_hit_rate": counters.get("l2_hit_rate"),
         },
         "roofline": {
             "bound": "mfma",

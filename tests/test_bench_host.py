@@ -74,6 +74,45 @@ def test_fp8_tiles_are_per_block():
     assert bench.issued_tile_flop(w) >= 4.0 * 128 * bench.attended_pairs(w)
 
 
+def _counter_csv(path, rows):
+    import os
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w") as f:
+        f.write('"Kernel_Name","Counter_Name","Counter_Value"\n')
+        for kernel, counter, value in rows:
+            f.write(f'"{kernel}","{counter}",{value}\n')
+
+
+def test_record_traffic_scales_counters_by_the_copy_calibration(tmp_path,
+                                                                monkeypatch):
+    import json
+    gib_kib = float(1 << 20)
+    kern = "void bsa_fwd_kernel<64, 0, false>(FwdParams)"
+    _counter_csv(tmp_path / "copy_fetch", [("__amd_rocclr_copyBuffer",
+                                            "FETCH_SIZE", gib_kib / 2)])
+    _counter_csv(tmp_path / "copy_write", [("__amd_rocclr_copyBuffer",
+                                            "WRITE_SIZE", gib_kib)])
+    _counter_csv(tmp_path / "fetch", [(kern, "FETCH_SIZE", 1000.0),
+                                      (kern, "FETCH_SIZE", 3000.0)])
+    _counter_csv(tmp_path / "write", [(kern, "WRITE_SIZE", 500.0)])
+    _counter_csv(tmp_path / "hit", [(kern, "TCC_HIT_sum", 30.0),
+                                    (kern, "TCC_MISS_sum", 70.0)])
+    table = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(table))
+    monkeypatch.setattr(bench, "kernel_hash", lambda: "feedfacefeedface")
+    assert bench.record_traffic(str(tmp_path), 2) == 0
+    e = json.load(open(table))[workloads.CONFIG_NAMES[2]]
+    # the copy's FETCH_SIZE shows half of the GiB it read: fetch counts x2
+    assert e["fetch_bytes_per_launch"] == 2 * 2000 * 1024
+    assert e["write_bytes_per_launch"] == 500 * 1024
+    assert e["hbm_bytes_per_launch"] == 2 * 2000 * 1024 + 500 * 1024
+    assert e["dispatches_averaged"] == [2, 1]
+    assert e["l2_hit_rate"] == 0.3
+    assert bench.stored_traffic(workloads.CONFIG_NAMES[2]) == e["hbm_bytes_per_launch"]
+    monkeypatch.setattr(bench, "kernel_hash", lambda: "0000000000000000")
+    assert bench.stored_traffic(workloads.CONFIG_NAMES[2]) is None  # stale source
+
+
 def test_multi_gpu_request_exits_with_message(monkeypatch, capsys):
     monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
     assert bench.main() == 2
