@@ -174,33 +174,44 @@ struct Acc {
   float l[2];
 };
 
+// K operands of one tile for this wave (A operand of S^T = K Q^T):
+// k[h][kk] holds dims kk*32 + 8g .. +7 of tile key h*16 + r16.  All eight
+// reads are issued together right after the tile is published, so their
+// latency is paid once per tile.
+struct KOps {
+  bf16x8 k[2][4];
+};
+
+__device__ __forceinline__ void load_k(const char* sb, uint32_t kbase, KOps& ko) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      ko.k[h][kk] = *(const bf16x8*)(sb + (kbase ^ (kk << 6)) + h * 16 * ROWB);
+}
+
 // Raw scores of one tile for this wave: s[qt][e], e = 4*s2 + j is key
 // s2*16 + 4g + j of the tile and query qt*16 + r16.  Keys at or past the
 // valid count (lane limit lim = nvt - 4g) are set to -inf.
 template <int KIND>
-__device__ __forceinline__ void tile_scores(const char* sb, uint32_t kbase,
-                                            const bf16x8 (&qreg)[2][4], int nvt,
-                                            int lim, float (&s)[2][8]) {
+__device__ __forceinline__ void tile_scores(const KOps& ko, const bf16x8 (&qreg)[2][4],
+                                            int nvt, int lim, float (&s)[2][8]) {
   f32x4 sacc[2][2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const bf16x8 kop = *(const bf16x8*)(sb + (kbase ^ (kk << 6)));
+  for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
       sacc[0][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          kop, qreg[qt][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[0][qt],
+          ko.k[0][kk], qreg[qt][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[0][qt],
           0, 0, 0);
-  }
   sacc[1][0] = sacc[1][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (KIND == FULL || nvt > 16) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 kop = *(const bf16x8*)(sb + (kbase ^ (kk << 6)) + 16 * ROWB);
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
         sacc[1][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            kop, qreg[qt][kk], sacc[1][qt], 0, 0, 0);
-    }
+            ko.k[1][kk], qreg[qt][kk], sacc[1][qt], 0, 0, 0);
   }
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
@@ -248,11 +259,16 @@ __device__ __forceinline__ void tile_probs(const float (&s)[2][8], float cs,
   }
 }
 
-// O^T[d][query] += V^T P^T.  The MFMA K index 8g+i maps to tile key 4g+i
-// (i<4) and 16+4g+(i-4) (i>=4), matching P's accumulator layout; V^T comes
-// from transposing LDS reads at vbase ^ (dt << 5) (+16 rows).
-__device__ __forceinline__ void tile_pv(const char* sb, uint32_t vbase,
-                                        const bf16x8 (&pop)[2], Acc& acc) {
+// V^T operands of one tile: v[dt] holds, for d-row dt*16 + r16 of V^T, the
+// tile keys of MFMA K index 8g+i: key 4g+i (i<4) and 16+4g+(i-4) (i>=4),
+// matching P's accumulator layout.  Read with the transposing LDS read at
+// vbase ^ (dt << 5) (+16 rows); issued before the softmax so that their
+// latency hides under it.
+struct VOps {
+  bf16x8 v[8];
+};
+
+__device__ __forceinline__ void load_v(const char* sb, uint32_t vbase, VOps& vo) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     const uint32_t va = vbase ^ (uint32_t)(dt << 5);
@@ -260,12 +276,18 @@ __device__ __forceinline__ void tile_pv(const char* sb, uint32_t vbase,
     const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_i16x4*)(sb + va + 16 * ROWB));
     const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-    const bf16x8 vop = __builtin_bit_cast(bf16x8, vv);
+    vo.v[dt] = __builtin_bit_cast(bf16x8, vv);
+  }
+}
+
+// O^T[d][query] += V^T P^T.
+__device__ __forceinline__ void tile_pv(const VOps& vo, const bf16x8 (&pop)[2], Acc& acc) {
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
-      acc.o[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[qt],
+      acc.o[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo.v[dt], pop[qt],
                                                                acc.o[dt][qt], 0, 0, 0);
-  }
 }
 
 // Direct loads of this wave's share of a bf16 tile.  The tile's 8 slices
@@ -320,6 +342,11 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   constexpr bool SCALED = KV != BSA_KV_BF16;  // per-block K/V scales
   constexpr int NW = BLK / 32;  // waves; each owns 32 query rows
   constexpr int NT = NW * 64;
+  // Operand reads pinned ahead of their products (K right after the tile is
+  // published, V before the softmax) where registers allow: with two waves
+  // per SIMD there is room for both operand sets; the block-128 bf16 kernel,
+  // capped for three waves per SIMD, leaves the order to the compiler.
+  constexpr bool EARLY_OPS = waves_per_simd<BLK, KV>() == 2;
   // All LDS is dynamic, so the stages start at LDS address 0 and every
   // operand address is a per-lane constant plus an immediate offset.
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -541,6 +568,12 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
       // tile `cur` complete in LDS for every wave; stage STG^1 free again
       wait_vm_all();
       __syncthreads();
+      const char* sb = smem + STG * STAGE_BYTES;
+      KOps ko;
+      if constexpr (EARLY_OPS) {
+        load_k(sb, kbase, ko);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       [[maybe_unused]] Tile nxt{};
       [[maybe_unused]] int nxt_rows = 0;
       bool has_next;
@@ -556,7 +589,6 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
         nvt = cur_rows;
       }
       const int lim = nvt - 4 * g;
-      const char* sb = smem + STG * STAGE_BYTES;
       float cs = p.c;
       float vsc = 1.f;
       if constexpr (SCALED) {
@@ -564,34 +596,42 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
         vsc = vsc_cur;
       }
 
-      // ---- A5 + A6: scores and probabilities
-      bf16x8 pop[2];
-      auto body = [&](auto kind_c) {
+      // ---- A5 + A6: scores and probabilities.  The two tile kinds differ in
+      // the scores only; the paths join before the V reads are issued.
+      float sv[2][8];
+      auto scores = [&](auto kind_c) {
         constexpr int KIND = decltype(kind_c)::value;
-        float sv[2][8];
-        tile_scores<KIND>(sb, kbase, qreg, nvt, lim, sv);
-        if constexpr (SAFE || FIRST) {
-          float tm[2];
-          tile_max(sv, cs, tm);
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) {
-            const float mnew = fmaxf(acc.m[qt], tm[qt]);
-            if constexpr (SAFE && !FIRST) {
-              const float alpha = __builtin_amdgcn_exp2f(acc.m[qt] - mnew);
-              acc.l[qt] *= alpha;
-#pragma unroll
-              for (int dt = 0; dt < 8; ++dt) acc.o[dt][qt] *= alpha;
-            }
-            acc.m[qt] = mnew;
-          }
-        }
-        tile_probs<SCALED>(sv, cs, vsc, acc, pop);
+        if constexpr (!EARLY_OPS) load_k(sb, kbase, ko);
+        tile_scores<KIND>(ko, qreg, nvt, lim, sv);
       };
-      if (nvt >= KT) body(IntC<FULL>{});
-      else body(IntC<PART>{});
+      if (nvt >= KT) scores(IntC<FULL>{});
+      else scores(IntC<PART>{});
+      VOps vo;
+      if constexpr (EARLY_OPS) {
+        load_v(sb, vbase, vo);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (SAFE || FIRST) {
+        float tm[2];
+        tile_max(sv, cs, tm);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const float mnew = fmaxf(acc.m[qt], tm[qt]);
+          if constexpr (SAFE && !FIRST) {
+            const float alpha = __builtin_amdgcn_exp2f(acc.m[qt] - mnew);
+            acc.l[qt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) acc.o[dt][qt] *= alpha;
+          }
+          acc.m[qt] = mnew;
+        }
+      }
+      bf16x8 pop[2];
+      tile_probs<SCALED>(sv, cs, vsc, acc, pop);
 
       // ---- A7: PV
-      tile_pv(sb, vbase, pop, acc);
+      if constexpr (!EARLY_OPS) load_v(sb, vbase, vo);
+      tile_pv(vo, pop, acc);
 
       if (!has_next) return true;
       if constexpr (FP8) store_tile_fp8<NT>(st, smem + (STG ^ 1) * STAGE_BYTES, tid);
