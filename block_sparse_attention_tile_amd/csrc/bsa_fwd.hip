@@ -569,25 +569,33 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
       wait_vm_all();
       __syncthreads();
       const char* sb = smem + STG * STAGE_BYTES;
+      [[maybe_unused]] Tile nxt{};
+      [[maybe_unused]] int nxt_rows = 0;
+      bool has_next = false;
+      // Loads of the next tile.  fp8 tiles come through registers and are
+      // stored to LDS at the end of this step, so their loads go out first;
+      // DMA tiles have a whole step of slack, so the K operand reads of this
+      // tile go out first.
+      auto issue_next = [&]() {
+        if constexpr (SCALED) {
+          nxt = cursor.next(cur, lane);
+          has_next = nxt.e < nsel;
+          if (has_next) issue(nxt, STG ^ 1);
+        } else {
+          has_next = walk.e < nsel;
+          if (has_next) nxt_rows = issue_stream(walk, STG ^ 1);
+        }
+      };
+      if constexpr (FP8) issue_next();
       KOps ko;
       if constexpr (EARLY_OPS) {
         load_k(sb, kbase, ko);
         __builtin_amdgcn_sched_barrier(0);
       }
-      [[maybe_unused]] Tile nxt{};
-      [[maybe_unused]] int nxt_rows = 0;
-      bool has_next;
+      if constexpr (!FP8) issue_next();
       int nvt;  // valid keys of this tile (>= 1)
-      if constexpr (SCALED) {
-        nxt = cursor.next(cur, lane);
-        has_next = nxt.e < nsel;
-        if (has_next) issue(nxt, STG ^ 1);
-        nvt = cur.nv - cur.t0;
-      } else {
-        has_next = walk.e < nsel;
-        if (has_next) nxt_rows = issue_stream(walk, STG ^ 1);
-        nvt = cur_rows;
-      }
+      if constexpr (SCALED) nvt = cur.nv - cur.t0;
+      else nvt = cur_rows;
       const int lim = nvt - 4 * g;
       float cs = p.c;
       float vsc = 1.f;
