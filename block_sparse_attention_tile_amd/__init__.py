@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     BSA_KV_BF16_SCALED,
     BSA_KV_FP8E4M3,
     BSA_MAX_KEY_BLOCKS,
+    BSA_MAX_ORDER_QBLOCKS,
     BSA_OK,
     LSE_EMPTY,
     BsaError,
@@ -26,4 +27,5 @@ from .api import (  # noqa: F401
     bsa_fwd_lut,
     bsa_mask_to_lut,
     bsa_status_str,
+    bsa_unit_order_lut,
 )

@@ -11,7 +11,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsa.so")
 
 # The exported C symbols, as declared in include/bsa.h.
-EXPORTS = ("bsa_fwd_lut", "bsa_fwd_bitmap", "bsa_mask_to_lut",
+EXPORTS = ("bsa_fwd_lut", "bsa_fwd_lut_ordered", "bsa_unit_order_lut",
+           "bsa_fwd_bitmap", "bsa_mask_to_lut",
            "bsa_bwd_workspace_size", "bsa_bwd_lut", "bsa_bwd_bitmap",
            "bsa_codebook_dequant", "bsa_status_str")
 
@@ -34,6 +35,13 @@ def load():
     lib.bsa_fwd_lut.argtypes = [
         P, P, P, i32, P, P, P, P, i32, i64, i64, P, f32, P, P,
         i32, i32, i32, i32, i32, i32, i32, P]
+    lib.bsa_fwd_lut_ordered.restype = ctypes.c_int32
+    lib.bsa_fwd_lut_ordered.argtypes = [
+        P, P, P, i32, P, P, P, P, i32, i64, i64, P, P, f32, P, P,
+        i32, i32, i32, i32, i32, i32, i32, P]
+    lib.bsa_unit_order_lut.restype = ctypes.c_int32
+    lib.bsa_unit_order_lut.argtypes = [
+        P, P, i32, i64, i64, P, P, i32, i32, i32, i32, i32, P]
     lib.bsa_fwd_bitmap.restype = ctypes.c_int32
     lib.bsa_fwd_bitmap.argtypes = [
         P, P, P, i32, P, P, P, i64, i64, P, f32, P, P,

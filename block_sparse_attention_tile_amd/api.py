@@ -33,6 +33,7 @@ BSA_CODEBOOK_I8 = 0
 BSA_CODEBOOK_I4 = 1
 LSE_EMPTY = -3.4028234663852886e38  # BSA_LSE_EMPTY = -FLT_MAX
 BSA_MAX_KEY_BLOCKS = 16384
+BSA_MAX_ORDER_QBLOCKS = 4096
 
 
 class BsaError(RuntimeError):
@@ -216,11 +217,18 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 need_lse: bool = True, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None,
                 k_codebook: Optional[torch.Tensor] = None,
-                v_codebook: Optional[torch.Tensor] = None):
+                v_codebook: Optional[torch.Tensor] = None,
+                balance: bool = True,
+                qblock_order: Optional[torch.Tensor] = None):
     """VSA form.  Returns ``(out, lse)`` (``lse`` is None if not needed).
     ``q`` is ``[B, H, S, D]``, ``k``/``v`` ``[B, Hk, Sk, D]`` (query head h
     reads K/V head h // (H // Hk)).  ``meta_strides=(sb, sh)``: the LUT row
-    of (b, h, qb) is ``b*sb + h*sh + qb``; default one row per unit."""
+    of (b, h, qb) is ``b*sb + h*sh + qb``; default one row per unit.
+    ``balance``: launch each head's query blocks heaviest first (an order
+    computed on the GPU by ``bsa_unit_order_lut``; the outputs are the same
+    bits either way); skipped beyond BSA_MAX_ORDER_QBLOCKS query blocks.
+    ``qblock_order``: an order computed beforehand (int32 ``[B*H*NQ]``, as
+    ``bsa_unit_order_lut`` returns it) to launch with instead."""
     q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
                                               lse, need_lse, block, k_codebook,
                                               v_codebook)
@@ -235,14 +243,61 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 k_scale=ks, v_scale=vs)
     if sm_scale is None:
         sm_scale = 1.0 / (D ** 0.5)
-    rc = _lib.load().bsa_fwd_lut(
+    order = None
+    if qblock_order is not None:
+        order = qblock_order
+        _need_device(q.device, qblock_order=order)
+        if order.dtype != torch.int32 or not order.is_contiguous():
+            raise TypeError("qblock_order must be a contiguous int32 tensor")
+        _need_elems("qblock_order", order, B * H * NQ)
+    elif balance and NQ <= BSA_MAX_ORDER_QBLOCKS:
+        order = torch.empty(B * H * NQ, dtype=torch.int32, device=q.device)
+        rc = _lib.load().bsa_unit_order_lut(
+            _ptr(idx), _ptr(num), int(idx.shape[-1]), int(sb), int(sh),
+            _ptr(vbs), _ptr(order), B, H, S, Sk, int(block), _cur_stream(q))
+        if rc != BSA_OK:
+            raise BsaError(rc)
+    rc = _lib.load().bsa_fwd_lut_ordered(
         _ptr(q), _ptr(k), _ptr(v), kvd, _ptr(ks), _ptr(vs), _ptr(idx),
         _ptr(num), int(idx.shape[-1]), int(sb), int(sh), _ptr(vbs),
-        float(sm_scale), _ptr(out), _ptr(lse), B, H, Hk, S, Sk, D, int(block),
-        _cur_stream(q))
+        _ptr(order), float(sm_scale), _ptr(out), _ptr(lse), B, H, Hk, S, Sk,
+        D, int(block), _cur_stream(q))
     if rc != BSA_OK:
         raise BsaError(rc)
     return out, lse
+
+
+@_on_stream
+def bsa_unit_order_lut(q2k_idx: torch.Tensor, q2k_num: torch.Tensor,
+                       variable_block_sizes: Optional[torch.Tensor] = None, *,
+                       B: int, H: int, S: int, Sk: int, block: int,
+                       meta_strides: Optional[Tuple[int, int]] = None):
+    """Launch order of the LUT-form units: int32 ``[B*H*NQ]``, for every
+    (b, h) its query blocks by decreasing attended-key count (ties by
+    q-block), computed on the GPU."""
+    idx = _i32(q2k_idx)
+    num = _i32(q2k_num)
+    vbs = _i32(variable_block_sizes)
+    if not idx.is_cuda:
+        raise ValueError(f"q2k_idx must be a GPU tensor, got {idx.device}")
+    _need_device(idx.device, q2k_num=num, variable_block_sizes=vbs)
+    NQ = S // block
+    sb, sh = meta_strides if meta_strides is not None else (H * NQ, NQ)
+    if block in (64, 128) and S % block == 0 and Sk % block == 0:
+        rows = _meta_rows(B, H, NQ, int(sb), int(sh))
+        width = int(idx.shape[-1]) if idx.dim() > 0 else 0
+        if width > 0 and idx.numel() // width < rows:
+            raise ValueError(f"q2k_idx has {idx.numel() // width} rows; the "
+                             f"strides address {rows}")
+        _need_elems("q2k_num", num, rows)
+        _need_elems("variable_block_sizes", vbs, Sk // block)
+    order = torch.empty(max(B * H * NQ, 0), dtype=torch.int32, device=idx.device)
+    rc = _lib.load().bsa_unit_order_lut(
+        _ptr(idx), _ptr(num), int(idx.shape[-1]), int(sb), int(sh), _ptr(vbs),
+        _ptr(order), B, H, S, Sk, int(block), _cur_stream(idx))
+    if rc != BSA_OK:
+        raise BsaError(rc)
+    return order
 
 
 @_on_stream

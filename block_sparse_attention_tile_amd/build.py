@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "bsa_fwd.hip"),
            os.path.join(PKG, "csrc", "bsa_mask.hip"),
            os.path.join(PKG, "csrc", "bsa_bwd.hip"),
-           os.path.join(PKG, "csrc", "bsa_codebook.hip")]
+           os.path.join(PKG, "csrc", "bsa_codebook.hip"),
+           os.path.join(PKG, "csrc", "bsa_order.hip")]
 LIB = os.path.join(PKG, "libbsa.so")
 
 HIPCC_FLAGS = [

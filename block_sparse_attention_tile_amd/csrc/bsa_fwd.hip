@@ -72,6 +72,7 @@ struct FwdParams {
   const float* v_scale;
   const int32_t* idx;   // LUT form
   const int32_t* num;   // LUT form
+  const int32_t* order; // LUT form: q-block launch order per (b, h), or null
   const int8_t* mask;   // bitmap form
   int64_t meta_sb;      // metadata row stride per batch (rows)
   int64_t meta_sh;      // metadata row stride per head (rows)
@@ -365,8 +366,9 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
 
   // ---- A1: work unit
   const int u = remap_unit(blockIdx.x, p.n_units);
-  const int qb = u % p.NQ;
   const int bh = u / p.NQ;
+  // the u-th unit in launch order: q-block order, or the given permutation
+  const int qb = p.order ? clampi(p.order[u], 0, p.NQ - 1) : u % p.NQ;
   const int h = bh % p.H;
   const int b = bh / p.H;
   const int64_t plane = (int64_t)bh * p.S * HD;  // element offset of Q/O (b, h)
@@ -789,6 +791,31 @@ FwdParams make_params(const void* q, const void* k, const void* v,
 
 }  // namespace
 
+extern "C" bsa_status bsa_fwd_lut_ordered(
+    const void* q, const void* k, const void* v, int32_t kv_dtype,
+    const float* k_scale, const float* v_scale, const int32_t* q2k_idx,
+    const int32_t* q2k_num, int32_t max_kv, int64_t meta_stride_b,
+    int64_t meta_stride_h, const int32_t* variable_block_sizes,
+    const int32_t* qblock_order, float sm_scale, void* out, float* lse, int32_t B,
+    int32_t H, int32_t Hk, int32_t S, int32_t Sk, int32_t D, int32_t block,
+    void* stream) {
+  bsa_status st = check_common(q, k, v, kv_dtype, k_scale, v_scale, out, B, H,
+                               Hk, S, Sk, D, block);
+  if (st != BSA_OK) return st;
+  if (!q2k_idx || !q2k_num) return BSA_ERR_NULL;
+  if (max_kv < 1 || meta_stride_b < 0 || meta_stride_h < 0) return BSA_ERR_SHAPE;
+  FwdParams p = make_params(q, k, v, k_scale, v_scale, variable_block_sizes,
+                            sm_scale, out, lse, B, H, Hk, S, Sk, block);
+  p.idx = q2k_idx;
+  p.num = q2k_num;
+  p.order = qblock_order;
+  p.max_kv = max_kv;
+  p.meta_sb = meta_stride_b;
+  p.meta_sh = meta_stride_h;
+  return dispatch<false>(p, block, kv_dtype,
+                         (hipStream_t)stream);
+}
+
 extern "C" bsa_status bsa_fwd_lut(const void* q, const void* k, const void* v,
                                   int32_t kv_dtype, const float* k_scale,
                                   const float* v_scale, const int32_t* q2k_idx,
@@ -799,20 +826,10 @@ extern "C" bsa_status bsa_fwd_lut(const void* q, const void* k, const void* v,
                                   int32_t B, int32_t H, int32_t Hk, int32_t S,
                                   int32_t Sk, int32_t D, int32_t block,
                                   void* stream) {
-  bsa_status st = check_common(q, k, v, kv_dtype, k_scale, v_scale, out, B, H,
-                               Hk, S, Sk, D, block);
-  if (st != BSA_OK) return st;
-  if (!q2k_idx || !q2k_num) return BSA_ERR_NULL;
-  if (max_kv < 1 || meta_stride_b < 0 || meta_stride_h < 0) return BSA_ERR_SHAPE;
-  FwdParams p = make_params(q, k, v, k_scale, v_scale, variable_block_sizes,
-                            sm_scale, out, lse, B, H, Hk, S, Sk, block);
-  p.idx = q2k_idx;
-  p.num = q2k_num;
-  p.max_kv = max_kv;
-  p.meta_sb = meta_stride_b;
-  p.meta_sh = meta_stride_h;
-  return dispatch<false>(p, block, kv_dtype,
-                         (hipStream_t)stream);
+  return bsa_fwd_lut_ordered(q, k, v, kv_dtype, k_scale, v_scale, q2k_idx, q2k_num,
+                             max_kv, meta_stride_b, meta_stride_h,
+                             variable_block_sizes, nullptr, sm_scale, out, lse, B, H,
+                             Hk, S, Sk, D, block, stream);
 }
 
 extern "C" bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v,

@@ -1,0 +1,131 @@
+// bsa_order.hip -- work order of the forward launch (look-up-table form).
+//
+// Work units are independent: unit (b, h, qb) computes the same bits
+// whichever workgroup slot runs it and whenever it runs.  Their cost is
+// not equal, though: it grows with the unit's attended keys (the valid keys
+// of its selected key blocks, FastVideo "block_sparse_attn_sm100a.py",
+// `is_supported` docstring: counts in [0, max_kv], keys past a block's
+// `variable_block_sizes` entry masked).  Launched in q-block order, units
+// that happen to be heavy and start late leave a tail in which most slots
+// idle.  This pass orders the q-blocks of every (b, h) by decreasing
+// attended-key count (ties by increasing q-block), so that the forward
+// launch starts its heavy units first and runs units of similar length side
+// by side.  Two kernels:
+//   1. one wave per unit: work = sum over the row's first clamp(num, 0,
+//      max_kv) LUT entries inside [0, NK) of the block's valid keys (a cost
+//      estimate: a repeated entry is counted twice);
+//   2. one workgroup per (b, h): bitonic sort of the NQ 64-bit keys
+//      ((2^32 - 1 - work) << 32 | qb) in LDS, then the q-blocks in key order.
+// The result is deterministic (no atomics) and only affects scheduling.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bsa.h"
+#include "bsa_device.h"
+
+namespace {
+
+struct OrderParams {
+  const int32_t* idx;
+  const int32_t* num;
+  int32_t max_kv;
+  int64_t meta_sb;
+  int64_t meta_sh;
+  const int32_t* vbs;  // [NK] or null
+  int32_t* order;      // [B*H*NQ]: work after kernel 1, q-blocks after kernel 2
+  int32_t H;
+  int32_t NQ;
+  int32_t NK;
+  int32_t block;
+  int32_t n_units;
+};
+
+__global__ __launch_bounds__(256) void unit_work_kernel(OrderParams p) {
+  const int lane = threadIdx.x & 63;
+  const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (u >= p.n_units) return;
+  const int qb = u % p.NQ;
+  const int bh = u / p.NQ;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int64_t row = (int64_t)b * p.meta_sb + (int64_t)h * p.meta_sh + qb;
+  const int n = clampi(p.num[row], 0, p.max_kv);
+  const int32_t* irow = p.idx + row * p.max_kv;
+  int w = 0;
+  for (int j = lane; j < n; j += 64) {
+    const int kb = irow[j];
+    if (kb >= 0 && kb < p.NK) w += p.vbs ? clampi(p.vbs[kb], 0, p.block) : p.block;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o);
+  if (lane == 0) p.order[u] = w;
+}
+
+// np: NQ rounded up to a power of two (>= 2); LDS holds np 64-bit keys.
+__global__ __launch_bounds__(256) void unit_sort_kernel(OrderParams p, int np) {
+  extern __shared__ __attribute__((aligned(16))) uint64_t keys[];
+  int32_t* ord = p.order + (int64_t)blockIdx.x * p.NQ;
+  for (int i = threadIdx.x; i < np; i += 256)
+    keys[i] = i < p.NQ ? ((uint64_t)(0xFFFFFFFFu - (uint32_t)ord[i]) << 32) | (uint32_t)i
+                       : ~0ull;
+  __syncthreads();
+  for (int k = 2; k <= np; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < np; i += 256) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t a = keys[i], c = keys[ixj];
+          const bool ascending = (i & k) == 0;
+          if ((a > c) == ascending) {
+            keys[i] = c;
+            keys[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < p.NQ; i += 256) ord[i] = (int32_t)(uint32_t)keys[i];
+}
+
+}  // namespace
+
+extern "C" bsa_status bsa_unit_order_lut(const int32_t* q2k_idx, const int32_t* q2k_num,
+                                         int32_t max_kv, int64_t meta_stride_b,
+                                         int64_t meta_stride_h,
+                                         const int32_t* variable_block_sizes,
+                                         int32_t* order, int32_t B, int32_t H, int32_t S,
+                                         int32_t Sk, int32_t block, void* stream) {
+  if (!q2k_idx || !q2k_num || !order) return BSA_ERR_NULL;
+  if (B <= 0 || H <= 0 || S <= 0 || Sk <= 0 || block <= 0) return BSA_ERR_SHAPE;
+  if (S % block != 0 || Sk % block != 0) return BSA_ERR_SHAPE;
+  if (max_kv < 1 || meta_stride_b < 0 || meta_stride_h < 0) return BSA_ERR_SHAPE;
+  if (block != 64 && block != 128) return BSA_ERR_UNSUPPORTED;
+  const int NQ = S / block;
+  if (NQ > BSA_MAX_ORDER_QBLOCKS || Sk / block > BSA_MAX_KEY_BLOCKS)
+    return BSA_ERR_UNSUPPORTED;
+  const int64_t units = (int64_t)B * H * NQ;
+  if (units > INT32_MAX) return BSA_ERR_UNSUPPORTED;
+  OrderParams p{};
+  p.idx = q2k_idx;
+  p.num = q2k_num;
+  p.max_kv = max_kv;
+  p.meta_sb = meta_stride_b;
+  p.meta_sh = meta_stride_h;
+  p.vbs = variable_block_sizes;
+  p.order = order;
+  p.H = H;
+  p.NQ = NQ;
+  p.NK = Sk / block;
+  p.block = block;
+  p.n_units = (int32_t)units;
+  int np = 2;
+  while (np < NQ) np <<= 1;
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(unit_work_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, p);
+  if (hipGetLastError() != hipSuccess) return BSA_ERR_HIP;
+  hipLaunchKernelGGL(unit_sort_kernel, dim3((unsigned)(B * H)), dim3(256),
+                     (size_t)np * sizeof(uint64_t), s, p, np);
+  return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}

@@ -53,6 +53,10 @@ extern "C" {
  * one 32-bit list entry per key block per work unit). */
 #define BSA_MAX_KEY_BLOCKS 16384
 
+/* Largest number of query blocks S/block per (batch, head) that
+ * bsa_unit_order_lut sorts (LDS holds one 64-bit key per query block). */
+#define BSA_MAX_ORDER_QBLOCKS 4096
+
 typedef enum {
   BSA_OK = 0,
   BSA_ERR_NULL = 1,        /* a required pointer is NULL                      */
@@ -130,6 +134,61 @@ bsa_status bsa_fwd_lut(const void* q, const void* k, const void* v,
                        void* out, float* lse, int32_t B, int32_t H, int32_t Hk,
                        int32_t S, int32_t Sk, int32_t D, int32_t block,
                        void* stream);
+
+/*
+ * bsa_unit_order_lut -- launch order of the LUT-form work units.  Not an
+ * operation of the pages: a scheduling aid for the forward launch.  For
+ * every (b, h) it writes the permutation of the S/block query blocks by
+ * decreasing attended-key count, ties by increasing query block, so that
+ * bsa_fwd_lut_ordered starts its heavy units first and finishes on light
+ * ones.  The count of unit (b, h, qb) is the sum, over its row's first
+ * clamp(q2k_num, 0, max_kv) entries inside [0, Sk/block), of the entry's
+ * valid keys (variable_block_sizes clamped to [0, block]; repeated entries
+ * count twice: an estimate, exact for rows without repetitions).
+ *
+ *  q2k_idx, q2k_num, max_kv, meta_stride_b, meta_stride_h,
+ *  variable_block_sizes, B, H, S, Sk, block
+ *               exactly as for bsa_fwd_lut.
+ *  order        int32 [B*H*(S/block)], device memory, written in full:
+ *               entry (b*H + h)*(S/block) + i is the i-th query block of
+ *               (b, h) in launch order.
+ *  stream       hipStream_t (void*), NULL = null stream.
+ *
+ * Deterministic.  Errors: BSA_ERR_NULL, BSA_ERR_SHAPE (sizes, strides,
+ * max_kv as for bsa_fwd_lut), BSA_ERR_UNSUPPORTED (block not 64/128,
+ * S/block > BSA_MAX_ORDER_QBLOCKS, too many key blocks), BSA_ERR_HIP; on
+ * error nothing is launched.
+ */
+bsa_status bsa_unit_order_lut(const int32_t* q2k_idx, const int32_t* q2k_num,
+                              int32_t max_kv, int64_t meta_stride_b,
+                              int64_t meta_stride_h,
+                              const int32_t* variable_block_sizes,
+                              int32_t* order, int32_t B, int32_t H, int32_t S,
+                              int32_t Sk, int32_t block, void* stream);
+
+/*
+ * bsa_fwd_lut_ordered -- bsa_fwd_lut with the work units launched in a
+ * given order.  Arguments as bsa_fwd_lut, plus:
+ *
+ *  qblock_order int32 [B*H*(S/block)], device memory: for every (b, h), a
+ *               permutation of 0 .. S/block - 1 (bsa_unit_order_lut writes
+ *               one); NULL = q-block order, i.e. bsa_fwd_lut.  Entries
+ *               outside [0, S/block) are clamped into it; an order that is
+ *               not a permutation leaves some query blocks unwritten.
+ *
+ * Every unit computes the same bits in any order, so the outputs equal
+ * bsa_fwd_lut's exactly.
+ */
+bsa_status bsa_fwd_lut_ordered(const void* q, const void* k, const void* v,
+                               int32_t kv_dtype, const float* k_scale,
+                               const float* v_scale, const int32_t* q2k_idx,
+                               const int32_t* q2k_num, int32_t max_kv,
+                               int64_t meta_stride_b, int64_t meta_stride_h,
+                               const int32_t* variable_block_sizes,
+                               const int32_t* qblock_order, float sm_scale,
+                               void* out, float* lse, int32_t B, int32_t H,
+                               int32_t Hk, int32_t S, int32_t Sk, int32_t D,
+                               int32_t block, void* stream);
 
 /*
  * bsa_fwd_bitmap -- Jenga (bitmap) form.  Arguments as bsa_fwd_lut, except:

@@ -38,6 +38,8 @@ def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define BSA_MAX_KEY_BLOCKS (\d+)", text).group(1)) == \
         api.BSA_MAX_KEY_BLOCKS
+    assert int(re.search(r"#define BSA_MAX_ORDER_QBLOCKS (\d+)", text).group(1)) == \
+        api.BSA_MAX_ORDER_QBLOCKS
     for name in ("OK", "ERR_NULL", "ERR_SHAPE", "ERR_UNSUPPORTED", "ERR_ALIGN",
                  "ERR_HIP", "KV_BF16", "KV_FP8E4M3", "KV_BF16_SCALED",
                  "CODEBOOK_I8", "CODEBOOK_I4"):
@@ -62,6 +64,21 @@ def lut(**over):
                 Hk=1, S=512, Sk=512, D=128, block=64, stream=None)
     args.update(over)
     return _lib.load().bsa_fwd_lut(*args.values())
+
+
+def lut_ordered(**over):
+    args = dict(q=A, k=A, v=A, kv=0, ks=None, vs=None, idx=A, num=A, max_kv=4,
+                sb=8, sh=8, vbs=None, order=None, scale=0.1, out=A, lse=None,
+                B=1, H=1, Hk=1, S=512, Sk=512, D=128, block=64, stream=None)
+    args.update(over)
+    return _lib.load().bsa_fwd_lut_ordered(*args.values())
+
+
+def unit_order(**over):
+    args = dict(idx=A, num=A, max_kv=4, sb=8, sh=8, vbs=None, order=A, B=1,
+                H=1, S=512, Sk=512, block=64, stream=None)
+    args.update(over)
+    return _lib.load().bsa_unit_order_lut(*args.values())
 
 
 def bitmap(**over):
@@ -101,6 +118,27 @@ def bitmap(**over):
 ])
 def test_lut_rejects_invalid_static_arguments(over, status):
     assert lut(**over) == status
+    # the ordered entry point validates identically (order = NULL or not)
+    assert lut_ordered(**over) == status
+    assert lut_ordered(order=A, **over) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(idx=None), api.BSA_ERR_NULL),
+    (dict(num=None), api.BSA_ERR_NULL),
+    (dict(order=None), api.BSA_ERR_NULL),
+    (dict(B=0), api.BSA_ERR_SHAPE),
+    (dict(H=0), api.BSA_ERR_SHAPE),
+    (dict(S=500), api.BSA_ERR_SHAPE),
+    (dict(Sk=96), api.BSA_ERR_SHAPE),
+    (dict(max_kv=0), api.BSA_ERR_SHAPE),
+    (dict(sh=-1), api.BSA_ERR_SHAPE),
+    (dict(block=32), api.BSA_ERR_UNSUPPORTED),
+    (dict(S=64 * (api.BSA_MAX_ORDER_QBLOCKS + 1)), api.BSA_ERR_UNSUPPORTED),
+    (dict(Sk=64 * 16385), api.BSA_ERR_UNSUPPORTED),
+])
+def test_unit_order_rejects_invalid_static_arguments(over, status):
+    assert unit_order(**over) == status
 
 
 @pytest.mark.parametrize("over,status", [

@@ -1,0 +1,179 @@
+"""GPU tests of the launch order of LUT-form units (bsa_unit_order_lut) and
+of the ordered forward entry point: the order is exactly the host's stable
+sort of the attended-key counts, and the forward outputs are bit-identical
+with and without it (each unit computes the same bits in any order)."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_tile_amd as bsa
+import workloads
+from tests.gpu_helpers import log, run_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def expected_order(w) -> np.ndarray:
+    """Host reference of the order: per (b, h), q-blocks by decreasing
+    count (sum of the valid keys of the row's first clamp(num) in-range
+    entries, repeats counted), ties by increasing q-block."""
+    NQ, NK, B, H = w.NQ, w.NK, w.B, w.H
+    idx = w.q2k_idx.numpy().reshape(-1, w.q2k_idx.shape[-1])
+    num = w.q2k_num.numpy().reshape(-1)
+    max_kv = idx.shape[1]
+    vbs = (np.full(NK, w.block) if w.vbs is None
+           else np.clip(w.vbs.numpy(), 0, w.block))
+    sb, sh = w.meta_strides
+    out = np.empty(B * H * NQ, dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            work = []
+            for qb in range(NQ):
+                row = b * sb + h * sh + qb
+                n = int(np.clip(num[row], 0, max_kv))
+                e = idx[row, :n]
+                e = e[(e >= 0) & (e < NK)]
+                work.append(int(vbs[e].sum()))
+            o = sorted(range(NQ), key=lambda i: (-work[i], i))
+            out[(b * H + h) * NQ:(b * H + h + 1) * NQ] = o
+    return out
+
+
+def gpu_order(w, d):
+    o = bsa.bsa_unit_order_lut(d["q2k_idx"], d["q2k_num"], d["vbs"], B=w.B,
+                               H=w.H, S=w.S, Sk=w.Sk, block=w.block,
+                               meta_strides=w.meta_strides)
+    torch.cuda.synchronize()
+    return o.cpu().numpy()
+
+
+CASES = [
+    ("rand_lut64", dict(seed=301, B=2, H=3, S=64 * 37, block=64,
+                        count_mode="uniform", vbs_mode="random")),
+    ("rand_lut128_shared", dict(seed=302, B=2, H=2, S=128 * 20, block=128,
+                                shared_meta=True, count_mode="uniform",
+                                vbs_mode="partial")),
+    ("rand_lut64_garbage", dict(seed=303, B=1, H=2, S=64 * 9, block=64,
+                                count_mode="uniform", pad_value=2**31 - 1)),
+    ("rand_lut64_one_qblock", dict(seed=304, B=2, H=2, S=64, block=64,
+                                   count_mode="uniform")),
+]
+
+
+@pytest.mark.parametrize("label,kw", CASES, ids=[c[0] for c in CASES])
+def test_order_matches_host_sort(label, kw):
+    w = workloads.make_random(**kw)
+    if label == "rand_lut64_garbage":
+        # below the count: entries out of range (skipped) and repeats
+        # (counted twice by the estimate)
+        idx, num = w.q2k_idx, w.q2k_num
+        for r in range(idx.shape[0]):
+            if num[r] >= 3 and r % 3 == 0:
+                idx[r, 0] = w.NK + 3
+                idx[r, 1] = -5
+            elif num[r] >= 3 and r % 3 == 1:
+                idx[r, 2] = idx[r, 1]
+    log(f"[order] {label}: B={w.B} H={w.H} S={w.S} block={w.block}")
+    d = to_dev(w)
+    assert np.array_equal(gpu_order(w, d), expected_order(w))
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_order_matches_host_sort_full_configs(cfg):
+    w = workloads.make_config(cfg)
+    log(f"[order] {w.name}")
+    d = to_dev(w)
+    assert np.array_equal(gpu_order(w, d), expected_order(w))
+
+
+def test_order_at_the_query_block_limit():
+    S = 64 * bsa.BSA_MAX_ORDER_QBLOCKS
+    w = workloads.make_random(seed=305, B=1, H=1, S=S, block=64, max_kv=4,
+                              count_mode="uniform", vbs_mode="random")
+    log(f"[order] NQ = {w.NQ}")
+    d = to_dev(w)
+    assert np.array_equal(gpu_order(w, d), expected_order(w))
+
+
+FWD_CASES = [
+    ("rand_lut64", dict(seed=311, B=2, H=3, S=64 * 37, block=64,
+                        count_mode="uniform", vbs_mode="random")),
+    ("rand_lut128", dict(seed=312, B=1, H=3, S=128 * 21, block=128,
+                         count_mode="uniform", vbs_mode="partial")),
+    ("rand_lut64_shared_gqa", dict(seed=313, B=2, H=4, Hk=2, S=64 * 12,
+                                   block=64, shared_meta=True,
+                                   count_mode="uniform")),
+]
+
+
+@pytest.mark.parametrize("label,kw", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_ordered_forward_is_bitwise_the_unordered_one(label, kw):
+    w = workloads.make_random(**kw)
+    log(f"[order-fwd] {label}")
+    d = to_dev(w)
+    outs = []
+    for balance in (False, True):
+        out = torch.full(tuple(w.q.shape), float("nan"), dtype=torch.bfloat16,
+                         device="cuda")
+        lse = torch.full((w.B, w.H, w.S), float("nan"), dtype=torch.float32,
+                         device="cuda")
+        bsa.bsa_fwd_lut(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"],
+                        d["vbs"], block=w.block, sm_scale=w.sm_scale,
+                        meta_strides=w.meta_strides, out=out, lse=lse,
+                        balance=balance)
+        torch.cuda.synchronize()
+        outs.append((out, lse))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_ordered_forward_full_configs(cfg):
+    w = workloads.make_config(cfg)
+    log(f"[order-fwd] {w.name}")
+    d = to_dev(w)
+    a = run_gpu(w, dev_inputs=d)  # the binding orders by default
+    out = torch.empty(tuple(w.q.shape), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda")
+    bsa.bsa_fwd_lut(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"],
+                    d["vbs"], block=w.block, sm_scale=w.sm_scale,
+                    meta_strides=w.meta_strides, out=out, lse=lse,
+                    balance=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], out) and torch.equal(a[1], lse)
+
+
+def test_out_of_range_order_entries_are_clamped():
+    """Entries past NQ clamp to the last query block: every unit then
+    computes that block (the same bits), which must match the reference."""
+    w = workloads.make_random(seed=321, B=1, H=2, S=64 * 6, block=64,
+                              count_mode="uniform", vbs_mode="random")
+    d = to_dev(w)
+    ref, ref_lse = run_gpu(w, dev_inputs=d)
+    order = torch.full((w.B * w.H * w.NQ,), w.NQ + 7, dtype=torch.int32,
+                       device="cuda")
+    out = torch.zeros(tuple(w.q.shape), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((w.B, w.H, w.S), dtype=torch.float32, device="cuda")
+    from block_sparse_attention_tile_amd import _lib
+    from block_sparse_attention_tile_amd.api import _cur_stream, _ptr
+    idx = d["q2k_idx"].to(torch.int32).contiguous()
+    num = d["q2k_num"].to(torch.int32).contiguous()
+    vbs = d["vbs"].to(torch.int32).contiguous()
+    sb, sh = w.meta_strides
+    rc = _lib.load().bsa_fwd_lut_ordered(
+        _ptr(d["q"]), _ptr(d["k"]), _ptr(d["v"]), 0, None, None, _ptr(idx),
+        _ptr(num), int(idx.shape[-1]), int(sb), int(sh), _ptr(vbs),
+        _ptr(order), float(w.sm_scale), _ptr(out), _ptr(lse), w.B, w.H, w.H,
+        w.S, w.S, 128, w.block, _cur_stream(d["q"]))
+    assert rc == bsa.BSA_OK
+    torch.cuda.synchronize()
+    last = slice((w.NQ - 1) * w.block, w.NQ * w.block)
+    assert torch.equal(out[:, :, last], ref[:, :, last])
+    assert torch.equal(lse[:, :, last], ref_lse[:, :, last])
