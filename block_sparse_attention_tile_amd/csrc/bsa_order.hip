@@ -14,8 +14,8 @@
 //   1. one wave per unit: work = sum over the row's first clamp(num, 0,
 //      max_kv) LUT entries inside [0, NK) of the block's valid keys (a cost
 //      estimate: a repeated entry is counted twice);
-//   2. one workgroup per (b, h): bitonic sort of the NQ 64-bit keys
-//      ((2^32 - 1 - work) << 32 | qb) in LDS, then the q-blocks in key order.
+//   2. one workgroup per (b, h): each q-block's position is the rank of its
+//      64-bit key ((2^32 - 1 - work) << 32 | qb) among the NQ keys in LDS.
 // The result is deterministic (no atomics) and only affects scheduling.
 
 #include <hip/hip_runtime.h>
@@ -62,31 +62,36 @@ __global__ __launch_bounds__(256) void unit_work_kernel(OrderParams p) {
   if (lane == 0) p.order[u] = w;
 }
 
-// np: NQ rounded up to a power of two (>= 2); LDS holds np 64-bit keys.
-__global__ __launch_bounds__(256) void unit_sort_kernel(OrderParams p, int np) {
+// One workgroup per (b, h): the keys ((2^32 - 1 - work) << 32 | qb) are
+// distinct, so the position of q-block qb in the order is the number of
+// keys below its own; every thread ranks its keys against all NQ keys in
+// LDS (each step reads one key that every lane reads: a broadcast).
+constexpr int SORT_THREADS = 1024;
+static_assert(BSA_MAX_ORDER_QBLOCKS % SORT_THREADS == 0, "keys per thread");
+
+__global__ __launch_bounds__(SORT_THREADS) void unit_sort_kernel(OrderParams p) {
   extern __shared__ __attribute__((aligned(16))) uint64_t keys[];
   int32_t* ord = p.order + (int64_t)blockIdx.x * p.NQ;
-  for (int i = threadIdx.x; i < np; i += 256)
-    keys[i] = i < p.NQ ? ((uint64_t)(0xFFFFFFFFu - (uint32_t)ord[i]) << 32) | (uint32_t)i
-                       : ~0ull;
-  __syncthreads();
-  for (int k = 2; k <= np; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < np; i += 256) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t a = keys[i], c = keys[ixj];
-          const bool ascending = (i & k) == 0;
-          if ((a > c) == ascending) {
-            keys[i] = c;
-            keys[ixj] = a;
-          }
-        }
-      }
-      __syncthreads();
+  const int n = p.NQ;
+  uint64_t mine[BSA_MAX_ORDER_QBLOCKS / SORT_THREADS];
+#pragma unroll
+  for (int t = 0; t < BSA_MAX_ORDER_QBLOCKS / SORT_THREADS; ++t) {
+    const int i = threadIdx.x + t * SORT_THREADS;
+    if (i < n) {
+      mine[t] = ((uint64_t)(0xFFFFFFFFu - (uint32_t)ord[i]) << 32) | (uint32_t)i;
+      keys[i] = mine[t];
     }
   }
-  for (int i = threadIdx.x; i < p.NQ; i += 256) ord[i] = (int32_t)(uint32_t)keys[i];
+  __syncthreads();  // every work value is read before any position is written
+#pragma unroll
+  for (int t = 0; t < BSA_MAX_ORDER_QBLOCKS / SORT_THREADS; ++t) {
+    const int i = threadIdx.x + t * SORT_THREADS;
+    if (i < n) {
+      int rank = 0;
+      for (int j = 0; j < n; ++j) rank += keys[j] < mine[t] ? 1 : 0;
+      ord[rank] = (int32_t)(uint32_t)mine[t];
+    }
+  }
 }
 
 }  // namespace
@@ -120,12 +125,10 @@ extern "C" bsa_status bsa_unit_order_lut(const int32_t* q2k_idx, const int32_t* 
   p.NK = Sk / block;
   p.block = block;
   p.n_units = (int32_t)units;
-  int np = 2;
-  while (np < NQ) np <<= 1;
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(unit_work_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, p);
   if (hipGetLastError() != hipSuccess) return BSA_ERR_HIP;
-  hipLaunchKernelGGL(unit_sort_kernel, dim3((unsigned)(B * H)), dim3(256),
-                     (size_t)np * sizeof(uint64_t), s, p, np);
+  hipLaunchKernelGGL(unit_sort_kernel, dim3((unsigned)(B * H)), dim3(SORT_THREADS),
+                     (size_t)NQ * sizeof(uint64_t), s, p);
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
