@@ -21,7 +21,10 @@
 //                       forward pass (32-row tiles cut from the stream of
 //                       the unit's valid keys); dQ accumulates in registers
 //                       and is written once.
-//   4. dkdv_kernel      one workgroup per (b, K/V head, key block): its keys
+//   4. dkdv_kernel      one workgroup per (b, K/V head, key block), launched
+//                       heaviest first per K/V head (kunit_work_kernel and
+//                       the rank pass order them; dq_kernel's units are
+//                       ordered likewise with the LUT form): its keys
 //                       stay in registers while it walks every query unit
 //                       that attends the block (from the byte map), so dK and
 //                       dV are complete in one workgroup -- grouped query
@@ -36,6 +39,9 @@
 
 #include "bsa.h"
 #include "bsa_device.h"
+
+// launch-order ranking of work values, in bsa_order.hip
+bsa_status bsa_rank_runs(int32_t* order, int32_t groups, int32_t n, hipStream_t stream);
 
 namespace {
 
@@ -52,6 +58,8 @@ struct BwdParams {
   const int32_t* num;
   const int8_t* mask;   // bitmap form
   const int8_t* k2q;    // [B*Hk*NK, G*NQ]
+  const int32_t* order; // LUT form: q-block launch order of dq per (b, h), or null
+  const int32_t* korder; // key-block launch order of dk/dv per (b, K/V head), or null
   int64_t meta_sb, meta_sh;
   const int32_t* vbs;
   uint16_t* dq;
@@ -138,6 +146,36 @@ __global__ __launch_bounds__(256) void k2q_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // Shared pieces of the two gradient kernels.
 
+// dK/dV launch order, pass 1: the work of key-block unit u = (b*Hk + kvh)*NK
+// + kb is the number of query units set in its map row (0 for a block with
+// no valid key); bsa_rank_runs then orders each (b, K/V head) heaviest
+// first.  One wave per unit.
+__global__ __launch_bounds__(256) void kunit_work_kernel(BwdParams p, int32_t* work,
+                                                         int32_t n_kunits) {
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (u >= n_kunits) return;
+  const int kb = (int)(u % p.NK);
+  const int64_t gq = (int64_t)p.group * p.NQ;
+  const uint8_t* row = (const uint8_t*)p.k2q + u * gq;
+  int c = 0;
+  if (!p.vbs || p.vbs[kb] > 0) {
+    if ((gq & 3) == 0) {  // rows 4-byte aligned: the map starts 256-aligned
+      const uint32_t* w4 = (const uint32_t*)row;
+      for (int64_t i = lane; i < gq / 4; i += 64) {
+        const uint32_t x = w4[i];
+        c += ((x & 0xFFu) != 0) + ((x & 0xFF00u) != 0) + ((x & 0xFF0000u) != 0) +
+             ((x & 0xFF000000u) != 0);
+      }
+    } else {
+      for (int64_t i = lane; i < gq; i += 64) c += row[i] != 0;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if (lane == 0) work[u] = c;
+}
+
 // Ascending list of the set entries of an LDS byte map of n entries, each
 // entry stored as (index << 8) | payload, payload = map byte.  One wave.
 __device__ __forceinline__ int compact_list(const uint8_t* map, int n,
@@ -217,8 +255,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
   uint32_t* list = (uint32_t*)(bmp + ((NK + 15) & ~15));
 
   const int u = remap_unit(blockIdx.x, p.n_units);
-  const int qb = u % p.NQ;
   const int bh = u / p.NQ;
+  // the u-th unit in launch order (heaviest first with the LUT form)
+  const int qb = p.order ? clampi(p.order[u], 0, p.NQ - 1) : u % p.NQ;
   const int h = bh % p.H;
   const int b = bh / p.H;
   const int64_t plane = (int64_t)bh * p.S * HD;
@@ -429,15 +468,16 @@ __global__ __launch_bounds__(BLK * 4, 2) void dkdv_kernel(BwdParams p) {
   uint32_t* list = (uint32_t*)(map + ((gq + 15) & ~15));
 
   const int u = remap_unit(blockIdx.x, p.n_units);  // units = B*Hk*NK here
-  const int kb = u % p.NK;
   const int bkv = u / p.NK;                         // b*Hk + kvh
+  // the u-th unit in launch order (heaviest key blocks of the head first)
+  const int kb = p.korder ? clampi(p.korder[u], 0, p.NK - 1) : u % p.NK;
   const int kvh = bkv % p.Hk;
   const int b = bkv / p.Hk;
   const int64_t kvplane = (int64_t)bkv * p.Sk * HD;
   const int nv = block_valid<BLK>(p.vbs, kb);
   const int key = wave * 16 + r16;  // this lane's key within the block (output)
 
-  const int8_t* mrow = p.k2q + (int64_t)u * gq;
+  const int8_t* mrow = p.k2q + ((int64_t)bkv * p.NK + kb) * gq;  // this block's map row
   for (int i = tid; i < gq; i += NT) map[i] = (uint8_t)mrow[i];
   __syncthreads();
   if (wave == 0) {
@@ -657,9 +697,24 @@ size_t delta_bytes(int64_t B, int64_t H, int64_t S) {
   return (size_t)(B * H * S) * sizeof(float);
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t map_offset(int64_t B, int64_t H, int64_t S) { return align256(delta_bytes(B, H, S)); }
+
+size_t order_offset(int64_t B, int64_t H, int64_t S, int64_t Sk, int64_t block) {
+  return align256(map_offset(B, H, S) + map_bytes(B, H, S, Sk, block));
+}
+
+size_t korder_offset(int64_t B, int64_t H, int64_t S, int64_t Sk, int64_t block) {
+  return align256(order_offset(B, H, S, Sk, block) +
+                  (size_t)(B * H * (S / block)) * sizeof(int32_t));
+}
+
 size_t workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t Sk, int64_t block) {
-  // delta, then the byte map, 256-byte aligned
-  return ((delta_bytes(B, H, S) + 255) & ~(size_t)255) + map_bytes(B, H, S, Sk, block);
+  // delta, the byte map, the dq and the dk/dv launch orders (the latter
+  // sized for H >= Hk K/V heads), each 256-byte aligned
+  return korder_offset(B, H, S, Sk, block) +
+         (size_t)(B * H * (Sk / block)) * sizeof(int32_t);
 }
 
 bsa_status check_bwd(const void* q, const void* k, const void* v, const void* out,
@@ -686,7 +741,18 @@ bsa_status check_bwd(const void* q, const void* k, const void* v, const void* ou
 
 template <int BLK, bool BITMAP>
 bsa_status run_bwd(BwdParams p, const void* out, float* delta, int8_t* map,
-                   size_t nmap, hipStream_t st) {
+                   size_t nmap, int32_t* order, int32_t* korder, int32_t B,
+                   hipStream_t st) {
+  // LUT form: dq units launched heaviest first within each (b, h), as the
+  // forward pass does (same order pass; no effect on the result)
+  p.order = nullptr;
+  if (!BITMAP && p.NQ <= BSA_MAX_ORDER_QBLOCKS) {
+    const bsa_status os = bsa_unit_order_lut(p.idx, p.num, p.max_kv, p.meta_sb, p.meta_sh,
+                                             p.vbs, order, B, p.H, p.S, p.Sk,
+                                             p.S / p.NQ, (void*)st);
+    if (os != BSA_OK) return os;
+    p.order = order;
+  }
   const int64_t rows = (int64_t)p.n_units * BLK;  // B*H*S
   hipLaunchKernelGGL(delta_kernel, dim3((uint32_t)((rows + 15) / 16)), dim3(256), 0, st,
                      (const uint16_t*)out, p.dout, delta, rows);
@@ -719,6 +785,15 @@ bsa_status run_bwd(BwdParams p, const void* out, float* delta, int8_t* map,
       return BSA_ERR_HIP;
     BwdParams pk = p;
     pk.n_units = (int32_t)((int64_t)p.n_units / p.H * p.Hk / p.NQ * p.NK);
+    // key blocks of each (b, K/V head) launched heaviest first
+    pk.korder = nullptr;
+    if (p.NK <= BSA_MAX_ORDER_QBLOCKS) {
+      hipLaunchKernelGGL(kunit_work_kernel, dim3((uint32_t)((pk.n_units + 3) / 4)),
+                         dim3(256), 0, st, pk, korder, pk.n_units);
+      const bsa_status rs = bsa_rank_runs(korder, pk.n_units / p.NK, p.NK, st);
+      if (rs != BSA_OK) return rs;
+      pk.korder = korder;
+    }
     hipLaunchKernelGGL(kern, dim3(pk.n_units), dim3(BLK * 4), lds, st, pk);
   }
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
@@ -759,10 +834,13 @@ bsa_status dispatch_bwd(const BwdParams& p, int block, const void* out, void* ws
   const size_t need = workspace_bytes(B, H, S, Sk, block);
   if (ws_bytes < need) return BSA_ERR_SHAPE;
   float* delta = (float*)ws;
-  int8_t* map = (int8_t*)ws + ((delta_bytes(B, H, S) + 255) & ~(size_t)255);
+  int8_t* map = (int8_t*)ws + map_offset(B, H, S);
   const size_t nmap = map_bytes(B, H, S, Sk, block);
-  if (block == 64) return run_bwd<64, BITMAP>(p, out, delta, map, nmap, st);
-  return run_bwd<128, BITMAP>(p, out, delta, map, nmap, st);
+  int32_t* order = (int32_t*)((char*)ws + order_offset(B, H, S, Sk, block));
+  int32_t* korder = (int32_t*)((char*)ws + korder_offset(B, H, S, Sk, block));
+  if (block == 64)
+    return run_bwd<64, BITMAP>(p, out, delta, map, nmap, order, korder, B, st);
+  return run_bwd<128, BITMAP>(p, out, delta, map, nmap, order, korder, B, st);
 }
 
 }  // namespace

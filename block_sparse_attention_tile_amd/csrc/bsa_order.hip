@@ -96,6 +96,22 @@ __global__ __launch_bounds__(SORT_THREADS) void unit_sort_kernel(OrderParams p) 
 
 }  // namespace
 
+// Library-internal (not part of the C ABI): replaces each of `groups`
+// consecutive runs of `n` work values in `order` by the permutation of its
+// indices in decreasing work, ties by index (the rank kernel above);
+// n <= BSA_MAX_ORDER_QBLOCKS.  Used for the backward pass's units.
+__attribute__((visibility("hidden"))) bsa_status bsa_rank_runs(int32_t* order,
+                                                                int32_t groups,
+                                                                int32_t n,
+                                                                hipStream_t stream) {
+  OrderParams p{};
+  p.order = order;
+  p.NQ = n;
+  hipLaunchKernelGGL(unit_sort_kernel, dim3((unsigned)groups), dim3(SORT_THREADS),
+                     (size_t)n * sizeof(uint64_t), stream, p);
+  return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
 extern "C" bsa_status bsa_unit_order_lut(const int32_t* q2k_idx, const int32_t* q2k_num,
                                          int32_t max_kv, int64_t meta_stride_b,
                                          int64_t meta_stride_h,

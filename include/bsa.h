@@ -257,9 +257,11 @@ bsa_status bsa_mask_to_lut(const int8_t* mask, int64_t rows, int32_t nk,
  *               aligned; every element is written.
  *  workspace    device memory of at least bsa_bwd_workspace_size(...) bytes,
  *               256-byte aligned, owned by the caller, free for the library
- *               to overwrite during the call (it holds delta and the
- *               key-block -> query-block selection map).  Calls that overlap
- *               on the same workspace race.
+ *               to overwrite during the call (it holds delta, the
+ *               key-block -> query-block selection map and the launch
+ *               orders of the dq units -- LUT form, as bsa_unit_order_lut
+ *               computes it -- and of the dk/dv units: heaviest first).
+ *               Calls that overlap on the same workspace race.
  *  workspace_bytes  its size; a smaller value is BSA_ERR_SHAPE.
  *
  * Errors as the forward calls (plus BSA_ERR_UNSUPPORTED when (H/Hk)*S/block

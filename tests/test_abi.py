@@ -211,11 +211,13 @@ def bwd_lut(**over):
     return _lib.load().bsa_bwd_lut(*args.values())
 
 
-def test_bwd_workspace_size_covers_delta_and_map():
+def test_bwd_workspace_size_covers_delta_map_and_order():
     lib = _lib.load()
-    # delta: B*H*S floats (256-aligned), map: B*H*NQ*NK bytes
+    # delta: B*H*S floats, map: B*H*NQ*NK bytes, launch orders: B*H*NQ and
+    # B*H*NK int32; each region 256-aligned
+    up = lambda x: (x + 255) // 256 * 256
     assert lib.bsa_bwd_workspace_size(2, 3, 512, 1024, 64) == \
-        ((2 * 3 * 512 * 4 + 255) // 256) * 256 + 2 * 3 * 8 * 16
+        up(up(up(2 * 3 * 512 * 4) + 2 * 3 * 8 * 16) + 2 * 3 * 8 * 4) + 2 * 3 * 16 * 4
     assert lib.bsa_bwd_workspace_size(0, 3, 512, 512, 64) == 0
 
 

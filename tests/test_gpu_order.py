@@ -177,3 +177,33 @@ def test_out_of_range_order_entries_are_clamped():
     last = slice((w.NQ - 1) * w.block, w.NQ * w.block)
     assert torch.equal(out[:, :, last], ref[:, :, last])
     assert torch.equal(lse[:, :, last], ref_lse[:, :, last])
+
+
+def test_ordered_backward_is_bitwise_the_unordered_bitmap_form():
+    """The LUT-form backward launches its dq units heaviest first; the
+    bitmap form on the same selection keeps the q-block order.  Same set,
+    same per-unit arithmetic: the gradients must agree bit for bit."""
+    w = workloads.make_random(331, B=2, H=3, S=64 * 20, block=64,
+                              form="bitmap", density=0.5, vbs_mode="random")
+    log("[order-bwd] LUT vs bitmap")
+    mask = w.mask
+    idx = torch.full((mask.shape[0], w.NK), -1, dtype=torch.int32)
+    num = torch.zeros(mask.shape[0], dtype=torch.int32)
+    for r in range(mask.shape[0]):
+        sel = torch.nonzero(mask[r] != 0).flatten().to(torch.int32)
+        idx[r, :len(sel)] = sel
+        num[r] = len(sel)
+    assert len(set(num.tolist())) > 1  # the order is not the identity
+    d = to_dev(w)
+    out, lse = run_gpu(w, dev_inputs=d)
+    g = torch.Generator().manual_seed(12)
+    dout = torch.randn(tuple(w.q.shape), generator=g).to(torch.bfloat16).cuda()
+    common = dict(block=w.block, variable_block_sizes=d["vbs"],
+                  sm_scale=w.sm_scale, meta_strides=w.mask_strides)
+    g_bm = bsa.bsa_bwd(d["q"], d["k"], d["v"], out, dout, lse,
+                       mask=d["mask"], **common)
+    g_lut = bsa.bsa_bwd(d["q"], d["k"], d["v"], out, dout, lse,
+                        q2k_idx=idx.cuda(), q2k_num=num.cuda(), **common)
+    torch.cuda.synchronize()
+    for a, b in zip(g_bm, g_lut):
+        assert torch.equal(a, b)
