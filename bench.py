@@ -157,11 +157,11 @@ def launch(w, d, out, lse, kernel_events=None):
     """One forward pass; lse=None is the inference route (no LSE store).
     Codebook-coded K/V are dequantised inside the call.  The LUT form first
     computes its launch order on the GPU (heaviest units first, part of the
-    step).  kernel_events=(start, end): recorded around the forward call
+    step) when the launch has more units than run at once.  kernel_events=(start, end): recorded around the forward call
     alone (after the order pass)."""
     cb = dict(k_codebook=d.get("k_codebook"), v_codebook=d.get("v_codebook"))
     order = None
-    if w.form == "lut" and w.NQ <= bsa.BSA_MAX_ORDER_QBLOCKS:
+    if w.form == "lut" and bsa.api.launch_order_pays(w.B, w.H, w.NQ):
         order = bsa.bsa_unit_order_lut(d["q2k_idx"], d["q2k_num"], d["vbs"],
                                        B=w.B, H=w.H, S=w.S, Sk=w.Sk,
                                        block=w.block,
@@ -569,7 +569,8 @@ def main() -> int:
             "l2_hit_rate": counters.get("l2_hit_rate"),
             "launch_order": ("heaviest units first (order pass in the step)"
                              if w.form == "lut" and
-                             w.NQ <= bsa.BSA_MAX_ORDER_QBLOCKS else "q-block"),
+                             bsa.api.launch_order_pays(w.B, w.H, w.NQ)
+                             else "q-block"),
             "fwd_kernel_ms": None if ms_kernel is None else round(ms_kernel, 5),
         },
         "roofline": {

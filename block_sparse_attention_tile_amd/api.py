@@ -35,6 +35,16 @@ LSE_EMPTY = -3.4028234663852886e38  # BSA_LSE_EMPTY = -FLT_MAX
 BSA_MAX_KEY_BLOCKS = 16384
 BSA_MAX_ORDER_QBLOCKS = 4096
 
+# A launch of at most this many work units runs them all at once (256 CUs
+# hold up to 4 workgroups each), so their launch order cannot matter.
+ORDER_MIN_UNITS = 1024
+
+
+def launch_order_pays(B: int, H: int, NQ: int) -> bool:
+    """Whether the LUT-form forward computes a launch order by default:
+    more units than run at once, and few enough query blocks to sort."""
+    return B * H * NQ > ORDER_MIN_UNITS and NQ <= BSA_MAX_ORDER_QBLOCKS
+
 
 class BsaError(RuntimeError):
     def __init__(self, status: int):
@@ -226,7 +236,8 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     of (b, h, qb) is ``b*sb + h*sh + qb``; default one row per unit.
     ``balance``: launch each head's query blocks heaviest first (an order
     computed on the GPU by ``bsa_unit_order_lut``; the outputs are the same
-    bits either way); skipped beyond BSA_MAX_ORDER_QBLOCKS query blocks.
+    bits either way); skipped beyond BSA_MAX_ORDER_QBLOCKS query blocks and
+    for launches of at most ORDER_MIN_UNITS units, which all run at once.
     ``qblock_order``: an order computed beforehand (int32 ``[B*H*NQ]``, as
     ``bsa_unit_order_lut`` returns it) to launch with instead."""
     q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
@@ -250,7 +261,7 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         if order.dtype != torch.int32 or not order.is_contiguous():
             raise TypeError("qblock_order must be a contiguous int32 tensor")
         _need_elems("qblock_order", order, B * H * NQ)
-    elif balance and NQ <= BSA_MAX_ORDER_QBLOCKS:
+    elif balance and launch_order_pays(B, H, NQ):
         order = torch.empty(B * H * NQ, dtype=torch.int32, device=q.device)
         rc = _lib.load().bsa_unit_order_lut(
             _ptr(idx), _ptr(num), int(idx.shape[-1]), int(sb), int(sh),

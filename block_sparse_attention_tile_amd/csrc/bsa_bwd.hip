@@ -46,6 +46,9 @@ bsa_status bsa_rank_runs(int32_t* order, int32_t groups, int32_t n, hipStream_t 
 namespace {
 
 constexpr int BSTAGE = 2 * TILE_BYTES;  // two 32-row tiles per stage
+// A launch of at most this many workgroups runs them all at once (256 CUs
+// hold up to 4 each), so it is not reordered.
+constexpr int64_t ORDER_MIN_UNITS = 1024;
 
 struct BwdParams {
   const uint16_t* q;
@@ -746,7 +749,7 @@ bsa_status run_bwd(BwdParams p, const void* out, float* delta, int8_t* map,
   // LUT form: dq units launched heaviest first within each (b, h), as the
   // forward pass does (same order pass; no effect on the result)
   p.order = nullptr;
-  if (!BITMAP && p.NQ <= BSA_MAX_ORDER_QBLOCKS) {
+  if (!BITMAP && p.NQ <= BSA_MAX_ORDER_QBLOCKS && p.n_units > ORDER_MIN_UNITS) {
     const bsa_status os = bsa_unit_order_lut(p.idx, p.num, p.max_kv, p.meta_sb, p.meta_sh,
                                              p.vbs, order, B, p.H, p.S, p.Sk,
                                              p.S / p.NQ, (void*)st);
@@ -787,7 +790,7 @@ bsa_status run_bwd(BwdParams p, const void* out, float* delta, int8_t* map,
     pk.n_units = (int32_t)((int64_t)p.n_units / p.H * p.Hk / p.NQ * p.NK);
     // key blocks of each (b, K/V head) launched heaviest first
     pk.korder = nullptr;
-    if (p.NK <= BSA_MAX_ORDER_QBLOCKS) {
+    if (p.NK <= BSA_MAX_ORDER_QBLOCKS && pk.n_units > ORDER_MIN_UNITS) {
       hipLaunchKernelGGL(kunit_work_kernel, dim3((uint32_t)((pk.n_units + 3) / 4)),
                          dim3(256), 0, st, pk, korder, pk.n_units);
       const bsa_status rs = bsa_rank_runs(korder, pk.n_units / p.NK, p.NK, st);

@@ -260,7 +260,8 @@ bsa_status bsa_mask_to_lut(const int8_t* mask, int64_t rows, int32_t nk,
  *               to overwrite during the call (it holds delta, the
  *               key-block -> query-block selection map and the launch
  *               orders of the dq units -- LUT form, as bsa_unit_order_lut
- *               computes it -- and of the dk/dv units: heaviest first).
+ *               computes it -- and of the dk/dv units: heaviest first, for
+ *               launches of more than 1024 units).
  *               Calls that overlap on the same workspace race.
  *  workspace_bytes  its size; a smaller value is BSA_ERR_SHAPE.
  *

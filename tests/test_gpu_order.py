@@ -118,8 +118,13 @@ def test_ordered_forward_is_bitwise_the_unordered_one(label, kw):
     w = workloads.make_random(**kw)
     log(f"[order-fwd] {label}")
     d = to_dev(w)
+    order = bsa.bsa_unit_order_lut(d["q2k_idx"], d["q2k_num"], d["vbs"],
+                                   B=w.B, H=w.H, S=w.S, Sk=w.Sk, block=w.block,
+                                   meta_strides=w.meta_strides)
+    ident = torch.arange(w.NQ, dtype=torch.int32, device="cuda").repeat(w.B * w.H)
+    assert not torch.equal(order, ident)  # the ordered launch differs
     outs = []
-    for balance in (False, True):
+    for qo in (None, order):
         out = torch.full(tuple(w.q.shape), float("nan"), dtype=torch.bfloat16,
                          device="cuda")
         lse = torch.full((w.B, w.H, w.S), float("nan"), dtype=torch.float32,
@@ -127,7 +132,7 @@ def test_ordered_forward_is_bitwise_the_unordered_one(label, kw):
         bsa.bsa_fwd_lut(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"],
                         d["vbs"], block=w.block, sm_scale=w.sm_scale,
                         meta_strides=w.meta_strides, out=out, lse=lse,
-                        balance=balance)
+                        balance=False, qblock_order=qo)
         torch.cuda.synchronize()
         outs.append((out, lse))
     assert torch.equal(outs[0][0], outs[1][0])
@@ -139,6 +144,7 @@ def test_ordered_forward_full_configs(cfg):
     w = workloads.make_config(cfg)
     log(f"[order-fwd] {w.name}")
     d = to_dev(w)
+    assert bsa.api.launch_order_pays(w.B, w.H, w.NQ)
     a = run_gpu(w, dev_inputs=d)  # the binding orders by default
     out = torch.empty(tuple(w.q.shape), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda")
@@ -183,7 +189,9 @@ def test_ordered_backward_is_bitwise_the_unordered_bitmap_form():
     """The LUT-form backward launches its dq units heaviest first; the
     bitmap form on the same selection keeps the q-block order.  Same set,
     same per-unit arithmetic: the gradients must agree bit for bit."""
-    w = workloads.make_random(331, B=2, H=3, S=64 * 20, block=64,
+    # more units (1 536) than run at once, so both kinds of backward unit
+    # (query blocks and key blocks) are reordered
+    w = workloads.make_random(331, B=1, H=24, S=64 * 64, block=64,
                               form="bitmap", density=0.5, vbs_mode="random")
     log("[order-bwd] LUT vs bitmap")
     mask = w.mask
