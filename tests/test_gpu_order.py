@@ -215,3 +215,40 @@ def test_ordered_backward_is_bitwise_the_unordered_bitmap_form():
     torch.cuda.synchronize()
     for a, b in zip(g_bm, g_lut):
         assert torch.equal(a, b)
+
+
+LARGE = [
+    # more units than run at once, so the binding orders them by default
+    ("lut64_gqa", dict(seed=341, B=2, H=8, Hk=2, S=64 * 80, block=64,
+                       count_mode="uniform", vbs_mode="random", max_kv=24)),
+    ("lut128_shared", dict(seed=342, B=3, H=8, S=128 * 48, block=128,
+                           shared_meta=True, count_mode="uniform",
+                           vbs_mode="partial", max_kv=16)),
+    ("lut64_rect_tiny", dict(seed=343, B=1, H=16, S=64 * 72, Sk=64 * 40,
+                             block=64, count_mode="uniform", vbs_mode="tiny")),
+    ("lut64_fp8", dict(seed=344, B=2, H=8, S=64 * 72, block=64, kv="fp8",
+                       count_mode="uniform", max_kv=20)),
+]
+
+
+@pytest.mark.parametrize("label,kw", LARGE, ids=[c[0] for c in LARGE])
+def test_default_ordered_launch_is_bitwise_the_qblock_order(label, kw):
+    w = workloads.make_random(**kw)
+    assert bsa.api.launch_order_pays(w.B, w.H, w.NQ)
+    log(f"[order-large] {label}: units {w.n_units}")
+    d = to_dev(w)
+    res = []
+    for balance in (True, False):
+        out = torch.full(tuple(w.q.shape), float("nan"), dtype=torch.bfloat16,
+                         device="cuda")
+        lse = torch.full((w.B, w.H, w.S), float("nan"), dtype=torch.float32,
+                         device="cuda")
+        bsa.bsa_fwd_lut(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"],
+                        d["vbs"], block=w.block, sm_scale=w.sm_scale,
+                        k_scale=d["k_scale"], v_scale=d["v_scale"],
+                        meta_strides=w.meta_strides, out=out, lse=lse,
+                        balance=balance)
+        torch.cuda.synchronize()
+        res.append((out, lse))
+    assert not torch.isnan(res[0][0].float()).any()
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
