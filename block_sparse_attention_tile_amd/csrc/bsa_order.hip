@@ -8,12 +8,16 @@
 // `variable_block_sizes` entry masked).  Launched in q-block order, units
 // that happen to be heavy and start late leave a tail in which most slots
 // idle.  This pass orders the q-blocks of every (b, h) by decreasing
-// attended-key count (ties by increasing q-block), so that the forward
-// launch starts its heavy units first and runs units of similar length side
-// by side.  Two kernels:
+// attended-key count, so that the forward launch starts its heavy units
+// first and runs units of similar length side by side (they then also stay
+// at the same point of their ascending key sweeps, which keeps the K/V they
+// share in L2).  Two kernels:
 //   1. one wave per unit: work = sum over the row's first clamp(num, 0,
 //      max_kv) LUT entries inside [0, NK) of the block's valid keys (a cost
-//      estimate: a repeated entry is counted twice);
+//      estimate: a repeated entry is counted twice); the rank value is
+//      min(work / 64, 2^21 - 1) * 1024 + 1023 - mean, mean = the entries'
+//      average block index scaled to 0..1023 (truncated): counts in the
+//      same 64-key bucket order by where their selection lies;
 //   2. one workgroup per (b, h): each q-block's position is the rank of its
 //      64-bit key ((2^32 - 1 - work) << 32 | qb) among the NQ keys in LDS.
 // The result is deterministic (no atomics) and only affects scheduling.
@@ -52,14 +56,27 @@ __global__ __launch_bounds__(256) void unit_work_kernel(OrderParams p) {
   const int64_t row = (int64_t)b * p.meta_sb + (int64_t)h * p.meta_sh + qb;
   const int n = clampi(p.num[row], 0, p.max_kv);
   const int32_t* irow = p.idx + row * p.max_kv;
-  int w = 0;
+  long long w = 0, ps = 0, cnt = 0;
   for (int j = lane; j < n; j += 64) {
     const int kb = irow[j];
-    if (kb >= 0 && kb < p.NK) w += p.vbs ? clampi(p.vbs[kb], 0, p.block) : p.block;
+    if (kb >= 0 && kb < p.NK) {
+      w += p.vbs ? clampi(p.vbs[kb], 0, p.block) : p.block;
+      ps += kb;
+      cnt += 1;
+    }
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o);
-  if (lane == 0) p.order[u] = w;
+  for (int o = 32; o > 0; o >>= 1) {
+    w += __shfl_xor(w, o);
+    ps += __shfl_xor(ps, o);
+    cnt += __shfl_xor(cnt, o);
+  }
+  // rank value: valid keys in buckets of 64 (units within a bucket run about
+  // equally long), then the mean selected block scaled to 0..1023, lower
+  // first (units that start their sweeps alike run side by side)
+  const long long bucket = w >> 6 < (1ll << 21) - 1 ? w >> 6 : (1ll << 21) - 1;
+  const long long mean = cnt ? ps * 1023 / (cnt * (p.NK > 1 ? p.NK - 1 : 1)) : 0;
+  if (lane == 0) p.order[u] = (int32_t)((bucket << 10) | (1023 - mean));
 }
 
 // One workgroup per (b, h): the keys ((2^32 - 1 - work) << 32 | qb) are

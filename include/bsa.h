@@ -139,12 +139,16 @@ bsa_status bsa_fwd_lut(const void* q, const void* k, const void* v,
  * bsa_unit_order_lut -- launch order of the LUT-form work units.  Not an
  * operation of the pages: a scheduling aid for the forward launch.  For
  * every (b, h) it writes the permutation of the S/block query blocks by
- * decreasing attended-key count, ties by increasing query block, so that
- * bsa_fwd_lut_ordered starts its heavy units first and finishes on light
- * ones.  The count of unit (b, h, qb) is the sum, over its row's first
- * clamp(q2k_num, 0, max_kv) entries inside [0, Sk/block), of the entry's
- * valid keys (variable_block_sizes clamped to [0, block]; repeated entries
- * count twice: an estimate, exact for rows without repetitions).
+ * decreasing rank value, ties by increasing query block, so that
+ * bsa_fwd_lut_ordered starts its heavy units first, finishes on light ones
+ * and runs units of similar length and selection side by side.  Over unit
+ * (b, h, qb)'s first clamp(q2k_num, 0, max_kv) entries inside
+ * [0, Sk/block): count = the sum of the entries' valid keys
+ * (variable_block_sizes clamped to [0, block]; repeated entries count
+ * twice: an estimate, exact for rows without repetitions), mean = the
+ * entries' block indices summed, times 1023, divided by (number of entries
+ * * max(Sk/block - 1, 1)), truncated (0 without entries); rank value =
+ * min(count / 64, 2^21 - 1) * 1024 + 1023 - mean (integer division).
  *
  *  q2k_idx, q2k_num, max_kv, meta_stride_b, meta_stride_h,
  *  variable_block_sizes, B, H, S, Sk, block

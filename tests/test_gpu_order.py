@@ -21,9 +21,11 @@ def _need_gpu():
 
 
 def expected_order(w) -> np.ndarray:
-    """Host reference of the order: per (b, h), q-blocks by decreasing
-    count (sum of the valid keys of the row's first clamp(num) in-range
-    entries, repeats counted), ties by increasing q-block."""
+    """Host reference of the order: per (b, h), q-blocks by decreasing rank
+    value min(count // 64, 2^21 - 1) * 1024 + 1023 - mean (count = sum of
+    the valid keys of the row's first clamp(num) in-range entries, repeats
+    counted; mean = their block indices' sum * 1023 // (entries *
+    max(NK - 1, 1))), ties by increasing q-block."""
     NQ, NK, B, H = w.NQ, w.NK, w.B, w.H
     idx = w.q2k_idx.numpy().reshape(-1, w.q2k_idx.shape[-1])
     num = w.q2k_num.numpy().reshape(-1)
@@ -40,7 +42,10 @@ def expected_order(w) -> np.ndarray:
                 n = int(np.clip(num[row], 0, max_kv))
                 e = idx[row, :n]
                 e = e[(e >= 0) & (e < NK)]
-                work.append(int(vbs[e].sum()))
+                count = int(vbs[e].sum())
+                mean = (int(e.astype(np.int64).sum()) * 1023 //
+                        (len(e) * max(NK - 1, 1))) if len(e) else 0
+                work.append(min(count // 64, 2**21 - 1) * 1024 + 1023 - mean)
             o = sorted(range(NQ), key=lambda i: (-work[i], i))
             out[(b * H + h) * NQ:(b * H + h + 1) * NQ] = o
     return out
