@@ -34,8 +34,11 @@ import workloads  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+# the forward kernel and the launch-order pass (the order decides which
+# units share the L2, so it changes the kernel's traffic)
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_tile_amd", "csrc",
-                               f) for f in ("bsa_fwd.hip", "bsa_device.h")]
+                               f) for f in ("bsa_fwd.hip", "bsa_device.h",
+                                            "bsa_order.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsa_fwd_traffic.json")
 
 
