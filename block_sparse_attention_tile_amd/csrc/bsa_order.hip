@@ -84,6 +84,7 @@ __global__ __launch_bounds__(256) void unit_work_kernel(OrderParams p) {
 // keys below its own; every thread ranks its keys against all NQ keys in
 // LDS (each step reads one key that every lane reads: a broadcast).
 constexpr int SORT_THREADS = 1024;
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 static_assert(BSA_MAX_ORDER_QBLOCKS % SORT_THREADS == 0, "keys per thread");
 
 __global__ __launch_bounds__(SORT_THREADS) void unit_sort_kernel(OrderParams p) {
@@ -104,8 +105,15 @@ __global__ __launch_bounds__(SORT_THREADS) void unit_sort_kernel(OrderParams p) 
   for (int t = 0; t < BSA_MAX_ORDER_QBLOCKS / SORT_THREADS; ++t) {
     const int i = threadIdx.x + t * SORT_THREADS;
     if (i < n) {
+      // two keys per 16-byte LDS read, several reads in flight
       int rank = 0;
-      for (int j = 0; j < n; ++j) rank += keys[j] < mine[t] ? 1 : 0;
+      int j = 0;
+#pragma unroll 4
+      for (; j + 1 < n; j += 2) {
+        const u64x2 kk = *(const u64x2*)(keys + j);
+        rank += (kk.x < mine[t] ? 1 : 0) + (kk.y < mine[t] ? 1 : 0);
+      }
+      if (j < n) rank += keys[j] < mine[t] ? 1 : 0;
       ord[rank] = (int32_t)(uint32_t)mine[t];
     }
   }
