@@ -4,8 +4,12 @@
 // qb of head h of batch b.  The steps, in order:
 //
 //  A1  unit id -> (b, h, qb), with workgroups of consecutive ids spread so
-//      that each XCD (and its L2) serves a contiguous range of heads.  Query
-//      head h reads K/V head h / (H/Hk) (grouped-query attention; rocke
+//      that each XCD (and its L2) serves a contiguous range of heads.  The
+//      LUT form may take qb from a launch order (bsa_fwd_lut_ordered; the
+//      order pass in bsa_order.hip ranks each head's units heaviest first,
+//      so units of similar length run side by side and stay at the same
+//      point of their key sweeps, sharing K/V in L2).  Query head h reads
+//      K/V head h / (H/Hk) (grouped-query attention; rocke
 //      "sparse_attention.py" keeps separate query and KV head counts and
 //      query and key lengths, both supported here).
 //  A2  selected-set decode into LDS.  LUT form: the row's first
