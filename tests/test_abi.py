@@ -260,3 +260,14 @@ def test_codebook_dequant_rejects_invalid_static_arguments(args, status):
 def test_lut_accepts_scaled_bf16_mode_only_with_scales():
     assert lut(kv=2) == api.BSA_ERR_NULL
     assert lut(kv=2, ks=A) == api.BSA_ERR_NULL
+
+
+def test_launch_order_only_when_units_exceed_one_generation():
+    # more units than the 256 CUs hold at once, and at most
+    # BSA_MAX_ORDER_QBLOCKS query blocks per head
+    assert not api.launch_order_pays(1, 16, 64)          # Jenga: 1024 units
+    assert api.launch_order_pays(1, 24, 768)             # video: 18432 units
+    assert api.launch_order_pays(1, 1, 1025)
+    assert not api.launch_order_pays(1, 1, 1024)
+    assert not api.launch_order_pays(1, 2, api.BSA_MAX_ORDER_QBLOCKS + 1)
+    assert api.launch_order_pays(1, 2, api.BSA_MAX_ORDER_QBLOCKS)
