@@ -421,8 +421,9 @@ def bench_bwd(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the clock ramps over the first launches: warm up well past it
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2,
                     help="named workload index (default 2: video-shaped VSA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
