@@ -1,15 +1,17 @@
 """Benchmark of the block-sparse attention forward on one MI355X.
 
-A step is one forward pass (one kernel launch: decode, gather, QK^T, softmax,
-PV, epilogue) over the video-shaped VSA workload: B=1, H=24, S=49152
-(768 blocks of 64 tokens), D=128, bf16 N(0,1), 96 of 768 key blocks per query
-block (sorted LUT), variable_block_sizes uniform in [16, 64].  Inputs are
-resident in HBM before the timed region starts.
+A step is one forward pass over the video-shaped VSA workload: the launch
+order pass (two small kernels: each head's units heaviest first) and the
+forward kernel (decode, gather, QK^T, softmax, PV, epilogue).  Workload:
+B=1, H=24, S=49152 (768 blocks of 64 tokens), D=128, bf16 N(0,1), 96 of 768
+key blocks per query block (sorted LUT), variable_block_sizes uniform in
+[16, 64].  Inputs are resident in HBM before the timed region starts.
 
-Metric: effective TFLOP/s = 4*D*P / kernel time, with P the exact number of
+Metric: effective TFLOP/s = 4*D*P / time, with P the exact number of
 attended (query, key) pairs of the seeded metadata, against the MI355X bf16
-dense MFMA peak (2.5 PFLOP/s).  Prints ONE JSON line on stdout; progress goes
-to stderr.
+dense MFMA peak (2.5 PFLOP/s): `value` over the whole step, the roofline's
+`achieved` over the forward kernel alone (events around its launch).
+Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
 """
