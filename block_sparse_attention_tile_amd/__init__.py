@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     BSA_ERR_NULL,
     BSA_ERR_SHAPE,
     BSA_ERR_UNSUPPORTED,
+    BSA_ERR_VALUE,
     BSA_CODEBOOK_I4,
     BSA_CODEBOOK_I8,
     BSA_KV_BF16,

@@ -26,6 +26,7 @@ BSA_ERR_SHAPE = 2
 BSA_ERR_UNSUPPORTED = 3
 BSA_ERR_ALIGN = 4
 BSA_ERR_HIP = 5
+BSA_ERR_VALUE = 6
 BSA_KV_BF16 = 0
 BSA_KV_FP8E4M3 = 1
 BSA_KV_BF16_SCALED = 2

@@ -867,6 +867,7 @@ extern "C" bsa_status bsa_bwd_lut(const void* q, const void* k, const void* v,
   bsa_status st = check_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Hk, S,
                             Sk, D, block);
   if (st != BSA_OK) return st;
+  if (!__builtin_isfinite(sm_scale)) return BSA_ERR_VALUE;
   if (!q2k_idx || !q2k_num) return BSA_ERR_NULL;
   if (max_kv < 1 || meta_stride_b < 0 || meta_stride_h < 0) return BSA_ERR_SHAPE;
   BwdParams p = make_bwd_params(q, k, v, dout, lse, variable_block_sizes, sm_scale, dq,
@@ -892,6 +893,7 @@ extern "C" bsa_status bsa_bwd_bitmap(const void* q, const void* k, const void* v
   bsa_status st = check_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Hk, S,
                             Sk, D, block);
   if (st != BSA_OK) return st;
+  if (!__builtin_isfinite(sm_scale)) return BSA_ERR_VALUE;
   if (!mask) return BSA_ERR_NULL;
   if (mask_stride_b < 0 || mask_stride_h < 0) return BSA_ERR_SHAPE;
   BwdParams p = make_bwd_params(q, k, v, dout, lse, variable_block_sizes, sm_scale, dq,

@@ -27,7 +27,8 @@
  *    and is re-entrant.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    The call only enqueues work; it never synchronises.
- *  - Validation is static only (shapes, pointers, alignment); no device
+ *  - Validation is static only (shapes, pointers, alignment, finite
+ *    sm_scale); no device
  *    memory is read on the host.  On any error the status is returned,
  *    nothing is launched and `out`/`lse` are left untouched.
  *  - Device-side metadata is not validated; out-of-range values have the
@@ -65,7 +66,9 @@ typedef enum {
   BSA_ERR_UNSUPPORTED = 3, /* valid but not built: D != 128, block not 64/128,
                               too many key blocks, unknown kv dtype           */
   BSA_ERR_ALIGN = 4,       /* q, k, v or out not 16-byte aligned              */
-  BSA_ERR_HIP = 5          /* the HIP launch reported an error                */
+  BSA_ERR_HIP = 5,         /* the HIP launch reported an error                */
+  BSA_ERR_VALUE = 6        /* a scalar argument outside its domain: sm_scale
+                              not finite                                      */
 } bsa_status;
 
 typedef enum {
@@ -114,6 +117,11 @@ typedef enum {
  *               of each key block, clamped to [0, block]; keys at or past it
  *               are masked.  NULL = every block full.
  *  sm_scale     natural-log softmax scale (1/sqrt(D) is the usual value).
+ *               Any finite value: zero gives every attended key the same
+ *               weight, a negative value reverses the ranking.  NaN or
+ *               +-inf returns BSA_ERR_VALUE.  Per-block K/V scales (fp8,
+ *               scaled bf16) may likewise be zero or negative: a block's
+ *               keys are code value times scale, exactly.
  *  out          bf16 [B, H, S, D] contiguous, 16-byte aligned; every element
  *               is written.
  *  lse          fp32 [B, H, S] base-2 LSE, or NULL to skip it.

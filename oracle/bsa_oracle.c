@@ -129,11 +129,17 @@ static double kv_value(const attn_args* a, const void* base, const float* scale,
 /* Computes the `block` output rows of unit (b, h, qb) given its selected set.
  * Query head h reads key/value head h / (H/Hk): consecutive query heads
  * share one K/V head (rocke "sparse_attention.py": separate query and KV
- * head counts, a KV head index per head).  keys and t are scratch arrays of
- * length Sk, qd of length D. */
-static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
-                        const unsigned char* sel, int64_t* keys, double* t,
-                        double* qd, double* out, double* lse) {
+ * head counts, a KV head index per head).  The steps follow the definition
+ * in order: list the attended keys ascending; decode each attended key and
+ * value once into real numbers (rocke "sage_attention.py", module docstring:
+ * K/V are dequantised per block before the score and the PV product); then,
+ * per query row, the scores, their maximum, the weights, their sum, the
+ * weighted sum of values and the LSE.  keys and t are scratch arrays of
+ * length Sk, qd of length D.  Returns nonzero if the decoded-key buffers
+ * cannot be allocated. */
+static int attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
+                       const unsigned char* sel, int64_t* keys, double* t,
+                       double* qd, double* out, double* lse) {
   const int32_t D = a->D, block = a->block, NK = a->Sk / block;
   const int64_t qplane = ((int64_t)b * a->H + h) * (int64_t)a->Sq * D;
   const int64_t kvhead = (int64_t)b * a->Hk + h / (a->H / a->Hk);
@@ -148,6 +154,29 @@ static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
     for (int32_t tt = 0; tt < nv; ++tt) keys[n_att++] = (int64_t)kb * block + tt;
   }
 
+  /* decoded keys kd[j][d] and values vd[j][d] of the attended keys */
+  double* kd = NULL;
+  double* vd = NULL;
+  if (n_att > 0) {
+    kd = (double*)malloc(sizeof(double) * (size_t)n_att * (size_t)D);
+    vd = (double*)malloc(sizeof(double) * (size_t)n_att * (size_t)D);
+    if (!kd || !vd) {
+      free(kd);
+      free(vd);
+      return 1;
+    }
+    for (int64_t j = 0; j < n_att; ++j) {
+      const int64_t key = keys[j];
+      const int64_t srow = kvhead * NK + key / block;
+      for (int32_t d = 0; d < D; ++d) {
+        kd[j * D + d] = kv_value(a, a->k, a->k_scale, a->k_codebook,
+                                 plane + key * D + d, srow);
+        vd[j * D + d] = kv_value(a, a->v, a->v_scale, a->v_codebook,
+                                 plane + key * D + d, srow);
+      }
+    }
+  }
+
   for (int32_t r = 0; r < block; ++r) {
     double* o = out + (int64_t)r * D;
     const int64_t qrow = qplane + ((int64_t)qb * block + r) * D;
@@ -160,12 +189,8 @@ static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
     /* pass 1: scaled scores and their maximum */
     double m = -INFINITY;
     for (int64_t j = 0; j < n_att; ++j) {
-      const int64_t key = keys[j];
-      const int64_t srow = kvhead * NK + key / block;
       double s = 0.0;
-      for (int32_t d = 0; d < D; ++d)
-        s += qd[d] * kv_value(a, a->k, a->k_scale, a->k_codebook,
-                              plane + key * D + d, srow);
+      for (int32_t d = 0; d < D; ++d) s += qd[d] * kd[j * D + d];
       t[j] = s * c;
       if (t[j] > m) m = t[j];
     }
@@ -173,20 +198,24 @@ static void attend_unit(const attn_args* a, int32_t b, int32_t h, int32_t qb,
     double l = 0.0;
     for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
     for (int64_t j = 0; j < n_att; ++j) {
-      const int64_t key = keys[j];
-      const int64_t srow = kvhead * NK + key / block;
       const double w = exp2(t[j] - m);
       l += w;
-      for (int32_t d = 0; d < D; ++d)
-        o[d] += w * kv_value(a, a->v, a->v_scale, a->v_codebook,
-                             plane + key * D + d, srow);
+      for (int32_t d = 0; d < D; ++d) o[d] += w * vd[j * D + d];
     }
     for (int32_t d = 0; d < D; ++d) o[d] /= l;
     lse[r] = m + log2(l);
   }
+  free(kd);
+  free(vd);
+  return 0;
 }
 
 /* ---- argument checks shared by the entry points ---------------------- */
+
+/* The softmax scale may be any finite value (zero: equal weights;
+ * negative: reversed ranking); NaN and infinities are rejected, as by the
+ * GPU entry points. */
+static int check_scale(double sm_scale) { return isfinite(sm_scale) ? 0 : 1; }
 
 static int check_dims(int32_t B, int32_t H, int32_t Hk, int32_t Sq,
                       int32_t Sk, int32_t D, int32_t block) {
@@ -257,9 +286,12 @@ static int run_fwd(const attn_args* a, const sel_args* s, int32_t B,
       const int32_t h = (int32_t)((u / NQ) % a->H);
       const int32_t b = (int32_t)(u / ((int64_t)NQ * a->H));
       unit_select(s, b, h, qb, NK, sel);
-      attend_unit(a, b, h, qb, sel, keys, t, qd,
-                  out + i * (int64_t)a->block * a->D,
-                  lse + i * (int64_t)a->block);
+      if (attend_unit(a, b, h, qb, sel, keys, t, qd,
+                      out + i * (int64_t)a->block * a->D,
+                      lse + i * (int64_t)a->block)) {
+#pragma omp atomic write
+        failed = 1;
+      }
     }
     free(sel);
     free(keys);
@@ -284,6 +316,7 @@ int bsa_oracle_fwd_lut(const uint16_t* q, const void* k, const void* v,
                        double* lse) {
   if (!q || !k || !v || !q2k_idx || !q2k_num || !out || !lse) return 1;
   if (check_dims(B, H, Hk, Sq, Sk, D, block) || max_kv < 1) return 1;
+  if (check_scale(sm_scale)) return 1;
   if (check_kv(kv_dtype, k_scale, v_scale, k_codebook, v_codebook, D)) return 1;
   if (check_units(units, n_units, (int64_t)B * H * (Sq / block))) return 1;
   attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, k_codebook, v_codebook,
@@ -304,6 +337,7 @@ int bsa_oracle_fwd_bitmap(const uint16_t* q, const void* k, const void* v,
                           int64_t n_units, double* out, double* lse) {
   if (!q || !k || !v || !mask || !out || !lse) return 1;
   if (check_dims(B, H, Hk, Sq, Sk, D, block)) return 1;
+  if (check_scale(sm_scale)) return 1;
   if (check_kv(kv_dtype, k_scale, v_scale, k_codebook, v_codebook, D)) return 1;
   if (check_units(units, n_units, (int64_t)B * H * (Sq / block))) return 1;
   attn_args a = {q, k, v, kv_dtype, k_scale, v_scale, k_codebook, v_codebook,
@@ -436,6 +470,7 @@ int bsa_oracle_bwd(int form, const uint16_t* q, const uint16_t* k,
                    double* dv) {
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
   if (check_dims(B, H, Hk, Sq, Sk, D, block)) return 1;
+  if (check_scale(sm_scale)) return 1;
   if (form == FORM_LUT && (!q2k_idx || !q2k_num || max_kv < 1)) return 1;
   if (form == FORM_BITMAP && !mask) return 1;
   if (form != FORM_LUT && form != FORM_BITMAP) return 1;

@@ -40,6 +40,10 @@
  *   qk_scale = sm_scale*log2(e); the finite sentinel is -FLT_MAX; an empty
  *   row caused by vbs = 0 on every selected block is treated like count 0;
  *   out-of-range idx below the count is skipped, num and vbs are clamped.
+ *   sm_scale may be any finite value (zero: equal weights; negative:
+ *   reversed ranking), and so may the fp8 block scales (zero included: the
+ *   block's keys or values are then exactly zero); a non-finite sm_scale is
+ *   an invalid argument.
  *
  * Work units are numbered u = (b*H + h)*NQ + qb.  Outputs are compact: for
  * the i-th requested unit, out[i][r][d] (r < block, d < D) and lse[i][r].

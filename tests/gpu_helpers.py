@@ -24,7 +24,7 @@ def log(msg: str) -> None:
 def to_dev(w, dev="cuda"):
     d = {}
     for name in ("q", "k", "v", "k_scale", "v_scale", "q2k_idx", "q2k_num",
-                 "mask", "vbs"):
+                 "mask", "vbs", "k_codebook", "v_codebook"):
         t = getattr(w, name)
         d[name] = None if t is None else t.to(dev)
     return d
@@ -43,13 +43,15 @@ def run_gpu(w, *, need_lse=True, dev_inputs=None, prefill=float("nan")):
                         d["vbs"], block=w.block, sm_scale=w.sm_scale,
                         k_scale=d["k_scale"], v_scale=d["v_scale"],
                         meta_strides=w.meta_strides, need_lse=need_lse,
-                        out=out, lse=lse)
+                        out=out, lse=lse, k_codebook=d.get("k_codebook"),
+                        v_codebook=d.get("v_codebook"))
     else:
         bsa.bsa_fwd_bitmap(d["q"], d["k"], d["v"], d["mask"], d["vbs"],
                            block=w.block, sm_scale=w.sm_scale,
                            k_scale=d["k_scale"], v_scale=d["v_scale"],
                            mask_strides=w.mask_strides, need_lse=need_lse,
-                           out=out, lse=lse)
+                           out=out, lse=lse, k_codebook=d.get("k_codebook"),
+                           v_codebook=d.get("v_codebook"))
     torch.cuda.synchronize()
     return out, lse
 

@@ -41,15 +41,15 @@ def test_header_constants_match_the_binding():
     assert int(re.search(r"#define BSA_MAX_ORDER_QBLOCKS (\d+)", text).group(1)) == \
         api.BSA_MAX_ORDER_QBLOCKS
     for name in ("OK", "ERR_NULL", "ERR_SHAPE", "ERR_UNSUPPORTED", "ERR_ALIGN",
-                 "ERR_HIP", "KV_BF16", "KV_FP8E4M3", "KV_BF16_SCALED",
+                 "ERR_HIP", "ERR_VALUE", "KV_BF16", "KV_FP8E4M3", "KV_BF16_SCALED",
                  "CODEBOOK_I8", "CODEBOOK_I4"):
         m = re.search(r"\bBSA_%s\s*=\s*(\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(api, "BSA_" + name), name
 
 
 def test_status_strings():
-    for s in range(6):
-        assert api.bsa_status_str(s)
+    for s in range(7):
+        assert api.bsa_status_str(s) != "unknown status"
     assert api.bsa_status_str(99) == "unknown status"
 
 
@@ -211,6 +211,14 @@ def bwd_lut(**over):
     return _lib.load().bsa_bwd_lut(*args.values())
 
 
+def bwd_bitmap(**over):
+    args = dict(q=A, k=A, v=A, out=A, dout=A, lse=A, mask=A, sb=8, sh=8,
+                vbs=None, scale=0.1, dq=A, dk=A, dv=A, ws=A, ws_bytes=1 << 30,
+                B=1, H=1, Hk=1, S=512, Sk=512, D=128, block=64, stream=None)
+    args.update(over)
+    return _lib.load().bsa_bwd_bitmap(*args.values())
+
+
 def test_bwd_workspace_size_covers_delta_map_and_order():
     lib = _lib.load()
     # delta: B*H*S floats, map: B*H*NQ*NK bytes, launch orders: B*H*NQ and
@@ -271,3 +279,16 @@ def test_launch_order_only_when_units_exceed_one_generation():
     assert not api.launch_order_pays(1, 1, 1024)
     assert not api.launch_order_pays(1, 2, api.BSA_MAX_ORDER_QBLOCKS + 1)
     assert api.launch_order_pays(1, 2, api.BSA_MAX_ORDER_QBLOCKS)
+
+
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), -float("inf")])
+def test_non_finite_softmax_scale_is_rejected_by_every_entry_point(scale):
+    assert lut(scale=scale) == api.BSA_ERR_VALUE
+    assert lut_ordered(scale=scale) == api.BSA_ERR_VALUE
+    assert bitmap(scale=scale) == api.BSA_ERR_VALUE
+    assert bwd_lut(scale=scale) == api.BSA_ERR_VALUE
+    assert bwd_bitmap(scale=scale) == api.BSA_ERR_VALUE
+    # zero and negative scales are valid values, rejected only for other
+    # reasons (here: the null K pointer)
+    for ok in (0.0, -0.5):
+        assert lut(scale=ok, k=None) == api.BSA_ERR_NULL

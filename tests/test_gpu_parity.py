@@ -153,43 +153,92 @@ def test_tiny_named_workload_full_parity():
     check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, w.name)
 
 
-def _sample_units(w, n=24, seed=0):
-    g = np.random.default_rng(seed)
-    units = set([0, w.n_units - 1, w.n_units // 2])
-    units.update(g.choice(w.n_units, size=n, replace=False).tolist())
+def _unit_key_counts(w):
+    """Attended keys per work unit from the metadata (numpy; set semantics
+    per row: in-range entries below the clamped count, each block once)."""
+    NK, blk = w.NK, w.block
+    vbs = np.full(NK, blk) if w.vbs is None else np.clip(w.vbs.numpy(), 0, blk)
+    units = np.arange(w.n_units)
+    qb, h, b = units % w.NQ, (units // w.NQ) % w.H, units // (w.NQ * w.H)
     if w.form == "lut":
-        # include rows with count 0 when the workload has them
         sb, sh = w.meta_strides
-        zeros = []
-        for u in range(w.n_units):
-            qb = u % w.NQ
-            h = (u // w.NQ) % w.H
-            b = u // (w.NQ * w.H)
-            if int(w.q2k_num[b * sb + h * sh + qb]) == 0:
-                zeros.append(u)
-            if len(zeros) >= 3:
-                break
-        units.update(zeros)
-    return sorted(units)
+        rows = b * sb + h * sh + qb
+        idx = w.q2k_idx.numpy()[rows]
+        n = np.clip(w.q2k_num.numpy()[rows], 0, idx.shape[1])
+        ok = (np.arange(idx.shape[1])[None, :] < n[:, None]) & (idx >= 0) & (idx < NK)
+        sel = np.zeros((w.n_units, NK), dtype=bool)
+        r, c = np.nonzero(ok)
+        sel[r, idx[r, c]] = True
+    else:
+        sb, sh = w.mask_strides
+        sel = w.mask.numpy()[b * sb + h * sh + qb] != 0
+    return sel.astype(np.int64) @ vbs.astype(np.int64)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_named_workload_sampled_parity(cfg):
-    """Full-size named workloads, launched exactly as the benchmark launches
-    them; the oracle computes a sample of work units one by one."""
-    w = workloads.make_config(cfg)
-    log(f"[parity] {w.name}: B{w.B} H{w.H} S{w.S} blk{w.block} "
-        f"units={w.n_units}")
-    out, lse = run_gpu(w)
-    units = _sample_units(w, seed=cfg)
-    log(f"  oracle on {len(units)} sampled units")
+def _sample_units(w, n=1536, seed=0):
+    """n random units plus the 32 heaviest and 32 lightest units and every
+    unit with no attended key."""
+    g = np.random.default_rng(seed)
+    keys = _unit_key_counts(w)
+    order = np.argsort(-keys, kind="stable")
+    units = set([0, w.n_units - 1, w.n_units // 2])
+    units.update(g.choice(w.n_units, size=min(n, w.n_units), replace=False).tolist())
+    units.update(order[:32].tolist())
+    units.update(order[-32:].tolist())
+    units.update(np.nonzero(keys == 0)[0].tolist())
+    return sorted(int(u) for u in units)
+
+
+_FULL_SIZE = {}
+
+
+def _full_size_gpu(cfg):
+    """The named workload and its GPU outputs, launched exactly as the
+    benchmark launches them (computed once per module)."""
+    if cfg not in _FULL_SIZE:
+        _FULL_SIZE.clear()
+        w = workloads.make_config(cfg)
+        log(f"[parity] {w.name}: B{w.B} H{w.H} S{w.S} blk{w.block} "
+            f"units={w.n_units}")
+        out, lse = run_gpu(w)
+        # whole-output properties that hold at any size
+        assert not torch.isnan(out).any().item(), "unwritten or NaN output"
+        assert not torch.isnan(lse).any().item(), "unwritten or NaN lse"
+        assert torch.isfinite(lse).all().item()
+        _FULL_SIZE[cfg] = (w, out, lse)
+    return _FULL_SIZE[cfg]
+
+
+def _compare_units(w, out, lse, units, label):
     o_ref, l_ref = run_oracle(w, units=units)
     o_gpu, l_gpu = gather_units(w, out, lse, units)
-    check(o_gpu, l_gpu, o_ref, l_ref, w.name)
-    # whole-output properties that hold at any size
-    assert not torch.isnan(out).any().item(), "unwritten or NaN output"
-    assert not torch.isnan(lse).any().item(), "unwritten or NaN lse"
-    assert torch.isfinite(lse).all().item()
+    check(o_gpu, l_gpu, o_ref, l_ref, label)
+
+
+# (config, chunk, chunks): the Jenga and fp8 workloads element by element,
+# in chunks of work units; the video and 128-block workloads on samples
+FULL_SIZE = [(1, 0, 1), (4, 0, 4), (4, 1, 4), (4, 2, 4), (4, 3, 4),
+             (2, None, None), (3, None, None)]
+
+
+@pytest.mark.parametrize("cfg,chunk,chunks", FULL_SIZE,
+                         ids=[f"cfg{c}" + ("" if k is None else f"_part{k}of{n}")
+                              for c, k, n in FULL_SIZE])
+def test_named_workload_parity(cfg, chunk, chunks):
+    """Full-size named workloads, launched exactly as the benchmark launches
+    them.  The Jenga (1 024 units) and fp8 (6 144 units) workloads are
+    compared with the oracle on every element; the video (18 432 units) and
+    128-block (10 240 units) workloads on about 1 600 units each: a random
+    sample, the 32 heaviest and 32 lightest units and every empty unit."""
+    w, out, lse = _full_size_gpu(cfg)
+    if chunk is None:
+        units = _sample_units(w, seed=cfg)
+        log(f"  oracle on {len(units)} sampled units")
+    else:
+        per = (w.n_units + chunks - 1) // chunks
+        units = list(range(chunk * per, min(w.n_units, (chunk + 1) * per)))
+        log(f"  oracle on units {units[0]}..{units[-1]} of {w.n_units}")
+    _compare_units(w, out, lse, units, f"{w.name}[{len(units)} units]")
 
 
 def test_need_lse_false_gives_same_output_and_leaves_lse_alone():

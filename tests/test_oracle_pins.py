@@ -580,3 +580,94 @@ def test_integer_codebook_equals_bf16_values():
     o2, l2 = oracle.fwd_lut(w.q, kb, vb, w.q2k_idx, w.q2k_num, w.vbs,
                             block=w.block, meta_strides=w.meta_strides)
     assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+# ------------------------------------------- the softmax scale's full domain
+
+def test_oracle_rejects_a_non_finite_softmax_scale():
+    w = workloads.make_random(60, B=1, H=1, S=128, block=64)
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        with pytest.raises(ValueError):
+            run_oracle(w, sm_scale=bad)
+    with pytest.raises(ValueError):
+        oracle.bwd(w.q, w.k, w.v, w.q, block=64, q2k_idx=w.q2k_idx,
+                   q2k_num=w.q2k_num, sm_scale=float("nan"))
+
+
+SCALE_CASES = [
+    dict(seed=61, sm_scale=0.37, vbs_mode="partial"),
+    dict(seed=62, sm_scale=2.0, vbs_mode="random", form="bitmap"),
+    dict(seed=63, sm_scale=0.0, vbs_mode="partial", count_mode="uniform"),
+    dict(seed=64, sm_scale=-0.5, vbs_mode="zero_some", block=128, S=512),
+    dict(seed=65, sm_scale=-1.25, kv="fp8", vbs_mode="partial"),
+]
+
+
+@pytest.mark.parametrize("case", SCALE_CASES)
+def test_any_finite_softmax_scale_matches_dense_bruteforce(case):
+    case = dict(case)
+    seed, scale = case.pop("seed"), case.pop("sm_scale")
+    case.setdefault("S", 256)
+    case.setdefault("block", 64)
+    case.setdefault("density", 0.5)
+    w = workloads.make_random(seed, B=1, H=2, **case)
+    w.sm_scale = scale
+    o, lse = run_oracle(w)
+    o_ref, l_ref = bf.attention(w)
+    np.testing.assert_allclose(o, o_ref, atol=1e-10, rtol=1e-9)
+    empty = l_ref == bf.LSE_EMPTY
+    assert (lse[empty] == bf.LSE_EMPTY).all()
+    np.testing.assert_allclose(lse[~empty], l_ref[~empty], atol=1e-10,
+                               rtol=1e-10)
+
+
+def test_zero_softmax_scale_gives_mean_of_attended_values():
+    """sm_scale = 0: every attended key has weight 1, so O is the plain mean
+    of the attended values and LSE = log2(number of attended keys)."""
+    w = workloads.make_random(66, B=1, H=2, S=256, block=64, density=0.5,
+                              vbs_mode="partial")
+    w.sm_scale = 0.0
+    o, lse = run_oracle(w)
+    mask = bf.dense_mask(w)
+    v = bf.to_f64(w.v)
+    for h in range(w.H):
+        for r in range(w.S):
+            keys = np.nonzero(mask[0, h, r])[0]
+            np.testing.assert_allclose(o[0, h, r], v[0, h, keys].mean(axis=0),
+                                       atol=1e-12)
+            assert lse[0, h, r] == math.log2(len(keys))
+
+
+def test_negative_softmax_scale_equals_negated_query():
+    """t = (q . k) * c: negating the scale is negating every query (exact in
+    bf16 and in the products)."""
+    w = workloads.make_random(67, B=1, H=2, S=256, block=64, density=0.5,
+                              vbs_mode="random")
+    w.sm_scale = -0.3
+    o, lse = run_oracle(w)
+    w.sm_scale = 0.3
+    w.q = -w.q
+    o2, l2 = run_oracle(w)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+def test_zero_and_negative_fp8_block_scales_are_exact_products():
+    """A key block whose K scale is 0 scores exactly 0 on every query; a
+    block whose V scale is 0 contributes zero values but keeps its weights;
+    a negative scale negates the block (each against the dense brute force,
+    whose decode is torch's fp8 cast times the scale)."""
+    w = workloads.make_random(68, B=1, H=2, S=512, block=64, kv="fp8",
+                              density=0.6, vbs_mode="partial")
+    ks, vs = w.k_scale.clone(), w.v_scale.clone()
+    k = w.k.clone()
+    k[:, :, 64:128] = torch.zeros((1, 2, 64, 128)).to(torch.float8_e4m3fn)
+    ks[:, :, 1] = 0.0              # the all-zero block of amax/448 = 0
+    ks[:, 0, 3] = 0.0              # nonzero codes, zero scale
+    vs[:, 1, 2] = 0.0
+    ks[:, 1, 5] = -ks[:, 1, 5]
+    vs[:, 0, 6] = -2.0 * vs[:, 0, 6]
+    w.k, w.k_scale, w.v_scale = k, ks, vs
+    o, lse = run_oracle(w)
+    o_ref, l_ref = bf.attention(w)
+    np.testing.assert_allclose(o, o_ref, atol=1e-10, rtol=1e-9)
+    np.testing.assert_allclose(lse, l_ref, atol=1e-10, rtol=1e-10)
