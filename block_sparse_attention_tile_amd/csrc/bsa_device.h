@@ -86,19 +86,6 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Reductions over the two lanes l and l ^ 32 (the lanes that hold one query
-// in the 32x32 product layout), with the gfx950 cross-row lane swap.
-__device__ __forceinline__ float pair_max(float x) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                            false, false);
-  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                            false, false);
-  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
-}
-
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   return fmaxf(fmaxf(a, b), c);
 }

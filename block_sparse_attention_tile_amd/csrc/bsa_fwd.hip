@@ -41,12 +41,14 @@
 //      while tile i is computed.  fp8 e4m3 K/V are widened to bf16 exactly
 //      on the way into LDS.
 //  A5  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (fp32 accumulate), scaled by
-//      sm_scale*log2(e) (times the block's K scale for fp8); keys at or past
-//      the block's valid count are set to -inf.
-//  A6  softmax in exp2 form.  The reference m of each row is the row
-//      maximum of the unit's first tile and stays fixed (no per-tile max or
-//      rescale); if a weight or sum overflowed, the unit is recomputed with
-//      the running-max / rescale scheme (vLLM "tq_decode" step F shows it).
+//      c = sm_scale*log2(e) (times the block's K scale for fp8): t = s*c.
+//  A6  softmax in exp2 form.  The reference m of each row is the maximum of
+//      t over the valid keys of the unit's first tile and stays fixed (no
+//      per-tile max or rescale); exponents are t - m, set to -inf for keys
+//      at or past the block's valid count, so a masked key weighs exactly 0
+//      for any sign of c.  If a weight or sum overflowed, the unit is
+//      recomputed with the running-max / rescale scheme (vLLM "tq_decode"
+//      step F shows it).
 //      Partial sums l are kept per lane and reduced across the four lane
 //      groups that share a query once, at the end.
 //  A7  O^T += V^T P^T on the same MFMA; P is the softmax tile rounded to
@@ -95,16 +97,15 @@ struct FwdParams {
 
 // LDS tile layout: 32 rows of 256 B, 16-byte chunks XOR-swizzled per row so
 // that the MFMA operand reads are free of bank conflicts without padding.
-// K tiles are read row-wise (the 32x32x16 A operand: 32 rows x one chunk per
-// half-wave, 16 rows per 16-lane phase): chunk c of row r sits at position
-// c ^ (r & 15).  V tiles are read through the transposing LDS read (per
-// 16-lane group 4 rows x 32 bytes; 32 lanes cover 4 rows x 4 chunks):
-// position c ^ (4 * (r & 3)).
+// K tiles are read row-wise (16 rows x one chunk per 16 lanes): chunk c of
+// row r sits at position c ^ (r & 15).  V tiles are read through the
+// transposing LDS read (8 rows x 4 half-chunks per 32 lanes): position
+// c ^ ((r & 7) << 1).
 __device__ __forceinline__ int k_off(int r, int c) {
   return r * ROWB + ((c ^ (r & 15)) << 4);
 }
 __device__ __forceinline__ int v_off(int r, int c) {
-  return r * ROWB + ((c ^ ((r & 3) << 2)) << 4);
+  return r * ROWB + ((c ^ ((r & 7) << 1)) << 4);
 }
 
 // 4 fp8 e4m3 codes -> 4 bf16 (exact widening; scale 1).
@@ -168,148 +169,157 @@ __device__ __forceinline__ void store_tile_fp8(const Fp8Staging<NT>& st,
 }
 
 // Tile shapes of the K loop: FULL = 32 valid keys; PART = 1..31 valid keys
-// (keys past the count masked).
+// (keys past the count masked; the second 16-key half's QK^T is skipped
+// when it holds no valid key).
 enum TileKind { FULL = 0, PART = 1 };
 
-// The products are v_mfma_f32_32x32x16_bf16.  A 32x32 accumulator gives
-// lane l column l & 31 and rows 8*(i >> 2) + 4*(l >> 5) + (i & 3) in its
-// register i; the A operand gives lane l row l & 31 and K indices
-// 8*(l >> 5) .. +7, the B operand column l & 31 and the same K indices.
-// S^T = K Q^T puts keys on rows and this wave's 32 queries on columns, so
-// each lane holds 16 scores of one query: key 8*(i >> 2) + 4*hw + (i & 3) of
-// the tile, hw = l >> 5.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// Accumulator state of one wave: O^T tiles (d rows 32*dt + ..., this
-// lane's query on the column), the query's reference m (log2 units, equal
-// in lanes l and l ^ 32) and this lane's partial sum l.
+// Accumulator state of one wave: O^T tiles, per-row reference m (log2
+// units, identical in the four lanes of a row) and per-lane partial sums l.
 struct Acc {
-  f32x16 o[4];
-  float m;
-  float l;
+  f32x4 o[8][2];
+  float m[2];
+  float l[2];
 };
 
-// K operands of one tile (A operand of S^T = K Q^T): k[kk] holds dims
-// 16*kk + 8*hw .. +7 of tile key l & 31, read at the per-lane LDS offsets
-// ka[kk] (the swizzle makes each offset a per-lane constant).  All eight
-// reads are issued together right after the tile is published.
+// K operands of one tile for this wave (A operand of S^T = K Q^T):
+// k[h][kk] holds dims kk*32 + 8g .. +7 of tile key h*16 + r16.  All eight
+// reads are issued together right after the tile is published, so their
+// latency is paid once per tile.
 struct KOps {
-  bf16x8 k[8];
+  bf16x8 k[2][4];
 };
 
-__device__ __forceinline__ void load_k(const char* sb, const uint32_t (&ka)[8], KOps& ko) {
+__device__ __forceinline__ void load_k(const char* sb, uint32_t kbase, KOps& ko) {
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) ko.k[kk] = *(const bf16x8*)(sb + ka[kk]);
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      ko.k[h][kk] = *(const bf16x8*)(sb + (kbase ^ (kk << 6)) + h * 16 * ROWB);
 }
 
-// Raw scores of one tile for this wave (no masking here: the mask is
-// applied in t-space, see tile_exponents).
-__device__ __forceinline__ void tile_scores(const KOps& ko, const bf16x8 (&qreg)[8],
-                                            f32x16& s) {
-  s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko.k[0], qreg[0], f32x16{}, 0, 0, 0);
-#pragma unroll
-  for (int kk = 1; kk < 8; ++kk)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko.k[kk], qreg[kk], s, 0, 0, 0);
-}
-
-// Is score i of this lane a valid key of the tile?  (Lane limit
-// lim = nvt - 4*hw; a FULL tile has every key valid.)
+// Raw scores of one tile for this wave: s[qt][e], e = 4*s2 + j is key
+// s2*16 + 4g + j of the tile and query qt*16 + r16 (no masking here: the
+// mask is applied in t-space, see tile_exponents).
 template <int KIND>
-__device__ __forceinline__ bool key_valid(int i, int lim) {
-  return KIND == FULL || 8 * (i >> 2) + (i & 3) < lim;
+__device__ __forceinline__ void tile_scores(const KOps& ko, const bf16x8 (&qreg)[2][4],
+                                            int nvt, float (&s)[2][8]) {
+  f32x4 sacc[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+      sacc[0][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          ko.k[0][kk], qreg[qt][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[0][qt],
+          0, 0, 0);
+  sacc[1][0] = sacc[1][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (KIND == FULL || nvt > 16) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        sacc[1][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            ko.k[1][kk], qreg[qt][kk], sacc[1][qt], 0, 0, 0);
+  }
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[qt][e] = sacc[e >> 2][qt][e & 3];
 }
 
-// Maximum of the tile in t-space for this lane's query: max over the valid
-// keys of t = s*cs (any sign of cs), over both half-waves.
+// Is entry e of this lane a valid key of the tile?  (Lane limit
+// lim = nvt - 4g; a FULL tile has every key valid.)
 template <int KIND>
-__device__ __forceinline__ float tile_max(const f32x16& s, float cs, int lim) {
-  float t[16];
+__device__ __forceinline__ bool key_valid(int e, int lim) {
+  return KIND == FULL || (e >> 2) * 16 + (e & 3) < lim;
+}
+
+// Row maximum of the tile in t-space: max over the valid keys of t = s*cs
+// (any sign of cs), reduced over the four lanes of each row.
+template <int KIND>
+__device__ __forceinline__ void tile_max(const float (&s)[2][8], float cs, int lim,
+                                         float (&tm)[2]) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) t[i] = key_valid<KIND>(i, lim) ? s[i] * cs : -INFINITY;
+  for (int qt = 0; qt < 2; ++qt) {
+    float t[8];
 #pragma unroll
-  for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-    for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
-  return pair_max(t[0]);
+    for (int e = 0; e < 8; ++e)
+      t[e] = key_valid<KIND>(e, lim) ? s[qt][e] * cs : -INFINITY;
+    const float m0 = max3f(t[0], t[1], t[2]);
+    const float m1 = max3f(t[3], t[4], t[5]);
+    const float m2 = max3f(t[6], t[7], m0);
+    tm[qt] = group_max(fmaxf(m1, m2));
+  }
 }
 
 // Exponents of the tile's weights in place: s <- s*cs - m, and -inf for keys
 // at or past the valid count, so that a masked key's weight is exactly 0
 // whatever the sign of cs (cs = 0 included).
 template <int KIND>
-__device__ __forceinline__ void tile_exponents(f32x16& s, float cs, int lim, float m) {
-  const float nm = -m;
+__device__ __forceinline__ void tile_exponents(float (&s)[2][8], float cs, int lim,
+                                               const Acc& acc) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float x = __builtin_fmaf(s[i], cs, nm);
-    s[i] = key_valid<KIND>(i, lim) ? x : -INFINITY;
+  for (int qt = 0; qt < 2; ++qt) {
+    const float nm = -acc.m[qt];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = __builtin_fmaf(s[qt][e], cs, nm);
+      s[qt][e] = key_valid<KIND>(e, lim) ? x : -INFINITY;
+    }
   }
 }
 
-// P = 2^x (zero for masked keys), added to the lane's partial sum, scaled by
-// vsc (per-block V scale) and packed to bf16 as the B operands of the two
-// 16-key PV steps: pop[st] holds scores 8*st .. 8*st+7, i.e. keys
-// 16*st + 4*hw + (0..3) and 16*st + 8 + 4*hw + (0..3) at K indices
-// 8*hw + (0..7).
+// P = 2^x from the exponents of tile_exponents (zero for masked keys),
+// added to the partial row sums, scaled by vsc (fp8 V scale) and packed to
+// bf16 in the PV operand layout.
 template <bool SCALE_P>
-__device__ __forceinline__ void tile_probs(const f32x16& x, float vsc, Acc& acc,
+__device__ __forceinline__ void tile_probs(const float (&x)[2][8], float vsc, Acc& acc,
                                            bf16x8 (&pop)[2]) {
-  float pv[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(x[i]);
-  float a[8];
+  for (int qt = 0; qt < 2; ++qt) {
+    float pv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = pv[i] + pv[i + 8];
+    for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(x[qt][e]);
+    acc.l[qt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) +
+                 ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    if constexpr (SCALE_P) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] += a[i + 4];
-  acc.l += (a[0] + a[1]) + (a[2] + a[3]);
-  if constexpr (SCALE_P) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) pv[i] *= vsc;
-  }
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const u32x4 pk = {pack_bf16x2(pv[8 * st], pv[8 * st + 1]),
-                      pack_bf16x2(pv[8 * st + 2], pv[8 * st + 3]),
-                      pack_bf16x2(pv[8 * st + 4], pv[8 * st + 5]),
-                      pack_bf16x2(pv[8 * st + 6], pv[8 * st + 7])};
-    pop[st] = __builtin_bit_cast(bf16x8, pk);
+      for (int e = 0; e < 8; ++e) pv[e] *= vsc;
+    }
+    const u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                      pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+    pop[qt] = __builtin_bit_cast(bf16x8, pk);
   }
 }
 
-// V^T operands of one tile: v[dt][st] is the A operand of the PV step st
-// for d rows 32*dt + (l & 31): tile keys 16*st + 4*hw + (0..3) (first
-// transposing read, +0 rows) and 16*st + 8 + 4*hw + (0..3) (second read,
-// +8 rows), matching P's key order.  va[dt] is this lane's LDS offset of
-// the first read for st = 0; the others differ by immediates.  Issued
-// before the softmax so that their latency hides under it.
+// V^T operands of one tile: v[dt] holds, for d-row dt*16 + r16 of V^T, the
+// tile keys of MFMA K index 8g+i: key 4g+i (i<4) and 16+4g+(i-4) (i>=4),
+// matching P's accumulator layout.  Read with the transposing LDS read at
+// vbase ^ (dt << 5) (+16 rows); issued before the softmax so that their
+// latency hides under it.
 struct VOps {
-  bf16x8 v[4][2];
+  bf16x8 v[8];
 };
 
-__device__ __forceinline__ void load_v(const char* sb, const uint32_t (&va)[4], VOps& vo) {
+__device__ __forceinline__ void load_v(const char* sb, uint32_t vbase, VOps& vo) {
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const char* a = sb + va[dt] + st * 16 * ROWB;
-      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + 8 * ROWB));
-      const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      vo.v[dt][st] = __builtin_bit_cast(bf16x8, vv);
-    }
+  for (int dt = 0; dt < 8; ++dt) {
+    const uint32_t va = vbase ^ (uint32_t)(dt << 5);
+    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + va));
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(sb + va + 16 * ROWB));
+    const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    vo.v[dt] = __builtin_bit_cast(bf16x8, vv);
+  }
 }
 
-// O^T[d][query] += V^T P^T.  Masked keys carry P = 0 and their V rows hold
-// copies of a valid row (never a key past the count), so a partial tile
-// needs no special case here.
+// O^T[d][query] += V^T P^T.
 __device__ __forceinline__ void tile_pv(const VOps& vo, const bf16x8 (&pop)[2], Acc& acc) {
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
+  for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-      acc.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.v[dt][st], pop[st], acc.o[dt],
-                                                          0, 0, 0);
+    for (int qt = 0; qt < 2; ++qt)
+      acc.o[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo.v[dt], pop[qt],
+                                                               acc.o[dt][qt], 0, 0, 0);
 }
 
 // Direct loads of this wave's share of a bf16 tile.  The tile's 8 slices
@@ -376,6 +386,8 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;    // lane group: 0..3
+  const int r16 = lane & 15;  // row within a 16-row MFMA tile
 
   const int NK = p.NK;
   int* s_nsel = (int*)(smem + NSTAGE * STAGE_BYTES);
@@ -398,16 +410,16 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
 
   const int qrow0 = qb * BLK + wave * 32;  // first query row of this wave
 
-  // ---- A3: Q operands (B operand of S^T = K Q^T): qreg[kk] holds dims
-  // 16*kk + 8*hw .. +7 of query qrow0 + (lane & 31), loaded first so that
-  // they arrive while the selected set is decoded.
-  const int hw = lane >> 5;   // half-wave: K indices 8*hw .. 8*hw+7
-  const int c32 = lane & 31;  // column of the 32x32 products: the query
-  bf16x8 qreg[8];
+  // ---- A3: Q operands (B operand of S^T = K Q^T): Q[row r16][d kk*32+g*8..],
+  // loaded first so that they arrive while the selected set is decoded.
+  bf16x8 qreg[2][4];
   {
-    const uint16_t* qg = p.q + plane + (int64_t)(qrow0 + c32) * HD + 8 * hw;
+    const uint16_t* qg = p.q + plane + (int64_t)qrow0 * HD;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qreg[kk] = *(const bf16x8*)(qg + 16 * kk);
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qreg[qt][kk] = *(const bf16x8*)(qg + (qt * 16 + r16) * HD + kk * 32 + g * 8);
   }
   if (tid == 0) *s_redo = 0;
 
@@ -446,18 +458,16 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   __syncthreads();
   const int nsel = *s_nsel;
 
-  // Output row of this lane's query and the d offsets of its accumulator
-  // registers: register i of O^T tile dt is d = 32*dt + 8*(i >> 2) + 4*hw +
-  // (i & 3), stored four at a time.
-  const int64_t orow = (int64_t)bh * p.S + qrow0 + c32;
   if (nsel == 0) {
     // A8 for a unit with no attended key: exact zeros and the sentinel
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int qt = 0; qt < 2; ++qt) {
+      const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *(u32x2*)(p.out + orow * HD + 32 * dt + 8 * j + 4 * hw) = u32x2{0u, 0u};
-    if (p.lse && hw == 0) p.lse[orow] = BSA_LSE_EMPTY;
+      for (int dt = 0; dt < 8; ++dt)
+        *(u32x2*)(p.out + r * HD + dt * 16 + g * 4) = u32x2{0u, 0u};
+      if (p.lse && g == 0) p.lse[r] = BSA_LSE_EMPTY;
+    }
     return;
   }
 
@@ -467,40 +477,26 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   const char* vplane = (const char*)p.v + kvplane * EB;
   const int64_t scale_row = kvh * NK;  // fp8 scales of the K/V head
 
-  // Per-lane constant LDS offsets of the operand reads (the XOR swizzles
-  // make each a per-lane constant; the stage and the second half of a tile
-  // are immediates).  K operand of step kk: row c32, chunk 2*kk + hw at
-  // position (2*kk + hw) ^ (c32 & 15).  V^T transposing reads: the 16 lanes
-  // of group gq = lane >> 4 read 4 rows x 32 bytes; lane i = lane & 15 of
-  // the group gives row 4*hw + (i >> 2) (+ 8 for the second read, + 16 per
-  // PV step) and 8 bytes of the group's 32-byte column window, d =
-  // 32*dt + 16*(gq & 1) + 4*(i & 3) .. +3, i.e. chunk 4*dt + 2*(gq & 1) +
-  // ((i >> 1) & 1) at position chunk ^ 4*(i >> 2).
-  uint32_t ka[8], va[4];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    ka[kk] = (uint32_t)(c32 * ROWB + (((2 * kk + hw) ^ (c32 & 15)) << 4));
-  {
-    const int i = lane & 15, gq = lane >> 4, r = i >> 2;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-      va[dt] = (uint32_t)(TILE_BYTES + (4 * hw + r) * ROWB +
-                          (((4 * dt + 2 * (gq & 1) + ((i >> 1) & 1)) ^ (4 * r)) << 4) +
-                          (i & 1) * 8);
-  }
+  // Per-lane constant byte offsets (the XOR swizzles make every address a
+  // per-lane base XORed with a constant): K operand kbase ^ (kk << 6),
+  // keys 16..31 at +16 rows; V^T transposing reads vbase ^ (dt << 5), rows
+  // 16..31 at +16 rows; DMA offsets within a 4-row slice dko / dvo.
+  const uint32_t kbase = (uint32_t)(r16 * ROWB + ((g ^ r16) << 4));
+  const uint32_t vbase = (uint32_t)(TILE_BYTES + (lane >> 2) * ROWB +
+                                    ((2 * ((lane >> 2) & 7) + ((lane & 3) >> 1)) << 4) +
+                                    (lane & 1) * 8);
   const int l4 = lane >> 4, pos = lane & 15;
   // DMA source offsets of this lane for its wave's slices (see issue_bf16).
-  // The V swizzle depends only on l4, and with 4 waves the two slices of a
-  // wave share their K swizzle, so the stream path keeps one offset per
-  // tensor there and reaches the second slice 4 KB further through the
-  // scalar base (fewer live registers).
+  // With 4 waves the two slices of a wave share their swizzle, so the
+  // stream path keeps one offset per tensor and reaches the second slice
+  // 4 KB further through the scalar base (fewer live registers).
   constexpr int KP = (SCALED || NW != 4) ? 8 / NW : 1;
   [[maybe_unused]] uint32_t dko[KP], dvo[KP];
 #pragma unroll
   for (int i = 0; i < KP; ++i) {
     const int j = wave + i * NW;
     dko[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ l4) ^ ((j & 3) << 2)) << 4));
-    dvo[i] = (uint32_t)(j * 1024 + l4 * ROWB + ((pos ^ (4 * l4)) << 4));
+    dvo[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ (2 * l4)) ^ ((j & 1) << 3)) << 4));
   }
 
   ListCursor cursor{list, nsel, 0, 0u};
@@ -576,9 +572,11 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   auto run_pass = [&](auto safe_c, Acc& acc) {
     constexpr bool SAFE = decltype(safe_c)::value;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc.o[dt] = f32x16{};
-    acc.m = -INFINITY;
-    acc.l = 0.f;
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) acc.o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.m[0] = acc.m[1] = -INFINITY;
+    acc.l[0] = acc.l[1] = 0.f;
 
     cursor.reset(lane);
     [[maybe_unused]] Tile cur{};
@@ -624,14 +622,14 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
       if constexpr (FP8) issue_next();
       KOps ko;
       if constexpr (EARLY_OPS) {
-        load_k(sb, ka, ko);
+        load_k(sb, kbase, ko);
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (!FP8) issue_next();
       int nvt;  // valid keys of this tile (>= 1)
       if constexpr (SCALED) nvt = cur.nv - cur.t0;
       else nvt = cur_rows;
-      const int lim = nvt - 4 * hw;
+      const int lim = nvt - 4 * g;
       float cs = p.c;
       float vsc = 1.f;
       if constexpr (SCALED) {
@@ -641,37 +639,42 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
 
       // ---- A5 + A6: scores, the reference update (first tile, or every
       // tile of the rescaling pass) and the exponents in t-space.  The two
-      // tile kinds differ in the masking only; the paths join before the V
-      // reads are issued.
-      f32x16 sv;
-      if constexpr (!EARLY_OPS) load_k(sb, ka, ko);
-      tile_scores(ko, qreg, sv);
-      auto exponents = [&](auto kind_c) {
+      // tile kinds differ up to here only; the paths join before the V reads
+      // are issued.
+      float sv[2][8];
+      auto scores = [&](auto kind_c) {
         constexpr int KIND = decltype(kind_c)::value;
+        if constexpr (!EARLY_OPS) load_k(sb, kbase, ko);
+        tile_scores<KIND>(ko, qreg, nvt, sv);
         if constexpr (SAFE || FIRST) {
-          const float mnew = fmaxf(acc.m, tile_max<KIND>(sv, cs, lim));
-          if constexpr (SAFE && !FIRST) {
-            const float alpha = __builtin_amdgcn_exp2f(acc.m - mnew);
-            acc.l *= alpha;
+          float tm[2];
+          tile_max<KIND>(sv, cs, lim, tm);
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc.o[dt] *= alpha;
+          for (int qt = 0; qt < 2; ++qt) {
+            const float mnew = fmaxf(acc.m[qt], tm[qt]);
+            if constexpr (SAFE && !FIRST) {
+              const float alpha = __builtin_amdgcn_exp2f(acc.m[qt] - mnew);
+              acc.l[qt] *= alpha;
+#pragma unroll
+              for (int dt = 0; dt < 8; ++dt) acc.o[dt][qt] *= alpha;
+            }
+            acc.m[qt] = mnew;
           }
-          acc.m = mnew;
         }
-        tile_exponents<KIND>(sv, cs, lim, acc.m);
+        tile_exponents<KIND>(sv, cs, lim, acc);
       };
-      if (nvt >= KT) exponents(IntC<FULL>{});
-      else exponents(IntC<PART>{});
+      if (nvt >= KT) scores(IntC<FULL>{});
+      else scores(IntC<PART>{});
       VOps vo;
       if constexpr (EARLY_OPS) {
-        load_v(sb, va, vo);
+        load_v(sb, vbase, vo);
         __builtin_amdgcn_sched_barrier(0);
       }
       bf16x8 pop[2];
       tile_probs<SCALED>(sv, vsc, acc, pop);
 
       // ---- A7: PV
-      if constexpr (!EARLY_OPS) load_v(sb, va, vo);
+      if constexpr (!EARLY_OPS) load_v(sb, vbase, vo);
       tile_pv(vo, pop, acc);
 
       if (!has_next) return true;
@@ -700,28 +703,30 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   // maximum.  Then the unit is recomputed with the online rescale.
   Acc acc;
   run_pass(IntC<0>{}, acc);
-  bool bad = !(acc.l <= 1e37f);
+  bool bad = !(acc.l[0] <= 1e37f) || !(acc.l[1] <= 1e37f);
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bad |= !(__builtin_fabsf(acc.o[dt][i]) <= 3e38f);
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bad |= !(__builtin_fabsf(acc.o[dt][qt][i]) <= 3e38f);
   if (__any(bad)) *s_redo = 1;
   __syncthreads();  // every wave is done with both stages; s_redo visible
   if (*s_redo) run_pass(IntC<1>{}, acc);
 
   // ---- A8: epilogue
-  {
-    const float l = pair_sum(acc.l);  // >= 1: the reference key has weight >= 1
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float l = group_sum(acc.l[qt]);  // >= 1: the reference key has weight >= 1
     const float inv = 1.0f / l;
+    const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x16 o = acc.o[dt] * inv;
-        *(u32x2*)(p.out + orow * HD + 32 * dt + 8 * j + 4 * hw) =
-            u32x2{pack_bf16x2(o[4 * j], o[4 * j + 1]), pack_bf16x2(o[4 * j + 2], o[4 * j + 3])};
-      }
-    if (p.lse && hw == 0) p.lse[orow] = acc.m + __builtin_amdgcn_logf(l);
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 o = acc.o[dt][qt] * inv;
+      *(u32x2*)(p.out + r * HD + dt * 16 + g * 4) =
+          u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+    if (p.lse && g == 0) p.lse[r] = acc.m[qt] + __builtin_amdgcn_logf(l);
   }
 }
 
