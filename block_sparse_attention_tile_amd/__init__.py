@@ -18,10 +18,12 @@ from .api import (  # noqa: F401
     BSA_KV_FP8E4M3,
     BSA_MAX_KEY_BLOCKS,
     BSA_MAX_ORDER_QBLOCKS,
+    BSA_NOALLOC_SCRATCH_BYTES,
     BSA_OK,
     LSE_EMPTY,
     BsaError,
     bsa_bwd,
+    bsa_bwd_lut_noalloc,
     bsa_codebook_dequant,
     bsa_fwd_bitmap,
     bsa_fwd_from_mask,

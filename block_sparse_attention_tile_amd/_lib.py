@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libbsa.so")
 EXPORTS = ("bsa_fwd_lut", "bsa_fwd_lut_ordered", "bsa_unit_order_lut",
            "bsa_fwd_bitmap", "bsa_mask_to_lut",
            "bsa_bwd_workspace_size", "bsa_bwd_lut", "bsa_bwd_bitmap",
+           "bsa_bwd_lut_noalloc",
            "bsa_codebook_dequant", "bsa_status_str")
 
 _lib = None
@@ -58,6 +59,10 @@ def load():
     lib.bsa_bwd_bitmap.restype = ctypes.c_int32
     lib.bsa_bwd_bitmap.argtypes = [
         P, P, P, P, P, P, P, i64, i64, P, f32, P, P, P, P, sz,
+        i32, i32, i32, i32, i32, i32, i32, P]
+    lib.bsa_bwd_lut_noalloc.restype = ctypes.c_int32
+    lib.bsa_bwd_lut_noalloc.argtypes = [
+        P, P, P, P, P, P, P, P, i32, i64, i64, P, f32, P, P, P,
         i32, i32, i32, i32, i32, i32, i32, P]
     lib.bsa_codebook_dequant.restype = ctypes.c_int32
     lib.bsa_codebook_dequant.argtypes = [P, i32, P, P, i64, P]

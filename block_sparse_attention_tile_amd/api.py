@@ -27,6 +27,7 @@ BSA_ERR_UNSUPPORTED = 3
 BSA_ERR_ALIGN = 4
 BSA_ERR_HIP = 5
 BSA_ERR_VALUE = 6
+BSA_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 BSA_KV_BF16 = 0
 BSA_KV_FP8E4M3 = 1
 BSA_KV_BF16_SCALED = 2
@@ -454,6 +455,64 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         rc = lib.bsa_bwd_bitmap(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
                                 _ptr(lse), _ptr(m), int(sb), int(sh), _ptr(vbs),
                                 *common_tail)
+    if rc != BSA_OK:
+        raise BsaError(rc)
+    return dq, dk, dv
+
+
+def bsa_bwd_lut_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                        q2k_idx: torch.Tensor, q2k_num: torch.Tensor,
+                        variable_block_sizes: Optional[torch.Tensor] = None, *,
+                        block: int, sm_scale: Optional[float] = None,
+                        meta_strides: Optional[Tuple[int, int]] = None,
+                        dq: Optional[torch.Tensor] = None,
+                        dk: Optional[torch.Tensor] = None,
+                        dv: Optional[torch.Tensor] = None):
+    """LUT-form backward through ``bsa_bwd_lut_noalloc``: the library's own
+    per-GPU scratch replaces the workspace, so the C call allocates nothing
+    (pass ``dq``, ``dk``, ``dv`` to keep this call allocation-free; metadata
+    must already be contiguous int32).  Sizes whose workspace exceeds
+    ``BSA_NOALLOC_SCRATCH_BYTES`` raise ``BsaError(BSA_ERR_UNSUPPORTED)``.
+    Calls that overlap on one GPU race on the shared scratch."""
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or \
+            v.dtype != torch.bfloat16:
+        raise TypeError("the backward pass takes bf16 q, k, v")
+    if not q.is_cuda:
+        raise ValueError(f"q must be a GPU tensor, got {q.device}")
+    _need_device(q.device, k=k, v=v, out=out, dout=dout, lse=lse, dq=dq, dk=dk,
+                 dv=dv)
+    B, H, S, D = q.shape
+    Hk, Sk = int(k.shape[1]), int(k.shape[2])
+    for name, t, shape, dt in (("q", q, (B, H, S, D), torch.bfloat16),
+                               ("k", k, (B, Hk, Sk, D), torch.bfloat16),
+                               ("v", v, (B, Hk, Sk, D), torch.bfloat16),
+                               ("out", out, (B, H, S, D), torch.bfloat16),
+                               ("dout", dout, (B, H, S, D), torch.bfloat16),
+                               ("lse", lse, (B, H, S), torch.float32)):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape}")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor like {ref.shape}")
+    NQ = S // block
+    sb, sh = meta_strides if meta_strides is not None else (H * NQ, NQ)
+    for name, t in (("q2k_idx", q2k_idx), ("q2k_num", q2k_num),
+                    ("variable_block_sizes", variable_block_sizes)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    _check_meta(q, k, block, int(sb), int(sh), idx=q2k_idx, num=q2k_num,
+                vbs=variable_block_sizes)
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    rc = _lib.load().bsa_bwd_lut_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+        _ptr(q2k_idx), _ptr(q2k_num), int(q2k_idx.shape[-1]), int(sb), int(sh),
+        _ptr(variable_block_sizes), float(sm_scale), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, H, Hk, S, Sk, D, int(block), _cur_stream(q))
     if rc != BSA_OK:
         raise BsaError(rc)
     return dq, dk, dv

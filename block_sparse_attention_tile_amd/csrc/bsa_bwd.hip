@@ -35,6 +35,8 @@
 // bf16 (RNE).
 
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 #include <stdint.h>
 
 #include "bsa.h"
@@ -720,12 +722,12 @@ size_t workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t Sk, int64_t bloc
          (size_t)(B * H * (Sk / block)) * sizeof(int32_t);
 }
 
-bsa_status check_bwd(const void* q, const void* k, const void* v, const void* out,
-                     const void* dout, const float* lse, const void* dq,
-                     const void* dk, const void* dv, const void* ws,
-                     int32_t B, int32_t H, int32_t Hk, int32_t S, int32_t Sk,
-                     int32_t D, int32_t block) {
-  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !ws)
+// Static checks of the tensors and sizes (everything but the workspace).
+bsa_status check_bwd_args(const void* q, const void* k, const void* v, const void* out,
+                          const void* dout, const float* lse, const void* dq,
+                          const void* dk, const void* dv, int32_t B, int32_t H,
+                          int32_t Hk, int32_t S, int32_t Sk, int32_t D, int32_t block) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
     return BSA_ERR_NULL;
   if (B <= 0 || H <= 0 || Hk <= 0 || S <= 0 || Sk <= 0 || D <= 0 || block <= 0)
     return BSA_ERR_SHAPE;
@@ -737,8 +739,21 @@ bsa_status check_bwd(const void* q, const void* k, const void* v, const void* ou
     return BSA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       !aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
-      !aligned16(dv) || ((uintptr_t)ws & 255u) != 0)
+      !aligned16(dv))
     return BSA_ERR_ALIGN;
+  return BSA_OK;
+}
+
+bsa_status check_bwd(const void* q, const void* k, const void* v, const void* out,
+                     const void* dout, const float* lse, const void* dq,
+                     const void* dk, const void* dv, const void* ws,
+                     int32_t B, int32_t H, int32_t Hk, int32_t S, int32_t Sk,
+                     int32_t D, int32_t block) {
+  if (!ws) return BSA_ERR_NULL;
+  const bsa_status st = check_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, B, H, Hk, S,
+                                       Sk, D, block);
+  if (st != BSA_OK) return st;
+  if (((uintptr_t)ws & 255u) != 0) return BSA_ERR_ALIGN;
   return BSA_OK;
 }
 
@@ -903,4 +918,61 @@ extern "C" bsa_status bsa_bwd_bitmap(const void* q, const void* k, const void* v
   p.meta_sh = mask_stride_h;
   return dispatch_bwd<true>(p, block, out, workspace, workspace_bytes_, B, H, S, Sk,
                             (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward entry point: the workspace is the library's own
+// device array, one copy per GPU (allocated when the library's code object
+// is loaded on that GPU, held until the process ends).  Host code uses the
+// array only through its device address, taken once per device.
+
+static __device__ __align__(256) char scratch[BSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// Device address of `scratch` on the current device.
+bsa_status scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return BSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BSA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" bsa_status bsa_bwd_lut_noalloc(const void* q, const void* k, const void* v,
+                                          const void* out, const void* dout,
+                                          const float* lse, const int32_t* q2k_idx,
+                                          const int32_t* q2k_num, int32_t max_kv,
+                                          int64_t meta_stride_b, int64_t meta_stride_h,
+                                          const int32_t* variable_block_sizes,
+                                          float sm_scale, void* dq, void* dk, void* dv,
+                                          int32_t B, int32_t H, int32_t Hk, int32_t S,
+                                          int32_t Sk, int32_t D, int32_t block,
+                                          void* stream) {
+  bsa_status st = check_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, B, H, Hk, S, Sk, D,
+                                 block);
+  if (st != BSA_OK) return st;
+  if (!__builtin_isfinite(sm_scale)) return BSA_ERR_VALUE;
+  if (!q2k_idx || !q2k_num) return BSA_ERR_NULL;
+  if (max_kv < 1 || meta_stride_b < 0 || meta_stride_h < 0) return BSA_ERR_SHAPE;
+  if (workspace_bytes(B, H, S, Sk, block) > (size_t)BSA_NOALLOC_SCRATCH_BYTES)
+    return BSA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != BSA_OK) return st;
+  return bsa_bwd_lut(q, k, v, out, dout, lse, q2k_idx, q2k_num, max_kv, meta_stride_b,
+                     meta_stride_h, variable_block_sizes, sm_scale, dq, dk, dv, ws,
+                     (size_t)BSA_NOALLOC_SCRATCH_BYTES, B, H, Hk, S, Sk, D, block, stream);
 }

@@ -306,6 +306,37 @@ bsa_status bsa_bwd_bitmap(const void* q, const void* k, const void* v,
                           int32_t Hk, int32_t S, int32_t Sk, int32_t D,
                           int32_t block, void* stream);
 
+/* Size of the library-owned workspace of bsa_bwd_lut_noalloc, per GPU. */
+#define BSA_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+
+/*
+ * bsa_bwd_lut_noalloc -- bsa_bwd_lut for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result and errors as
+ * bsa_bwd_lut, without workspace / workspace_bytes: the workspace is the
+ * library's own device array of BSA_NOALLOC_SCRATCH_BYTES, one per GPU,
+ * allocated when the library is loaded on that GPU and held until the
+ * process ends.  The call allocates and frees nothing.
+ *
+ *  - Sizes whose bsa_bwd_workspace_size(B, H, S, Sk, block) exceeds
+ *    BSA_NOALLOC_SCRATCH_BYTES return BSA_ERR_UNSUPPORTED (nothing is
+ *    launched); use bsa_bwd_lut with a workspace of your own then.
+ *  - All calls on one GPU share the array: calls whose stream work
+ *    overlaps on the same GPU race, so serialise them (one stream, or
+ *    events).  Nothing in the array needs clearing by the caller; each call
+ *    writes what it reads.
+ *  - The current device must be the GPU of the tensors and the stream.
+ */
+bsa_status bsa_bwd_lut_noalloc(const void* q, const void* k, const void* v,
+                               const void* out, const void* dout, const float* lse,
+                               const int32_t* q2k_idx, const int32_t* q2k_num,
+                               int32_t max_kv, int64_t meta_stride_b,
+                               int64_t meta_stride_h,
+                               const int32_t* variable_block_sizes, float sm_scale,
+                               void* dq, void* dk, void* dv, int32_t B, int32_t H,
+                               int32_t Hk, int32_t S, int32_t Sk, int32_t D,
+                               int32_t block, void* stream);
+
 /*
  * bsa_codebook_dequant -- codebook K/V codes to bf16 values (rocke
  * "sage_attention.py": K/V stored as i8 or i4 codes of an f32 codebook,

@@ -292,3 +292,38 @@ def test_non_finite_softmax_scale_is_rejected_by_every_entry_point(scale):
     # reasons (here: the null K pointer)
     for ok in (0.0, -0.5):
         assert lut(scale=ok, k=None) == api.BSA_ERR_NULL
+
+
+def bwd_noalloc(**over):
+    args = dict(q=A, k=A, v=A, out=A, dout=A, lse=A, idx=A, num=A, max_kv=4,
+                sb=8, sh=8, vbs=None, scale=0.1, dq=A, dk=A, dv=A, B=1, H=1, Hk=1,
+                S=512, Sk=512, D=128, block=64, stream=None)
+    args.update(over)
+    return _lib.load().bsa_bwd_lut_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), api.BSA_ERR_NULL),
+    (dict(idx=None), api.BSA_ERR_NULL),
+    (dict(S=500), api.BSA_ERR_SHAPE),
+    (dict(max_kv=0), api.BSA_ERR_SHAPE),
+    (dict(D=64), api.BSA_ERR_UNSUPPORTED),
+    (dict(dq=A + 8), api.BSA_ERR_ALIGN),
+    (dict(scale=float("nan")), api.BSA_ERR_VALUE),
+    # workspace beyond the library's scratch: delta 4*B*H*S bytes plus the
+    # B*H*NQ*NK byte map exceed BSA_NOALLOC_SCRATCH_BYTES
+    (dict(B=1, H=64, Hk=64, S=64 * 256, Sk=64 * 2048), api.BSA_ERR_UNSUPPORTED),
+])
+def test_noalloc_backward_rejects_invalid_static_arguments(over, status):
+    assert bwd_noalloc(**over) == status
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define BSA_NOALLOC_SCRATCH_BYTES \((\d+) \* (\d+) \* (\d+)\)", text)
+    assert m
+    assert int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == \
+        api.BSA_NOALLOC_SCRATCH_BYTES
+    # the largest size the tests use stays inside it
+    assert _lib.load().bsa_bwd_workspace_size(24, 1, 49152, 49152, 64) <= \
+        api.BSA_NOALLOC_SCRATCH_BYTES
