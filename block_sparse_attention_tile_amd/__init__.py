@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     BSA_KV_BF16,
     BSA_KV_BF16_SCALED,
     BSA_KV_FP8E4M3,
+    BSA_FWD_KEY_SPLIT_MAX_UNITS,
     BSA_MAX_KEY_BLOCKS,
     BSA_MAX_ORDER_QBLOCKS,
     BSA_NOALLOC_SCRATCH_BYTES,

@@ -36,6 +36,9 @@ BSA_CODEBOOK_I4 = 1
 LSE_EMPTY = -3.4028234663852886e38  # BSA_LSE_EMPTY = -FLT_MAX
 BSA_MAX_KEY_BLOCKS = 16384
 BSA_MAX_ORDER_QBLOCKS = 4096
+# forward launches (block 64, bf16 K/V) of at most this many units split each
+# unit's keys over two wave groups of its workgroup
+BSA_FWD_KEY_SPLIT_MAX_UNITS = 512
 
 # A launch of at most this many work units runs them all at once (256 CUs
 # hold up to 4 workgroups each), so their launch order cannot matter.

@@ -366,14 +366,20 @@ constexpr int waves_per_simd() {
 }
 
 // KV: BSA_KV_BF16, BSA_KV_FP8E4M3 or BSA_KV_BF16_SCALED (bf16 values with
-// per-block scales, folded in exactly as for fp8).
-template <int BLK, int KV, bool BITMAP>
-__global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_kernel(
+// per-block scales, folded in exactly as for fp8).  KS: key halves.  With
+// KS = 2 two groups of NW waves share the unit: group 0 sweeps the selected
+// blocks up to the one where half of the unit's tiles are reached, group 1
+// the rest, each on its own pair of LDS stages; the two partial results
+// (O, m, l per query row) are merged in a fixed order at the end.  Used for
+// short launches, where the heaviest units would otherwise set the time.
+template <int BLK, int KV, bool BITMAP, int KS>
+__global__ __launch_bounds__(BLK * 2 * KS, (waves_per_simd<BLK, KV>())) void bsa_fwd_kernel(
     FwdParams p) {
   constexpr bool FP8 = KV == BSA_KV_FP8E4M3;  // codes staged through VGPRs
   constexpr bool SCALED = KV != BSA_KV_BF16;  // per-block K/V scales
-  constexpr int NW = BLK / 32;  // waves; each owns 32 query rows
-  constexpr int NT = NW * 64;
+  constexpr int NW = BLK / 32;  // waves of a key group; each owns 32 query rows
+  constexpr int NT = NW * 64;   // threads of a key group
+  constexpr int NTA = NT * KS;  // threads of the workgroup
   // Operand reads pinned ahead of their products (K right after the tile is
   // published, V before the softmax) where registers allow: with two waves
   // per SIMD there is room for both operand sets; the block-128 bf16 kernel,
@@ -385,14 +391,20 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave_all / NW;      // key group
+  const int wave = wave_all % NW;      // wave within the key group
+  const int htid = tid - half * NT;    // thread within the key group
   const int g = lane >> 4;    // lane group: 0..3
   const int r16 = lane & 15;  // row within a 16-row MFMA tile
 
   const int NK = p.NK;
-  int* s_nsel = (int*)(smem + NSTAGE * STAGE_BYTES);
-  int* s_redo = s_nsel + 1;
-  uint8_t* bmp = (uint8_t*)(smem + NSTAGE * STAGE_BYTES + 16);
+  // LDS: the key groups' stages, then the header (selected blocks, redo
+  // flag, split entry, tile counts), the byte map and the block list.
+  int* s_hdr = (int*)(smem + KS * NSTAGE * STAGE_BYTES);
+  int* s_nsel = s_hdr;
+  int* s_redo = s_hdr + 1;
+  uint8_t* bmp = (uint8_t*)(smem + KS * NSTAGE * STAGE_BYTES + 32);
   uint32_t* list = (uint32_t*)(bmp + ((NK + 15) & ~15));
 
   // ---- A1: work unit
@@ -427,14 +439,14 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   // selected, else 0 (every thread reads the valid counts of its entries)
   if constexpr (BITMAP) {
     const int8_t* mrow = p.mask + row * NK;
-    for (int i = tid; i < NK; i += NT)
+    for (int i = tid; i < NK; i += NTA)
       bmp[i] = mrow[i] != 0 ? (uint8_t)block_valid<BLK>(p.vbs, i) : (uint8_t)0;
   } else {
-    for (int i = tid; i < NK; i += NT) bmp[i] = 0;
+    for (int i = tid; i < NK; i += NTA) bmp[i] = 0;
     __syncthreads();
     const int n = clampi(p.num[row], 0, p.max_kv);
     const int32_t* irow = p.idx + row * p.max_kv;
-    for (int j = tid; j < n; j += NT) {
+    for (int j = tid; j < n; j += NTA) {
       const int kb = irow[j];
       // duplicates store the same value
       if (kb >= 0 && kb < NK) bmp[kb] = (uint8_t)block_valid<BLK>(p.vbs, kb);
@@ -442,7 +454,7 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   }
   __syncthreads();
   // byte map -> ascending list of selected blocks with >= 1 valid key
-  if (wave == 0) {
+  if (wave_all == 0) {
     int base = 0;
     for (int c0 = 0; c0 < NK; c0 += 64) {
       const int kb = c0 + lane;
@@ -454,11 +466,57 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
       base += __popcll(bal);
     }
     if (lane == 0) *s_nsel = base;
+    if constexpr (KS == 2) {
+      // Split entry E1: group 0 takes entries [0, E1), where the first half
+      // of the unit's tiles ends (at least one entry), group 1 the rest.
+      // Tiles of an entry: its valid keys / 32 as a share of the key stream
+      // (bf16), or ceil(valid keys / 32) (per-block tiles).
+      auto work = [&](int nv) { return SCALED ? (nv + KT - 1) / KT : nv; };
+      int total = 0;
+      for (int c0 = 0; c0 < base; c0 += 64) {
+        int x = c0 + lane < base ? work((int)(list[c0 + lane] & 255u)) : 0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+        total += x;
+      }
+      int e1 = base, run = 0, w0 = 0;
+      for (int c0 = 0; c0 < base && e1 == base; c0 += 64) {
+        const int w = c0 + lane < base ? work((int)(list[c0 + lane] & 255u)) : 0;
+        int x = w;  // inclusive scan over the lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(x, o);
+          if (lane >= o) x += y;
+        }
+        // first entry whose inclusive sum reaches half the work
+        const uint64_t hit = __ballot(c0 + lane < base && 2 * (run + x) >= total);
+        if (hit) {
+          const int l0 = __ffsll((unsigned long long)hit) - 1;
+          e1 = c0 + l0 + 1;
+          w0 = run + __shfl(x, l0);
+        }
+        run += __shfl(x, 63);
+      }
+      e1 = min(max(e1, 1), base);
+      if (e1 == base) w0 = total;
+      if (lane == 0) {
+        s_hdr[2] = e1;
+        // tiles per group
+        s_hdr[3] = SCALED ? w0 : (w0 + KT - 1) / KT;
+        s_hdr[4] = SCALED ? total - w0 : (total - w0 + KT - 1) / KT;
+      }
+    }
   }
   __syncthreads();
   const int nsel = *s_nsel;
+  // this key group's entries [e0, e0 + nsel_g) and the steps of the pass
+  const int e0 = KS == 2 && half ? s_hdr[2] : 0;
+  const int nsel_g = KS == 2 ? (half ? nsel - s_hdr[2] : s_hdr[2]) : nsel;
+  const int t_mine = KS == 2 ? (half ? s_hdr[4] : s_hdr[3]) : 0;
+  const int t_steps = KS == 2 ? max(s_hdr[3], s_hdr[4]) : 0;
 
   if (nsel == 0) {
+    if (half) return;
     // A8 for a unit with no attended key: exact zeros and the sentinel
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -481,10 +539,12 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   // per-lane base XORed with a constant): K operand kbase ^ (kk << 6),
   // keys 16..31 at +16 rows; V^T transposing reads vbase ^ (dt << 5), rows
   // 16..31 at +16 rows; DMA offsets within a 4-row slice dko / dvo.
-  const uint32_t kbase = (uint32_t)(r16 * ROWB + ((g ^ r16) << 4));
-  const uint32_t vbase = (uint32_t)(TILE_BYTES + (lane >> 2) * ROWB +
-                                    ((2 * ((lane >> 2) & 7) + ((lane & 3) >> 1)) << 4) +
-                                    (lane & 1) * 8);
+  // (the key group's stages start at stage0 bytes)
+  const uint32_t stage0 = (uint32_t)(half * NSTAGE * STAGE_BYTES);
+  const uint32_t kbase = stage0 + (uint32_t)(r16 * ROWB + ((g ^ r16) << 4));
+  const uint32_t vbase = stage0 + (uint32_t)(TILE_BYTES + (lane >> 2) * ROWB +
+                                             ((2 * ((lane >> 2) & 7) + ((lane & 3) >> 1)) << 4) +
+                                             (lane & 1) * 8);
   const int l4 = lane >> 4, pos = lane & 15;
   // DMA source offsets of this lane for its wave's slices (see issue_bf16).
   // With 4 waves the two slices of a wave share their swizzle, so the
@@ -499,7 +559,7 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
     dvo[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ (2 * l4)) ^ ((j & 1) << 3)) << 4));
   }
 
-  ListCursor cursor{list, nsel, 0, 0u};
+  ListCursor cursor{list + e0, nsel_g, 0, 0u};
   [[maybe_unused]] Fp8Staging<NT> st;
   [[maybe_unused]] float ksc_cur = 1.f, vsc_cur = 1.f, ksc_nxt = 1.f, vsc_nxt = 1.f;
 
@@ -510,11 +570,11 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
     const int64_t key0 = (int64_t)t.kb * BLK + t.t0;
     const int nvt = t.nv - t.t0;
     if constexpr (FP8) {
-      load_tile_fp8<NT>(st, kplane + key0 * HD, vplane + key0 * HD, nvt, tid);
+      load_tile_fp8<NT>(st, kplane + key0 * HD, vplane + key0 * HD, nvt, htid);
     } else if constexpr (SCALED) {
       const char* kg = kplane + key0 * ROWB;
       const char* vg = vplane + key0 * ROWB;
-      const uint32_t sl = smem_lds + stg * STAGE_BYTES;
+      const uint32_t sl = smem_lds + stage0 + stg * STAGE_BYTES;
       issue_bf16<NW>(kg, vg, sl, sl + TILE_BYTES, dko, dvo, wave, l4, nvt);
     }
     if constexpr (SCALED) {
@@ -532,9 +592,9 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   // blocks adds, per lane, the offset of the run of rows its row falls in.
   // Rows past the count re-read row 0's chunk.
   auto issue_stream = [&](Walk& w, int stg) -> int {
-    const uint32_t sl = smem_lds + stg * STAGE_BYTES;
+    const uint32_t sl = smem_lds + stage0 + stg * STAGE_BYTES;
     return next_stream_tile<BLK, NW>(
-        cursor, w, nsel, wave, l4, lane,
+        cursor, w, nsel_g, wave, l4, lane,
         [&](int64_t key0) {
           const char* kg = kplane + key0 * ROWB;
           const char* vg = vplane + key0 * ROWB;
@@ -582,25 +642,30 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
     [[maybe_unused]] Tile cur{};
     [[maybe_unused]] Walk walk{0, 0};
     [[maybe_unused]] int cur_rows = 0;
-    if constexpr (SCALED) {
-      cur = cursor.at(0, lane);
-      issue(cur, 0);
-    } else {
-      cur_rows = issue_stream(walk, 0);
-    }
-    if constexpr (FP8) store_tile_fp8<NT>(st, smem, tid);
-    if constexpr (SCALED) {
-      ksc_cur = ksc_nxt;
-      vsc_cur = vsc_nxt;
+    if (nsel_g > 0) {
+      if constexpr (SCALED) {
+        cur = cursor.at(0, lane);
+        issue(cur, 0);
+      } else {
+        cur_rows = issue_stream(walk, 0);
+      }
+      if constexpr (FP8) store_tile_fp8<NT>(st, smem + stage0, htid);
+      if constexpr (SCALED) {
+        ksc_cur = ksc_nxt;
+        vsc_cur = vsc_nxt;
+      }
     }
 
     // stg_c: LDS stage of `cur` (compile-time); first_c: this is tile 0
-    auto step = [&](auto stg_c, auto first_c) -> bool {
+    // (active = false: this key group has no tile left; it only takes part
+    // in the workgroup's barrier)
+    auto step = [&](auto stg_c, auto first_c, bool active) -> bool {
       constexpr int STG = decltype(stg_c)::value;
       constexpr bool FIRST = decltype(first_c)::value != 0;
       // tile `cur` complete in LDS for every wave; stage STG^1 free again
       wait_vm_all();
       __syncthreads();
+      if (!active) return true;
       const char* sb = smem + STG * STAGE_BYTES;
       [[maybe_unused]] Tile nxt{};
       [[maybe_unused]] int nxt_rows = 0;
@@ -612,10 +677,10 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
       auto issue_next = [&]() {
         if constexpr (SCALED) {
           nxt = cursor.next(cur, lane);
-          has_next = nxt.e < nsel;
+          has_next = nxt.e < nsel_g;
           if (has_next) issue(nxt, STG ^ 1);
         } else {
-          has_next = walk.e < nsel;
+          has_next = walk.e < nsel_g;
           if (has_next) nxt_rows = issue_stream(walk, STG ^ 1);
         }
       };
@@ -678,7 +743,7 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
       tile_pv(vo, pop, acc);
 
       if (!has_next) return true;
-      if constexpr (FP8) store_tile_fp8<NT>(st, smem + (STG ^ 1) * STAGE_BYTES, tid);
+      if constexpr (FP8) store_tile_fp8<NT>(st, smem + stage0 + (STG ^ 1) * STAGE_BYTES, htid);
       if constexpr (SCALED) {
         ksc_cur = ksc_nxt;
         vsc_cur = vsc_nxt;
@@ -689,10 +754,22 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
       return false;
     };
 
-    if (!step(IntC<0>{}, IntC<1>{})) {
-      while (true) {
-        if (step(IntC<1>{}, IntC<0>{})) break;
-        if (step(IntC<0>{}, IntC<0>{})) break;
+    if constexpr (KS == 1) {
+      if (!step(IntC<0>{}, IntC<1>{}, true)) {
+        while (true) {
+          if (step(IntC<1>{}, IntC<0>{}, true)) break;
+          if (step(IntC<0>{}, IntC<0>{}, true)) break;
+        }
+      }
+    } else {
+      // both key groups take t_steps barrier steps; a group whose tiles are
+      // done idles through the rest
+      int s = 0;
+      step(IntC<0>{}, IntC<1>{}, s < t_mine);
+      for (++s; s < t_steps; ++s) {
+        step(IntC<1>{}, IntC<0>{}, s < t_mine);
+        if (++s >= t_steps) break;
+        step(IntC<0>{}, IntC<0>{}, s < t_mine);
       }
     }
   };
@@ -714,10 +791,53 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
   __syncthreads();  // every wave is done with both stages; s_redo visible
   if (*s_redo) run_pass(IntC<1>{}, acc);
 
+  if constexpr (KS == 2) {
+    // Merge of the key groups' partial results for the same query rows:
+    // group 1 hands O, m and l over through LDS, group 0 combines
+    //   m = max(m0, m1) + 1,  O = O0 2^(m0-m) + O1 2^(m1-m),  l likewise
+    // (a group without tiles has m = -inf, O = l = 0 and weighs 0).  The
+    // + 1 halves both weights, exactly, so that the sum of two partial O
+    // that each passed the overflow check stays finite; O/l and m + log2 l
+    // are unchanged by it.
+    float* mb = (float*)smem;  // [68][NW][64], after every wave left its stages
+    auto at = [&](int i) -> float& { return mb[(i * NW + wave) * 64 + lane]; };
+    __syncthreads();
+    if (half) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) at((dt * 2 + qt) * 4 + i) = acc.o[dt][qt][i];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        at(64 + qt) = acc.m[qt];
+        at(66 + qt) = acc.l[qt];
+      }
+    }
+    __syncthreads();
+    if (half) return;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float m1 = at(64 + qt);
+      const float m = fmaxf(acc.m[qt], m1) + 1.f;
+      const float a0 = __builtin_amdgcn_exp2f(acc.m[qt] - m);
+      const float a1 = __builtin_amdgcn_exp2f(m1 - m);
+      acc.l[qt] = acc.l[qt] * a0 + at(66 + qt) * a1;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc.o[dt][qt][i] = acc.o[dt][qt][i] * a0 + at((dt * 2 + qt) * 4 + i) * a1;
+      acc.m[qt] = m;
+    }
+  }
+
   // ---- A8: epilogue
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const float l = group_sum(acc.l[qt]);  // >= 1: the reference key has weight >= 1
+    // >= 1 (>= 1/2 after a merge): the reference key has weight >= 1
+    const float l = group_sum(acc.l[qt]);
     const float inv = 1.0f / l;
     const int64_t r = (int64_t)bh * p.S + qrow0 + qt * 16 + r16;
 #pragma unroll
@@ -733,31 +853,36 @@ __global__ __launch_bounds__(BLK * 2, (waves_per_simd<BLK, KV>())) void bsa_fwd_
 // ----------------------------------------------------------------------------
 // host side
 
-size_t lds_bytes(int NK) {
-  return (size_t)NSTAGE * STAGE_BYTES + 16 + (size_t)((NK + 15) & ~15) +
+size_t lds_bytes(int NK, int KS) {
+  return (size_t)KS * NSTAGE * STAGE_BYTES + 32 + (size_t)((NK + 15) & ~15) +
          (size_t)NK * sizeof(uint32_t);
 }
 
-template <int BLK, int KV, bool BITMAP>
+template <int BLK, int KV, bool BITMAP, int KS>
 bsa_status launch(const FwdParams& p, hipStream_t stream) {
-  auto kern = bsa_fwd_kernel<BLK, KV, BITMAP>;
-  const size_t lds = lds_bytes(p.NK);
+  auto kern = bsa_fwd_kernel<BLK, KV, BITMAP, KS>;
+  const size_t lds = lds_bytes(p.NK, KS);
   if (lds > 65536) {
     if (hipFuncSetAttribute((const void*)kern,
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds) != hipSuccess)
       return BSA_ERR_HIP;
   }
-  hipLaunchKernelGGL(kern, dim3(p.n_units), dim3(BLK * 2), lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3(p.n_units), dim3(BLK * 2 * KS), lds, stream, p);
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 
 template <bool BITMAP, int BLK>
 bsa_status dispatch_kv(const FwdParams& p, int kv, hipStream_t s) {
   switch (kv) {
-    case BSA_KV_FP8E4M3: return launch<BLK, BSA_KV_FP8E4M3, BITMAP>(p, s);
-    case BSA_KV_BF16_SCALED: return launch<BLK, BSA_KV_BF16_SCALED, BITMAP>(p, s);
-    default: return launch<BLK, BSA_KV_BF16, BITMAP>(p, s);
+    case BSA_KV_FP8E4M3: return launch<BLK, BSA_KV_FP8E4M3, BITMAP, 1>(p, s);
+    case BSA_KV_BF16_SCALED: return launch<BLK, BSA_KV_BF16_SCALED, BITMAP, 1>(p, s);
+    default:
+      // short launches split each unit's keys over two wave groups (with
+      // more units than run at once, whole units balance better)
+      if (BLK == 64 && p.n_units <= BSA_FWD_KEY_SPLIT_MAX_UNITS)
+        return launch<BLK, BSA_KV_BF16, BITMAP, 2>(p, s);
+      return launch<BLK, BSA_KV_BF16, BITMAP, 1>(p, s);
   }
 }
 

@@ -58,6 +58,16 @@ extern "C" {
  * bsa_unit_order_lut sorts (LDS holds one 64-bit key per query block). */
 #define BSA_MAX_ORDER_QBLOCKS 4096
 
+/* Forward launches with block 64, bf16 K/V and at most this many work units
+ * (B*H*S/block) split each unit's attended keys between two wave groups of
+ * its workgroup and merge the two partial results (O, row maximum, row sum)
+ * in a fixed order: so few units all run at once (two such workgroups per
+ * compute unit on 256 CUs), and the longest unit sets the time.  The result
+ * is deterministic for given sizes and metadata; it can differ in the last
+ * bits from the same unit computed in a larger launch (the partial sums are
+ * added in another order). */
+#define BSA_FWD_KEY_SPLIT_MAX_UNITS 512
+
 typedef enum {
   BSA_OK = 0,
   BSA_ERR_NULL = 1,        /* a required pointer is NULL                      */

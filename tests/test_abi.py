@@ -40,6 +40,8 @@ def test_header_constants_match_the_binding():
         api.BSA_MAX_KEY_BLOCKS
     assert int(re.search(r"#define BSA_MAX_ORDER_QBLOCKS (\d+)", text).group(1)) == \
         api.BSA_MAX_ORDER_QBLOCKS
+    assert int(re.search(r"#define BSA_FWD_KEY_SPLIT_MAX_UNITS (\d+)", text).group(1)) == \
+        api.BSA_FWD_KEY_SPLIT_MAX_UNITS
     for name in ("OK", "ERR_NULL", "ERR_SHAPE", "ERR_UNSUPPORTED", "ERR_ALIGN",
                  "ERR_HIP", "ERR_VALUE", "KV_BF16", "KV_FP8E4M3", "KV_BF16_SCALED",
                  "CODEBOOK_I8", "CODEBOOK_I4"):

@@ -113,6 +113,47 @@ def test_small_random_parity(label, kw):
         check(o_gpu, l_gpu, o_ref, l_ref, label)
 
 
+# Launches on either side of BSA_FWD_KEY_SPLIT_MAX_UNITS at block 64 with
+# bf16 K/V: "wide" ones (more units) run one wave group per unit, "split"
+# ones divide every unit's selected blocks between two wave groups and merge
+# the partial results.  Each list holds ragged, empty and one-block rows.
+KEY_SPLIT = [
+    ("wide_lut64_vbs_edges", True, dict(seed=140, B=2, H=40, S=512, block=64,
+                                         count_mode="uniform", vbs_mode="edges")),
+    ("wide_bitmap64_vbs_tiny", True, dict(seed=141, B=1, H=72, S=512, block=64,
+                                           form="bitmap", density=0.8,
+                                           vbs_mode="tiny")),
+    ("wide_gqa_lut64_zero_some", True, dict(seed=142, B=2, H=48, Hk=8, S=384,
+                                             block=64, count_mode="uniform",
+                                             vbs_mode="zero_some")),
+    ("split_lut64_vbs_edges", False, dict(seed=143, B=2, H=4, S=1024, block=64,
+                                           count_mode="uniform", vbs_mode="edges")),
+    ("split_bitmap64_rect", False, dict(seed=144, B=1, H=4, Hk=2, S=1024,
+                                         Sk=4096, block=64, form="bitmap",
+                                         density=0.3, vbs_mode="partial")),
+    # a few full blocks among many 1..4-key ones: the halves are cut at a
+    # block boundary, far from half the blocks
+    ("split_lut64_heavy_blocks", False, dict(seed=145, B=1, H=8, S=2048,
+                                              block=64, density=0.7,
+                                              vbs_mode="tiny")),
+]
+
+
+@pytest.mark.parametrize("label,wide,kw", KEY_SPLIT, ids=[c[0] for c in KEY_SPLIT])
+def test_key_split_launch_parity(label, wide, kw):
+    kw = dict(kw)
+    w = workloads.make_random(kw.pop("seed"), **kw)
+    if label.endswith("heavy_blocks"):
+        w.vbs[::7] = 64
+    assert (w.n_units > bsa.BSA_FWD_KEY_SPLIT_MAX_UNITS) == wide
+    log(f"[parity] {label} units={w.n_units} B{w.B} H{w.H} Hk{w.Hk} S{w.S} Sk{w.Sk} "
+        f"form={w.form}")
+    out, lse = run_gpu(w)
+    o_ref, l_ref = run_oracle(w)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(),
+          o_ref.reshape(tuple(out.shape)), l_ref.reshape(tuple(lse.shape)), label)
+
+
 # BSA_MAX_KEY_BLOCKS key blocks: the LDS byte map and block list at their
 # largest, the list walked in 64-entry chunks to its end and per-lane load
 # offsets up to the last block (512 MB into the K/V plane at block 128).

@@ -25,6 +25,7 @@ import numpy as np
 import pytest
 import torch
 
+import block_sparse_attention_tile_amd as bsa
 import workloads
 from tests import bruteforce as bf
 from tests.gpu_helpers import (check, gather_units, log, run_gpu, run_oracle,
@@ -118,11 +119,31 @@ def test_fp8_zero_and_negative_block_scales_parity():
     _parity(w, "fp8_zero_neg_scales")
 
 
-def _first_tile_max(w, units):
-    """Per row of each unit, the reference the fixed pass starts from: the
-    maximum of t over the unit's first tile (the first 32 keys of the stream
-    of valid keys for bf16 K/V; the lowest block's first min(32, valid)
-    keys when K/V carry per-block scales), by dense float64 arithmetic."""
+def _key_groups(w, keys):
+    """A unit's attended keys (ascending) as its wave groups sweep them.  A
+    split launch (block 64, bf16 K/V, at most BSA_FWD_KEY_SPLIT_MAX_UNITS
+    units) hands the selected blocks up to the first one at which the
+    running count of valid keys reaches half the unit's total (at least one
+    block) to group 0 and the rest to group 1; otherwise one group takes
+    them all.  Each group starts its own fixed reference."""
+    split = (w.block == 64 and not (w.kv_fp8 or w.kv_codebook)
+             and w.n_units <= bsa.BSA_FWD_KEY_SPLIT_MAX_UNITS)
+    if not split:
+        return [keys]
+    _, counts = np.unique(keys // w.block, return_counts=True)
+    cum = np.cumsum(counts)
+    e1 = min(max(int(np.argmax(2 * cum >= cum[-1])) + 1, 1), len(counts))
+    cut = int(cum[e1 - 1])
+    return [g for g in (keys[:cut], keys[cut:]) if len(g)]
+
+
+def _rescale_gaps(w, units):
+    """Per checked unit, the largest gap over its rows and wave groups
+    between the group's log2-sum of weights, log2 sum 2^t, and the group's
+    fixed reference: the maximum of t over the group's first tile (the first
+    32 keys of its stream of valid keys for bf16 K/V; the lowest block's
+    first min(32, valid) keys when K/V carry per-block scales), by dense
+    float64 arithmetic.  None for a unit without keys."""
     mask = bf.dense_mask(w)
     q = bf.to_f64(w.q)
     k, _ = bf.kv_f64(w)
@@ -138,23 +159,28 @@ def _first_tile_max(w, units):
         if len(keys) == 0:
             res.append(None)
             continue
-        if per_block:
-            first = keys[keys // w.block == keys[0] // w.block][:32]
-        else:
-            first = keys[:32]
-        t = q[b, h, rows] @ k[b, h, first].T * c
-        res.append(t.max(axis=1))
+        gap = -np.inf
+        for grp in _key_groups(w, keys):
+            if per_block:
+                first = grp[grp // w.block == grp[0] // w.block][:32]
+            else:
+                first = grp[:32]
+            m = (q[b, h, rows] @ k[b, h, first].T * c).max(axis=1)
+            t = q[b, h, rows] @ k[b, h, grp].T * c
+            tm = t.max(axis=1)
+            lsum = tm + np.log2(np.exp2(t - tm[:, None]).sum(axis=1))
+            gap = max(gap, float((lsum - m).max()))
+        res.append(gap)
     return res
 
 
-def _assert_rescale_needed(w, units, l_ref):
-    """Some checked row has LSE - (first tile maximum) > 130: its row sum
-    exceeds 2^130 relative to the fixed reference, so at least one lane's
-    partial sum passes 2^128 and overflows fp32 -- the unit's result is
-    right only if the rescaling pass ran."""
-    refs = _first_tile_max(w, units)
-    lr = l_ref.reshape(len(units), w.block)
-    gaps = [float((lr[i] - m).max()) for i, m in enumerate(refs) if m is not None]
+def _assert_rescale_needed(w, units):
+    """Some checked row and wave group has a log2-sum of weights more than
+    130 above the group's fixed reference: its row sum exceeds 2^130 relative
+    to that reference, so at least one lane's partial sum passes 2^128 and
+    overflows fp32 -- the unit's result is right only if the rescaling pass
+    ran."""
+    gaps = [g for g in _rescale_gaps(w, units) if g is not None]
     n_over = sum(g > 130 for g in gaps)
     log(f"  rows needing the rescale in {n_over} of {len(gaps)} checked units "
         f"(largest gap {max(gaps):.0f} log2 units)")
@@ -170,13 +196,19 @@ RESCALE = [
     ("lut64_planted_block", dict(seed=321, B=1, H=2, S=2048, block=64,
                                  density=0.5, vbs_mode="partial"), 0.5, 24),
     ("lut64_planted_tiny", dict(seed=322, B=1, H=2, S=4096, block=64,
-                                density=0.8, vbs_mode="tiny"), 0.5, 40),
+                                density=0.8, vbs_mode="tiny"), 0.5, 56),
     ("bitmap128_planted_block", dict(seed=323, B=1, H=2, S=2048, block=128,
                                      form="bitmap", density=0.5,
                                      vbs_mode="edges"), 0.5, 11),
     ("lut128_planted_block", dict(seed=324, B=2, H=2, S=2048, block=128,
                                   count_mode="uniform", vbs_mode="partial"),
      0.5, 9),
+    # more units than a split launch takes: one wave group per unit
+    ("wide_lut64_scale_16", dict(seed=326, B=1, H=36, S=1024, block=64,
+                                 density=0.5, vbs_mode="partial"), 16.0, None),
+    ("wide_bitmap64_planted_block", dict(seed=327, B=2, H=18, S=1024,
+                                         block=64, form="bitmap", density=0.5,
+                                         vbs_mode="edges"), 0.5, 11),
     # fp8: the block's K scale times 16
     ("fp8_lut64_planted_scale", dict(seed=325, B=1, H=2, S=2048, block=64,
                                      kv="fp8", density=0.5,
@@ -202,5 +234,5 @@ def test_rescaling_pass_parity(label, kw, scale, plant):
             w.k = k
     log(f"[softmax] rescale {label} sm_scale={scale} planted={plant}")
     units = _units(w) or list(range(w.n_units))
-    o_ref, l_ref = _parity(w, label)
-    _assert_rescale_needed(w, units, l_ref)
+    _parity(w, label)
+    _assert_rescale_needed(w, units)
