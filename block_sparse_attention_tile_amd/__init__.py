@@ -31,5 +31,6 @@ from .api import (  # noqa: F401
     bsa_fwd_lut,
     bsa_mask_to_lut,
     bsa_status_str,
+    bsa_unit_order_bitmap,
     bsa_unit_order_lut,
 )

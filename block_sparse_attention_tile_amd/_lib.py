@@ -12,7 +12,8 @@ LIB_PATH = os.path.join(_HERE, "libbsa.so")
 
 # The exported C symbols, as declared in include/bsa.h.
 EXPORTS = ("bsa_fwd_lut", "bsa_fwd_lut_ordered", "bsa_unit_order_lut",
-           "bsa_fwd_bitmap", "bsa_mask_to_lut",
+           "bsa_fwd_bitmap", "bsa_fwd_bitmap_ordered", "bsa_unit_order_bitmap",
+           "bsa_mask_to_lut",
            "bsa_bwd_workspace_size", "bsa_bwd_lut", "bsa_bwd_bitmap",
            "bsa_bwd_lut_noalloc",
            "bsa_codebook_dequant", "bsa_status_str")
@@ -47,6 +48,13 @@ def load():
     lib.bsa_fwd_bitmap.argtypes = [
         P, P, P, i32, P, P, P, i64, i64, P, f32, P, P,
         i32, i32, i32, i32, i32, i32, i32, P]
+    lib.bsa_fwd_bitmap_ordered.restype = ctypes.c_int32
+    lib.bsa_fwd_bitmap_ordered.argtypes = [
+        P, P, P, i32, P, P, P, i64, i64, P, P, f32, P, P,
+        i32, i32, i32, i32, i32, i32, i32, P]
+    lib.bsa_unit_order_bitmap.restype = ctypes.c_int32
+    lib.bsa_unit_order_bitmap.argtypes = [
+        P, i64, i64, P, P, i32, i32, i32, i32, i32, P]
     lib.bsa_mask_to_lut.restype = ctypes.c_int32
     lib.bsa_mask_to_lut.argtypes = [P, i64, i32, P, P, P]
     sz = ctypes.c_size_t

@@ -221,6 +221,20 @@ def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block,
     return q, k, v, kvd, k_scale, v_scale, out, lse
 
 
+def _launch_order(q, qblock_order, balance, B, H, NQ):
+    """The given order (checked), True if one should be computed, or None
+    (q-block order)."""
+    if qblock_order is not None:
+        _need_device(q.device, qblock_order=qblock_order)
+        if qblock_order.dtype != torch.int32 or not qblock_order.is_contiguous():
+            raise TypeError("qblock_order must be a contiguous int32 tensor")
+        _need_elems("qblock_order", qblock_order, B * H * NQ)
+        return qblock_order
+    if balance and launch_order_pays(B, H, NQ):
+        return True
+    return None
+
+
 @_on_stream
 def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 q2k_idx: torch.Tensor, q2k_num: torch.Tensor,
@@ -259,14 +273,8 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 k_scale=ks, v_scale=vs)
     if sm_scale is None:
         sm_scale = 1.0 / (D ** 0.5)
-    order = None
-    if qblock_order is not None:
-        order = qblock_order
-        _need_device(q.device, qblock_order=order)
-        if order.dtype != torch.int32 or not order.is_contiguous():
-            raise TypeError("qblock_order must be a contiguous int32 tensor")
-        _need_elems("qblock_order", order, B * H * NQ)
-    elif balance and launch_order_pays(B, H, NQ):
+    order = _launch_order(q, qblock_order, balance, B, H, NQ)
+    if order is True:
         order = torch.empty(B * H * NQ, dtype=torch.int32, device=q.device)
         rc = _lib.load().bsa_unit_order_lut(
             _ptr(idx), _ptr(num), int(idx.shape[-1]), int(sb), int(sh),
@@ -317,6 +325,34 @@ def bsa_unit_order_lut(q2k_idx: torch.Tensor, q2k_num: torch.Tensor,
 
 
 @_on_stream
+def bsa_unit_order_bitmap(mask: torch.Tensor,
+                          variable_block_sizes: Optional[torch.Tensor] = None, *,
+                          B: int, H: int, S: int, Sk: int, block: int,
+                          mask_strides: Optional[Tuple[int, int]] = None):
+    """Launch order of the bitmap-form units: int32 ``[B*H*NQ]``, for every
+    (b, h) its query blocks by decreasing attended-key count (ties by
+    q-block), computed on the GPU."""
+    if not mask.is_cuda:
+        raise ValueError(f"mask must be a GPU tensor, got {mask.device}")
+    m = mask.to(torch.int8).contiguous()
+    vbs = _i32(variable_block_sizes)
+    _need_device(m.device, variable_block_sizes=vbs)
+    NQ = S // block
+    sb, sh = mask_strides if mask_strides is not None else (H * NQ, NQ)
+    if block in (64, 128) and S % block == 0 and Sk % block == 0:
+        rows = _meta_rows(B, H, NQ, int(sb), int(sh))
+        _need_elems("mask", m, rows * (Sk // block))
+        _need_elems("variable_block_sizes", vbs, Sk // block)
+    order = torch.empty(max(B * H * NQ, 0), dtype=torch.int32, device=m.device)
+    rc = _lib.load().bsa_unit_order_bitmap(
+        _ptr(m), int(sb), int(sh), _ptr(vbs), _ptr(order), B, H, S, Sk,
+        int(block), _cur_stream(m))
+    if rc != BSA_OK:
+        raise BsaError(rc)
+    return order
+
+
+@_on_stream
 def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    mask: torch.Tensor,
                    variable_block_sizes: Optional[torch.Tensor] = None, *,
@@ -327,11 +363,14 @@ def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    need_lse: bool = True, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None,
                    k_codebook: Optional[torch.Tensor] = None,
-                   v_codebook: Optional[torch.Tensor] = None):
+                   v_codebook: Optional[torch.Tensor] = None,
+                   balance: bool = True,
+                   qblock_order: Optional[torch.Tensor] = None):
     """Jenga form.  ``mask`` is an int8 (or bool) tensor of rows of S/block
     bytes; ``mask_strides=(sb, sh)`` as in the LUT form ((0, 0) = one
     [NQ, NK] mask shared by all batches and heads).  Shapes as in the LUT
-    form."""
+    form.  ``balance`` and ``qblock_order`` as in the LUT form, with the
+    order from ``bsa_unit_order_bitmap``."""
     q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
                                               lse, need_lse, block, k_codebook,
                                               v_codebook)
@@ -345,10 +384,18 @@ def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 v_scale=vs)
     if sm_scale is None:
         sm_scale = 1.0 / (D ** 0.5)
-    rc = _lib.load().bsa_fwd_bitmap(
+    order = _launch_order(q, qblock_order, balance, B, H, NQ)
+    if order is True:
+        order = torch.empty(B * H * NQ, dtype=torch.int32, device=q.device)
+        rc = _lib.load().bsa_unit_order_bitmap(
+            _ptr(m), int(sb), int(sh), _ptr(vbs), _ptr(order), B, H, S, Sk,
+            int(block), _cur_stream(q))
+        if rc != BSA_OK:
+            raise BsaError(rc)
+    rc = _lib.load().bsa_fwd_bitmap_ordered(
         _ptr(q), _ptr(k), _ptr(v), kvd, _ptr(ks), _ptr(vs), _ptr(m),
-        int(sb), int(sh), _ptr(vbs), float(sm_scale), _ptr(out), _ptr(lse),
-        B, H, Hk, S, Sk, D, int(block), _cur_stream(q))
+        int(sb), int(sh), _ptr(vbs), _ptr(order), float(sm_scale), _ptr(out),
+        _ptr(lse), B, H, Hk, S, Sk, D, int(block), _cur_stream(q))
     if rc != BSA_OK:
         raise BsaError(rc)
     return out, lse

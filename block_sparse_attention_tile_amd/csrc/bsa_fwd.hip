@@ -5,7 +5,8 @@
 //
 //  A1  unit id -> (b, h, qb), with workgroups of consecutive ids spread so
 //      that each XCD (and its L2) serves a contiguous range of heads.  The
-//      LUT form may take qb from a launch order (bsa_fwd_lut_ordered; the
+//      unit may take qb from a launch order (bsa_fwd_lut_ordered,
+//      bsa_fwd_bitmap_ordered; the
 //      order pass in bsa_order.hip ranks each head's units heaviest first,
 //      so units of similar length run side by side and stay at the same
 //      point of their key sweeps, sharing K/V in L2).  Query head h reads
@@ -993,15 +994,13 @@ extern "C" bsa_status bsa_fwd_lut(const void* q, const void* k, const void* v,
                              Hk, S, Sk, D, block, stream);
 }
 
-extern "C" bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v,
-                                     int32_t kv_dtype, const float* k_scale,
-                                     const float* v_scale, const int8_t* mask,
-                                     int64_t mask_stride_b, int64_t mask_stride_h,
-                                     const int32_t* variable_block_sizes,
-                                     float sm_scale, void* out, float* lse,
-                                     int32_t B, int32_t H, int32_t Hk,
-                                     int32_t S, int32_t Sk, int32_t D,
-                                     int32_t block, void* stream) {
+extern "C" bsa_status bsa_fwd_bitmap_ordered(
+    const void* q, const void* k, const void* v, int32_t kv_dtype,
+    const float* k_scale, const float* v_scale, const int8_t* mask,
+    int64_t mask_stride_b, int64_t mask_stride_h,
+    const int32_t* variable_block_sizes, const int32_t* qblock_order,
+    float sm_scale, void* out, float* lse, int32_t B, int32_t H, int32_t Hk,
+    int32_t S, int32_t Sk, int32_t D, int32_t block, void* stream) {
   bsa_status st = check_common(q, k, v, kv_dtype, k_scale, v_scale, out, B, H,
                                Hk, S, Sk, D, block);
   if (st != BSA_OK) return st;
@@ -1011,10 +1010,26 @@ extern "C" bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v
   FwdParams p = make_params(q, k, v, k_scale, v_scale, variable_block_sizes,
                             sm_scale, out, lse, B, H, Hk, S, Sk, block);
   p.mask = mask;
+  p.order = qblock_order;
   p.meta_sb = mask_stride_b;
   p.meta_sh = mask_stride_h;
   return dispatch<true>(p, block, kv_dtype,
                         (hipStream_t)stream);
+}
+
+extern "C" bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v,
+                                     int32_t kv_dtype, const float* k_scale,
+                                     const float* v_scale, const int8_t* mask,
+                                     int64_t mask_stride_b, int64_t mask_stride_h,
+                                     const int32_t* variable_block_sizes,
+                                     float sm_scale, void* out, float* lse,
+                                     int32_t B, int32_t H, int32_t Hk,
+                                     int32_t S, int32_t Sk, int32_t D,
+                                     int32_t block, void* stream) {
+  return bsa_fwd_bitmap_ordered(q, k, v, kv_dtype, k_scale, v_scale, mask,
+                                mask_stride_b, mask_stride_h, variable_block_sizes,
+                                nullptr, sm_scale, out, lse, B, H, Hk, S, Sk, D,
+                                block, stream);
 }
 
 extern "C" const char* bsa_status_str(int32_t status) {

@@ -233,6 +233,49 @@ bsa_status bsa_fwd_bitmap(const void* q, const void* k, const void* v,
                           int32_t block, void* stream);
 
 /*
+ * bsa_unit_order_bitmap -- launch order of the bitmap-form work units, as
+ * bsa_unit_order_lut computes it for the LUT form (not an operation of the
+ * pages: a scheduling aid).  Over the key blocks inside [0, Sk/block) that
+ * unit (b, h, qb)'s mask row selects: count = the sum of their valid keys
+ * (variable_block_sizes clamped to [0, block]; exact, a block is selected
+ * once), mean and rank value as for bsa_unit_order_lut.
+ *
+ *  mask, mask_stride_b, mask_stride_h, variable_block_sizes, B, H, S, Sk,
+ *  block        exactly as for bsa_fwd_bitmap.
+ *  order        int32 [B*H*(S/block)], device memory, written in full (as
+ *               for bsa_unit_order_lut).
+ *  stream       hipStream_t (void*), NULL = null stream.
+ *
+ * Deterministic.  Errors: BSA_ERR_NULL, BSA_ERR_SHAPE (sizes, negative
+ * strides), BSA_ERR_UNSUPPORTED (block not 64/128, S/block >
+ * BSA_MAX_ORDER_QBLOCKS, too many key blocks), BSA_ERR_HIP; on error
+ * nothing is launched.
+ */
+bsa_status bsa_unit_order_bitmap(const int8_t* mask, int64_t mask_stride_b,
+                                 int64_t mask_stride_h,
+                                 const int32_t* variable_block_sizes,
+                                 int32_t* order, int32_t B, int32_t H, int32_t S,
+                                 int32_t Sk, int32_t block, void* stream);
+
+/*
+ * bsa_fwd_bitmap_ordered -- bsa_fwd_bitmap with the work units launched in
+ * a given order.  Arguments as bsa_fwd_bitmap, plus qblock_order as for
+ * bsa_fwd_lut_ordered (NULL = q-block order, i.e. bsa_fwd_bitmap; entries
+ * clamped into [0, S/block); not a permutation leaves query blocks
+ * unwritten).  Every unit computes the same bits in any order, so the
+ * outputs equal bsa_fwd_bitmap's exactly.
+ */
+bsa_status bsa_fwd_bitmap_ordered(const void* q, const void* k, const void* v,
+                                  int32_t kv_dtype, const float* k_scale,
+                                  const float* v_scale, const int8_t* mask,
+                                  int64_t mask_stride_b, int64_t mask_stride_h,
+                                  const int32_t* variable_block_sizes,
+                                  const int32_t* qblock_order, float sm_scale,
+                                  void* out, float* lse, int32_t B, int32_t H,
+                                  int32_t Hk, int32_t S, int32_t Sk, int32_t D,
+                                  int32_t block, void* stream);
+
+/*
  * bsa_mask_to_lut -- compaction of a block map into the look-up-table form
  * (the `map_to_index` step that FastVideo "block_sparse_attn_sm100a.py"
  * runs before its from-mask launch, `block_sparse_attn_sm100a_from_mask`).

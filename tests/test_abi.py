@@ -143,6 +143,36 @@ def test_unit_order_rejects_invalid_static_arguments(over, status):
     assert unit_order(**over) == status
 
 
+def bitmap_ordered(**over):
+    args = dict(q=A, k=A, v=A, kv=0, ks=None, vs=None, mask=A, sb=8, sh=8,
+                vbs=None, order=None, scale=0.1, out=A, lse=None, B=1, H=1,
+                Hk=1, S=512, Sk=512, D=128, block=64, stream=None)
+    args.update(over)
+    return _lib.load().bsa_fwd_bitmap_ordered(*args.values())
+
+
+def unit_order_bitmap(**over):
+    args = dict(mask=A, sb=8, sh=8, vbs=None, order=A, B=1, H=1, S=512,
+                Sk=512, block=64, stream=None)
+    args.update(over)
+    return _lib.load().bsa_unit_order_bitmap(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(mask=None), api.BSA_ERR_NULL),
+    (dict(order=None), api.BSA_ERR_NULL),
+    (dict(B=0), api.BSA_ERR_SHAPE),
+    (dict(S=500), api.BSA_ERR_SHAPE),
+    (dict(Sk=96), api.BSA_ERR_SHAPE),
+    (dict(sb=-1), api.BSA_ERR_SHAPE),
+    (dict(block=32), api.BSA_ERR_UNSUPPORTED),
+    (dict(S=64 * (api.BSA_MAX_ORDER_QBLOCKS + 1)), api.BSA_ERR_UNSUPPORTED),
+    (dict(Sk=64 * 16385), api.BSA_ERR_UNSUPPORTED),
+])
+def test_unit_order_bitmap_rejects_invalid_static_arguments(over, status):
+    assert unit_order_bitmap(**over) == status
+
+
 @pytest.mark.parametrize("over,status", [
     (dict(mask=None), api.BSA_ERR_NULL),
     (dict(q=None), api.BSA_ERR_NULL),
@@ -155,6 +185,9 @@ def test_unit_order_rejects_invalid_static_arguments(over, status):
 ])
 def test_bitmap_rejects_invalid_static_arguments(over, status):
     assert bitmap(**over) == status
+    # the ordered entry point validates identically (order = NULL or not)
+    assert bitmap_ordered(**over) == status
+    assert bitmap_ordered(order=A, **over) == status
 
 
 def test_python_binding_checks_dtypes_before_calling():

@@ -1,7 +1,8 @@
-"""GPU tests of the launch order of LUT-form units (bsa_unit_order_lut) and
-of the ordered forward entry point: the order is exactly the host's stable
-sort of the attended-key counts, and the forward outputs are bit-identical
-with and without it (each unit computes the same bits in any order)."""
+"""GPU tests of the launch order of the work units (bsa_unit_order_lut,
+bsa_unit_order_bitmap) and of the ordered forward entry points: the order is
+exactly the host's stable sort of the attended-key counts, and the forward
+outputs are bit-identical with and without it (each unit computes the same
+bits in any order)."""
 
 import numpy as np
 import pytest
@@ -49,6 +50,37 @@ def expected_order(w) -> np.ndarray:
             o = sorted(range(NQ), key=lambda i: (-work[i], i))
             out[(b * H + h) * NQ:(b * H + h + 1) * NQ] = o
     return out
+
+
+def expected_order_bitmap(w) -> np.ndarray:
+    """Host reference of the bitmap-form order: as expected_order, over the
+    key blocks the unit's mask row selects (each once)."""
+    NQ, NK, B, H = w.NQ, w.NK, w.B, w.H
+    mask = w.mask.numpy().reshape(-1, NK)
+    vbs = (np.full(NK, w.block) if w.vbs is None
+           else np.clip(w.vbs.numpy(), 0, w.block))
+    sb, sh = w.mask_strides
+    out = np.empty(B * H * NQ, dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            work = []
+            for qb in range(NQ):
+                e = np.nonzero(mask[b * sb + h * sh + qb])[0]
+                count = int(vbs[e].sum())
+                mean = (int(e.sum()) * 1023 // (len(e) * max(NK - 1, 1))
+                        if len(e) else 0)
+                work.append(min(count // 64, 2**21 - 1) * 1024 + 1023 - mean)
+            o = sorted(range(NQ), key=lambda i: (-work[i], i))
+            out[(b * H + h) * NQ:(b * H + h + 1) * NQ] = o
+    return out
+
+
+def gpu_order_bitmap(w, d):
+    o = bsa.bsa_unit_order_bitmap(d["mask"], d["vbs"], B=w.B, H=w.H, S=w.S,
+                                  Sk=w.Sk, block=w.block,
+                                  mask_strides=w.mask_strides)
+    torch.cuda.synchronize()
+    return o.cpu().numpy()
 
 
 def gpu_order(w, d):
@@ -257,3 +289,75 @@ def test_default_ordered_launch_is_bitwise_the_qblock_order(label, kw):
         res.append((out, lse))
     assert not torch.isnan(res[0][0].float()).any()
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+BITMAP_CASES = [
+    ("rand_bitmap64", dict(seed=321, B=2, H=3, S=64 * 37, block=64,
+                           form="bitmap", density=0.4, vbs_mode="random")),
+    ("rand_bitmap128_shared", dict(seed=322, B=2, H=2, S=128 * 20, block=128,
+                                   form="bitmap", shared_meta=True,
+                                   density=0.6, vbs_mode="partial")),
+    ("rand_bitmap64_rect", dict(seed=323, B=1, H=2, S=64 * 9, Sk=64 * 70,
+                                block=64, form="bitmap", density=0.1)),
+]
+
+
+@pytest.mark.parametrize("label,kw", BITMAP_CASES, ids=[c[0] for c in BITMAP_CASES])
+def test_bitmap_order_matches_host_sort(label, kw):
+    w = workloads.make_random(**kw)
+    log(f"[order] {label}: B={w.B} H={w.H} S={w.S} Sk={w.Sk} block={w.block}")
+    d = to_dev(w)
+    assert np.array_equal(gpu_order_bitmap(w, d), expected_order_bitmap(w))
+
+
+def test_bitmap_order_full_jenga_config():
+    w = workloads.make_config(1)
+    log(f"[order] {w.name}")
+    d = to_dev(w)
+    assert np.array_equal(gpu_order_bitmap(w, d), expected_order_bitmap(w))
+
+
+@pytest.mark.parametrize("label,kw", BITMAP_CASES, ids=[c[0] for c in BITMAP_CASES])
+def test_ordered_bitmap_forward_is_bitwise_the_unordered_one(label, kw):
+    w = workloads.make_random(**kw)
+    log(f"[order-fwd] bitmap {label}")
+    d = to_dev(w)
+    order = bsa.bsa_unit_order_bitmap(d["mask"], d["vbs"], B=w.B, H=w.H,
+                                      S=w.S, Sk=w.Sk, block=w.block,
+                                      mask_strides=w.mask_strides)
+    ident = torch.arange(w.NQ, dtype=torch.int32, device="cuda").repeat(w.B * w.H)
+    assert not torch.equal(order, ident)  # the ordered launch differs
+    outs = []
+    for qo in (None, order):
+        out = torch.full(tuple(w.q.shape), float("nan"), dtype=torch.bfloat16,
+                         device="cuda")
+        lse = torch.full((w.B, w.H, w.S), float("nan"), dtype=torch.float32,
+                         device="cuda")
+        bsa.bsa_fwd_bitmap(d["q"], d["k"], d["v"], d["mask"], d["vbs"],
+                           block=w.block, sm_scale=w.sm_scale,
+                           mask_strides=w.mask_strides, out=out, lse=lse,
+                           balance=False, qblock_order=qo)
+        torch.cuda.synchronize()
+        outs.append((out, lse))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
+def test_bitmap_binding_orders_large_launches_by_default():
+    """More units than run at once: the binding computes the order, and the
+    result equals the q-block-order launch bit for bit."""
+    w = workloads.make_random(324, B=1, H=20, S=64 * 64, block=64,
+                              form="bitmap", density=0.5, vbs_mode="partial")
+    assert bsa.api.launch_order_pays(w.B, w.H, w.NQ)
+    log(f"[order-fwd] bitmap default order, {w.n_units} units")
+    d = to_dev(w)
+    a = run_gpu(w, dev_inputs=d)
+    out = torch.empty(tuple(w.q.shape), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda")
+    bsa.bsa_fwd_bitmap(d["q"], d["k"], d["v"], d["mask"], d["vbs"],
+                       block=w.block, sm_scale=w.sm_scale,
+                       mask_strides=w.mask_strides, out=out, lse=lse,
+                       balance=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], out)
+    assert torch.equal(a[1], lse)
