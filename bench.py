@@ -162,15 +162,21 @@ def launch(w, d, out, lse, kernel_events=None):
     """One forward pass; lse=None is the inference route (no LSE store).
     Codebook-coded K/V are dequantised inside the call.  The LUT form first
     computes its launch order on the GPU (heaviest units first, part of the
-    step) when the launch has more units than run at once.  kernel_events=(start, end): recorded around the forward call
-    alone (after the order pass)."""
+    step) when the launch has more units than run at once, in either form.
+    kernel_events=(start, end): recorded around the forward call alone
+    (after the order pass)."""
     cb = dict(k_codebook=d.get("k_codebook"), v_codebook=d.get("v_codebook"))
     order = None
-    if w.form == "lut" and bsa.api.launch_order_pays(w.B, w.H, w.NQ):
-        order = bsa.bsa_unit_order_lut(d["q2k_idx"], d["q2k_num"], d["vbs"],
-                                       B=w.B, H=w.H, S=w.S, Sk=w.Sk,
-                                       block=w.block,
-                                       meta_strides=w.meta_strides)
+    if bsa.api.launch_order_pays(w.B, w.H, w.NQ):
+        if w.form == "lut":
+            order = bsa.bsa_unit_order_lut(d["q2k_idx"], d["q2k_num"], d["vbs"],
+                                           B=w.B, H=w.H, S=w.S, Sk=w.Sk,
+                                           block=w.block,
+                                           meta_strides=w.meta_strides)
+        else:
+            order = bsa.bsa_unit_order_bitmap(d["mask"], d["vbs"], B=w.B, H=w.H,
+                                              S=w.S, Sk=w.Sk, block=w.block,
+                                              mask_strides=w.mask_strides)
     if kernel_events is not None:
         kernel_events[0].record()
     if w.form == "lut":
@@ -185,7 +191,8 @@ def launch(w, d, out, lse, kernel_events=None):
                            block=w.block, sm_scale=w.sm_scale,
                            k_scale=d["k_scale"], v_scale=d["v_scale"], **cb,
                            mask_strides=w.mask_strides, out=out, lse=lse,
-                           need_lse=lse is not None)
+                           need_lse=lse is not None, balance=False,
+                           qblock_order=order)
     if kernel_events is not None:
         kernel_events[1].record()
 
@@ -522,6 +529,7 @@ def main() -> int:
         ms = sum(a.elapsed_time(b) for a, b in pairs_ev) / args.steps
         del scrub
         ms_kernel = None
+        kernel_stats = None
     else:
         kev = [(torch.cuda.Event(enable_timing=True),
                 torch.cuda.Event(enable_timing=True))
@@ -533,7 +541,15 @@ def main() -> int:
         torch.cuda.synchronize()
         ms = ev0.elapsed_time(ev1) / args.steps
         # the forward kernel alone (the dominant kernel of the step)
-        ms_kernel = sum(a.elapsed_time(b) for a, b in kev) / args.steps
+        per_launch = sorted(a.elapsed_time(b) for a, b in kev)
+        ms_kernel = sum(per_launch) / args.steps
+        n = len(per_launch)
+        kernel_stats = {
+            "mean": round(ms_kernel, 5),
+            "median": round((per_launch[(n - 1) // 2] + per_launch[n // 2]) / 2, 5),
+            "min": round(per_launch[0], 5),
+            "max": round(per_launch[-1], 5),
+        }
     wall = time.perf_counter() - t0
     progress(f"timed {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)"
              + ("" if ms_kernel is None else
@@ -574,10 +590,14 @@ def main() -> int:
                            round(traffic / (ms * 1e-3) / 1e9, 1)),
             "l2_hit_rate": counters.get("l2_hit_rate"),
             "launch_order": ("heaviest units first (order pass in the step)"
-                             if w.form == "lut" and
-                             bsa.api.launch_order_pays(w.B, w.H, w.NQ)
+                             if bsa.api.launch_order_pays(w.B, w.H, w.NQ)
                              else "q-block"),
+            "key_split": (w.block == 64 and not (w.kv_fp8 or args.kv) and
+                          w.n_units <= bsa.BSA_FWD_KEY_SPLIT_MAX_UNITS),
             "fwd_kernel_ms": None if ms_kernel is None else round(ms_kernel, 5),
+            # per-launch forward kernel times over the timed steps (HIP events
+            # on the launch stream)
+            "fwd_kernel_ms_stats": kernel_stats,
         },
         "roofline": {
             "bound": "mfma",

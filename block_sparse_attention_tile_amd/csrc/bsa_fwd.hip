@@ -1,13 +1,16 @@
 // bsa_fwd.hip -- block-sparse attention forward for MI355X (gfx950 / CDNA4).
 //
 // One workgroup computes one work unit: the `BLK` query rows of query block
-// qb of head h of batch b.  The steps, in order:
+// qb of head h of batch b.  In a short launch (block 64, bf16 K/V, at most
+// BSA_FWD_KEY_SPLIT_MAX_UNITS units) the workgroup holds two groups of waves
+// that each sweep part of the unit's selected blocks for the same query
+// rows; their partial results are merged before A8.  The steps, in order:
 //
 //  A1  unit id -> (b, h, qb), with workgroups of consecutive ids spread so
 //      that each XCD (and its L2) serves a contiguous range of heads.  The
 //      unit may take qb from a launch order (bsa_fwd_lut_ordered,
-//      bsa_fwd_bitmap_ordered; the
-//      order pass in bsa_order.hip ranks each head's units heaviest first,
+//      bsa_fwd_bitmap_ordered; the order pass in bsa_order.hip ranks each
+//      head's units heaviest first,
 //      so units of similar length run side by side and stay at the same
 //      point of their key sweeps, sharing K/V in L2).  Query head h reads
 //      K/V head h / (H/Hk) (grouped-query attention; rocke
@@ -881,8 +884,9 @@ bsa_status dispatch_kv(const FwdParams& p, int kv, hipStream_t s) {
     default:
       // short launches split each unit's keys over two wave groups (with
       // more units than run at once, whole units balance better)
-      if (BLK == 64 && p.n_units <= BSA_FWD_KEY_SPLIT_MAX_UNITS)
-        return launch<BLK, BSA_KV_BF16, BITMAP, 2>(p, s);
+      if constexpr (BLK == 64)
+        if (p.n_units <= BSA_FWD_KEY_SPLIT_MAX_UNITS)
+          return launch<BLK, BSA_KV_BF16, BITMAP, 2>(p, s);
       return launch<BLK, BSA_KV_BF16, BITMAP, 1>(p, s);
   }
 }
