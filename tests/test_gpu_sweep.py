@@ -92,6 +92,42 @@ def test_forward_sweep(case):
     check(o_gpu, l_gpu, o_ref, l_ref, f"sweep{case}", o_rel=o_rel, o_abs=o_abs)
 
 
+def draw_wide(seed: int):
+    """A block-64 bf16 case with more work units than a key-split launch
+    takes (BSA_FWD_KEY_SPLIT_MAX_UNITS), so one wave group sweeps each
+    unit: the small sweep above runs split launches at block 64."""
+    r = random.Random(seed)
+    Hk = r.choice((1, 2, 4))
+    NQ = r.randint(2, 6)
+    B = r.choice((1, 2))
+    lo = bsa.BSA_FWD_KEY_SPLIT_MAX_UNITS + 1
+    g = -(-lo // (B * NQ * Hk))  # heads per K/V head that pass the threshold
+    H = Hk * (g + r.randint(0, 2))
+    NK = r.randint(1, 24)
+    kw = dict(B=B, H=H, Hk=Hk, S=NQ * 64, Sk=NK * 64, block=64,
+              form=r.choice(("lut", "bitmap")),
+              density=r.choice((0.1, 0.3, 0.6, 1.0)),
+              vbs_mode=r.choice(VBS), shared_meta=r.random() < 0.2)
+    if kw["form"] == "lut":
+        kw["count_mode"] = r.choice(("fixed", "uniform"))
+        kw["sort"] = r.random() < 0.5
+    return kw
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_forward_sweep_wide(case):
+    kw = draw_wide(6000 + case)
+    w = workloads.make_random(7000 + case, **kw)
+    assert w.n_units > bsa.BSA_FWD_KEY_SPLIT_MAX_UNITS
+    log(f"[sweep fwd wide {case}] units={w.n_units} {kw}")
+    out, lse = run_gpu(w)
+    o_ref, l_ref = run_oracle(w)
+    o_gpu, l_gpu = out.float().cpu().numpy(), lse.cpu().numpy()
+    o_abs, o_rel = scaled_input_bounds(float(w.v.float().abs().max()))
+    check(o_gpu, l_gpu, o_ref.reshape(o_gpu.shape), l_ref.reshape(l_gpu.shape),
+          f"sweep_wide{case}", o_rel=o_rel, o_abs=o_abs)
+
+
 @pytest.mark.parametrize("case", range(12))
 def test_backward_sweep(case):
     kw = draw(3000 + case, backward=True)
