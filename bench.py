@@ -464,9 +464,9 @@ def main() -> int:
     if args.record_traffic:
         return record_traffic(args.record_traffic, args.workload)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the forward "
-              "pass on a single MI355X (each GPU would take its own share of "
-              "heads with no communication); --gpus must be 1.",
+        print("bench.py measures one GPU only: the forward pass runs on a "
+              "single MI355X (each GPU would take its own share of heads "
+              "with no communication); --gpus must be 1.",
               file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
