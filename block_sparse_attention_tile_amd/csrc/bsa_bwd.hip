@@ -342,7 +342,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void dq_kernel(BwdParams p) {
 
   // Tiles are cut from the stream of the unit's valid keys (a tile may
   // span blocks; only the last one is partial).
-  ListCursor cursor{list, nsel, 0, 0u};
+  ListCursor cursor{list, nsel, 0, 0u, 0u};
   cursor.reset(lane);
   Walk walk{0, 0};
   auto issue = [&](int stg) -> int {

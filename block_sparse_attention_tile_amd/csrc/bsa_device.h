@@ -99,16 +99,22 @@ struct Tile {
 // Reader of the selected-block list ((kb << 8) | nv per entry, nv = valid
 // keys).  Entries are fetched from LDS 64 at a time into one VGPR (lane i
 // holds entry base + i) and picked out with v_readlane, so moving to the
-// next block costs no LDS round trip on the critical path.
+// next block costs no LDS round trip on the critical path.  The following
+// 64 entries are fetched one chunk ahead (into `ahead`): a chunk is read
+// long after its load was issued, so the walk never waits on the LDS
+// counter, which would also wait for every LDS read issued before it (the
+// K operand reads of the tile in hand).
 struct ListCursor {
   const uint32_t* list;
   int nsel;
   int base;
   uint32_t chunk;
+  uint32_t ahead;
 
   __device__ __forceinline__ void reset(int lane) {
     base = 0;
     chunk = lane < nsel ? list[lane] : 0u;
+    ahead = 64 + lane < nsel ? list[64 + lane] : 0u;
   }
 
   // Entries are visited in increasing order, one at a time.
@@ -121,7 +127,8 @@ struct ListCursor {
     if (e < nsel) {
       if (e >= base + 64) {
         base += 64;
-        chunk = base + lane < nsel ? list[base + lane] : 0u;
+        chunk = ahead;
+        ahead = base + 64 + lane < nsel ? list[base + 64 + lane] : 0u;
       }
       const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)chunk, e - base);
       t.kb = (int)(x >> 8);

@@ -563,7 +563,7 @@ __global__ __launch_bounds__(BLK * 2 * KS, (waves_per_simd<BLK, KV>())) void bsa
     dvo[i] = (uint32_t)(j * 1024 + l4 * ROWB + (((pos ^ (2 * l4)) ^ ((j & 1) << 3)) << 4));
   }
 
-  ListCursor cursor{list + e0, nsel_g, 0, 0u};
+  ListCursor cursor{list + e0, nsel_g, 0, 0u, 0u};
   [[maybe_unused]] Fp8Staging<NT> st;
   [[maybe_unused]] float ksc_cur = 1.f, vsc_cur = 1.f, ksc_nxt = 1.f, vsc_nxt = 1.f;
 
