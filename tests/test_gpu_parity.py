@@ -86,6 +86,20 @@ SMALL = [
     # the 64-entry list chunks in the middle of a tile
     ("lut64_many_tiny", dict(seed=129, B=1, H=1, S=1024, Sk=16384, block=64,
                              density=0.9, vbs_mode="tiny")),
+    # lists of exactly 64, 65, 128 and 129 selected blocks of 1-4 keys: the
+    # walk's list chunk and the one read ahead end exactly at, or one entry
+    # past, a 64-entry boundary (key-split launches, then one with more
+    # units than a split launch takes)
+    ("lut64_list64", dict(seed=130, B=1, H=1, S=256, Sk=4096, block=64,
+                          density=1.0, vbs_mode="tiny")),
+    ("lut64_list65", dict(seed=131, B=1, H=2, S=256, Sk=4160, block=64,
+                          density=1.0, vbs_mode="tiny")),
+    ("bitmap64_list128", dict(seed=132, B=1, H=1, S=512, Sk=8192, block=64,
+                              form="bitmap", density=1.0, vbs_mode="tiny")),
+    ("lut64_list129", dict(seed=133, B=1, H=1, S=512, Sk=8256, block=64,
+                           density=1.0, vbs_mode="tiny")),
+    ("wide_lut64_list129", dict(seed=134, B=1, H=9, S=4096, Sk=8256, block=64,
+                                density=1.0, vbs_mode="tiny")),
 ]
 
 
