@@ -158,6 +158,9 @@ def codebook_recode(w, kind: str):
     return w
 
 
+FP8_ROUTE = "auto"  # set from --fp8-route
+
+
 def launch(w, d, out, lse, kernel_events=None):
     """One forward pass; lse=None is the inference route (no LSE store).
     Codebook-coded K/V are dequantised inside the call.  The LUT form first
@@ -185,16 +188,27 @@ def launch(w, d, out, lse, kernel_events=None):
                         k_scale=d["k_scale"], v_scale=d["v_scale"], **cb,
                         meta_strides=w.meta_strides, out=out, lse=lse,
                         need_lse=lse is not None, balance=False,
-                        qblock_order=order)
+                        qblock_order=order, fp8_route=FP8_ROUTE)
     else:
         bsa.bsa_fwd_bitmap(d["q"], d["k"], d["v"], d["mask"], d["vbs"],
                            block=w.block, sm_scale=w.sm_scale,
                            k_scale=d["k_scale"], v_scale=d["v_scale"], **cb,
                            mask_strides=w.mask_strides, out=out, lse=lse,
                            need_lse=lse is not None, balance=False,
-                           qblock_order=order)
+                           qblock_order=order, fp8_route=FP8_ROUTE)
     if kernel_events is not None:
         kernel_events[1].record()
+
+
+def kv_route(w, args):
+    """How the step turns the workload's K/V into the kernel's operands."""
+    if args.kv or w.kv_codebook:
+        return "codebook dequantisation pass, then the scaled-bf16 kernel"
+    if w.kv_fp8:
+        if bsa.api._widen_fp8(w.B, w.H, w.NQ, args.fp8_route):
+            return "fp8 widening pass, then the scaled-bf16 kernel"
+        return "fp8 widened inside the kernel"
+    return "bf16"
 
 
 def stored_counters(workload_name: str) -> dict:
@@ -440,6 +454,9 @@ def main() -> int:
                     help="re-code the workload's K/V as i8 / packed-i4 "
                          "codebook codes (each step then includes the "
                          "dequantisation pass)")
+    ap.add_argument("--fp8-route", default="auto", choices=bsa.api.FP8_ROUTES,
+                    help="fp8 K/V: widened inside the kernel, in a pass of "
+                         "their own first, or by launch size (auto)")
     ap.add_argument("--no-lse", action="store_true",
                     help="inference route: the forward pass without the LSE "
                          "output")
@@ -460,6 +477,8 @@ def main() -> int:
                          "runs from PMC_DIR and store the workload's HBM "
                          "bytes per launch")
     args = ap.parse_args()
+    global FP8_ROUTE
+    FP8_ROUTE = args.fp8_route
 
     if args.record_traffic:
         return record_traffic(args.record_traffic, args.workload)
@@ -594,6 +613,7 @@ def main() -> int:
                              else "q-block"),
             "key_split": (w.block == 64 and not (w.kv_fp8 or args.kv) and
                           w.n_units <= bsa.BSA_FWD_KEY_SPLIT_MAX_UNITS),
+            "kv_route": kv_route(w, args),
             "fwd_kernel_ms": None if ms_kernel is None else round(ms_kernel, 5),
             # per-launch forward kernel times over the timed steps (HIP events
             # on the launch stream)

@@ -173,12 +173,40 @@ def bsa_codebook_dequant(codes: torch.Tensor, codebook: torch.Tensor
     return out
 
 
+FP8_ROUTES = ("auto", "kernel", "widen")
+_FP8_LEVELS = {}
+
+
+def _fp8_levels(device) -> torch.Tensor:
+    """The 256 fp8 e4m3 values as an i8 codebook: level l holds the value of
+    the code byte l ^ 0x80 (level = code + 128, the codebook convention).
+    Every value is exact in f32 and in bf16."""
+    key = str(device)
+    if key not in _FP8_LEVELS:
+        b = (torch.arange(256, dtype=torch.int32) ^ 0x80).to(torch.uint8)
+        _FP8_LEVELS[key] = b.view(torch.float8_e4m3fn).to(torch.float32).to(device)
+    return _FP8_LEVELS[key]
+
+
+def _widen_fp8(B: int, H: int, NQ: int, route: str) -> bool:
+    """Whether fp8 K/V are widened to bf16 in a pass of their own before the
+    forward (then the kernel loads them like scaled bf16) instead of inside
+    the kernel.  The two give the same bits; the pass pays on launches of
+    more units than run at once, where each key block is gathered many
+    times ("auto")."""
+    if route not in FP8_ROUTES:
+        raise ValueError(f"fp8_route must be one of {FP8_ROUTES}")
+    if route == "auto":
+        return B * H * NQ > ORDER_MIN_UNITS
+    return route == "widen"
+
+
 def _i32(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
     return None if t is None else t.to(torch.int32).contiguous()
 
 
 def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block,
-             k_codebook=None, v_codebook=None):
+             k_codebook=None, v_codebook=None, fp8_route="auto"):
     if q.dtype != torch.bfloat16 or q.dim() != 4:
         raise TypeError("q must be a 4-D bf16 [B, H, S, D] tensor")
     if not q.is_cuda:
@@ -192,6 +220,13 @@ def _prepare(q, k, v, k_scale, v_scale, out, lse, need_lse, block,
             raise TypeError("k and v must have the same dtype")
         k = bsa_codebook_dequant(k, k_codebook)
         v = bsa_codebook_dequant(v, v_codebook)
+        kvd = BSA_KV_BF16_SCALED
+    elif k.dtype == torch.float8_e4m3fn and v.dtype == k.dtype and \
+            _widen_fp8(int(q.shape[0]), int(q.shape[1]),
+                       int(q.shape[2]) // block if block > 0 else 0, fp8_route):
+        levels = _fp8_levels(q.device)
+        k = bsa_codebook_dequant(k.view(torch.int8), levels)
+        v = bsa_codebook_dequant(v.view(torch.int8), levels)
         kvd = BSA_KV_BF16_SCALED
     else:
         kvd = None
@@ -248,7 +283,8 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 k_codebook: Optional[torch.Tensor] = None,
                 v_codebook: Optional[torch.Tensor] = None,
                 balance: bool = True,
-                qblock_order: Optional[torch.Tensor] = None):
+                qblock_order: Optional[torch.Tensor] = None,
+                fp8_route: str = "auto"):
     """VSA form.  Returns ``(out, lse)`` (``lse`` is None if not needed).
     ``q`` is ``[B, H, S, D]``, ``k``/``v`` ``[B, Hk, Sk, D]`` (query head h
     reads K/V head h // (H // Hk)).  ``meta_strides=(sb, sh)``: the LUT row
@@ -258,10 +294,13 @@ def bsa_fwd_lut(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     bits either way); skipped beyond BSA_MAX_ORDER_QBLOCKS query blocks and
     for launches of at most ORDER_MIN_UNITS units, which all run at once.
     ``qblock_order``: an order computed beforehand (int32 ``[B*H*NQ]``, as
-    ``bsa_unit_order_lut`` returns it) to launch with instead."""
+    ``bsa_unit_order_lut`` returns it) to launch with instead.
+    ``fp8_route`` (fp8 K/V): "kernel" widens the codes inside the attention
+    kernel, "widen" in a pass of their own first (bf16 K/V of the call's
+    own), "auto" the latter past ORDER_MIN_UNITS units; same bits."""
     q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
                                               lse, need_lse, block, k_codebook,
-                                              v_codebook)
+                                              v_codebook, fp8_route)
     B, H, S, D = q.shape
     Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
@@ -365,15 +404,16 @@ def bsa_fwd_bitmap(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    k_codebook: Optional[torch.Tensor] = None,
                    v_codebook: Optional[torch.Tensor] = None,
                    balance: bool = True,
-                   qblock_order: Optional[torch.Tensor] = None):
+                   qblock_order: Optional[torch.Tensor] = None,
+                   fp8_route: str = "auto"):
     """Jenga form.  ``mask`` is an int8 (or bool) tensor of rows of S/block
     bytes; ``mask_strides=(sb, sh)`` as in the LUT form ((0, 0) = one
     [NQ, NK] mask shared by all batches and heads).  Shapes as in the LUT
-    form.  ``balance`` and ``qblock_order`` as in the LUT form, with the
-    order from ``bsa_unit_order_bitmap``."""
+    form.  ``balance``, ``qblock_order`` and ``fp8_route`` as in the LUT
+    form, with the order from ``bsa_unit_order_bitmap``."""
     q, k, v, kvd, ks, vs, out, lse = _prepare(q, k, v, k_scale, v_scale, out,
                                               lse, need_lse, block, k_codebook,
-                                              v_codebook)
+                                              v_codebook, fp8_route)
     B, H, S, D = q.shape
     Hk, Sk = int(k.shape[1]), int(k.shape[2])
     NQ = S // block
