@@ -8,12 +8,13 @@
 // from-mask launch (`block_sparse_attn_sm100a_from_mask`); the padding is
 // never read by the forward pass (`is_supported` docstring).
 //
-// One wave per row.  Each pass over the row covers 256 key blocks: every
-// lane tests 4 consecutive mask bytes, the wave forms the exclusive prefix
-// of the per-lane counts with three ballots (count = b0 + 2 b1 + 4 b2), and
-// each lane writes its selected indices at their final positions.  The
-// padding is then written with one store per lane per 64 entries.  Integer
-// work only: the result is exact.
+// One wave per row.  Each pass over the row covers 1024 key blocks: every
+// lane loads 16 consecutive mask bytes at once (a row of up to 1024 blocks
+// is one load per lane, so a wave waits for memory once), the wave forms
+// the exclusive prefix of the per-lane counts (0..16) with five ballots
+// (count = sum of 2^b over its bits b), and each lane writes its selected
+// indices at their final positions.  The padding is then written with one
+// store per lane per 64 entries.  Integer work only: the result is exact.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -22,13 +23,22 @@
 
 namespace {
 
-constexpr int WAVES = 4;  // rows per workgroup
-constexpr int CHUNK = 256;  // key blocks per wave pass (64 lanes x 4)
+constexpr int WAVES = 4;    // rows per workgroup
+constexpr int PER_LANE = 16;  // mask bytes per lane and pass
+constexpr int CHUNK = 64 * PER_LANE;  // key blocks per wave pass
 
 __device__ __forceinline__ int prefix_lt(uint64_t ballot) {
   // number of set bits of `ballot` in lanes below this one
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(ballot >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)ballot, 0));
+}
+
+// bit i of the result: byte i of w is nonzero (i < 4)
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
+  uint32_t b = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b |= ((w >> (8 * i)) & 0xFFu) ? (1u << i) : 0u;
+  return b;
 }
 
 __global__ __launch_bounds__(WAVES * 64) void mask_to_lut_kernel(
@@ -39,32 +49,48 @@ __global__ __launch_bounds__(WAVES * 64) void mask_to_lut_kernel(
   if (row >= rows) return;  // whole wave leaves together
   const int8_t* m = mask + row * nk;
   int32_t* out = idx + row * nk;
-  const bool aligned = ((uintptr_t)m & 3u) == 0;
+  const bool aligned16 = ((uintptr_t)m & 15u) == 0;
+  const bool aligned4 = ((uintptr_t)m & 3u) == 0;
 
   int n = 0;  // entries written so far (wave-uniform)
   for (int base = 0; base < nk; base += CHUNK) {
-    const int k0 = base + 4 * lane;
+    const int k0 = base + PER_LANE * lane;
     uint32_t bits = 0;  // bit i: key block k0 + i selected
-    if (aligned && k0 + 4 <= nk) {
-      const uint32_t w = *(const uint32_t*)(m + k0);
+    if (aligned16 && k0 + PER_LANE <= nk) {
+      const uint4 w = *(const uint4*)(m + k0);
+      bits = nonzero_bytes(w.x) | (nonzero_bytes(w.y) << 4) | (nonzero_bytes(w.z) << 8) |
+             (nonzero_bytes(w.w) << 12);
+    } else if (aligned4 && k0 + PER_LANE <= nk) {
+      const uint32_t* m4 = (const uint32_t*)(m + k0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bits |= ((w >> (8 * i)) & 0xFFu) ? (1u << i) : 0u;
+      for (int i = 0; i < PER_LANE / 4; ++i) bits |= nonzero_bytes(m4[i]) << (4 * i);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < PER_LANE; ++i)
         if (k0 + i < nk && m[k0 + i] != 0) bits |= 1u << i;
     }
     const int cnt = __builtin_popcount(bits);
-    const uint64_t b0 = __ballot(cnt & 1);
-    const uint64_t b1 = __ballot(cnt & 2);
-    const uint64_t b2 = __ballot(cnt & 4);
-    int pos = n + prefix_lt(b0) + 2 * prefix_lt(b1) + 4 * prefix_lt(b2);
+    int pos = n, total = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (bits & (1u << i)) out[pos++] = k0 + i;
-    n += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+    for (int b = 0; b < 5; ++b) {
+      const uint64_t bal = __ballot((cnt >> b) & 1);
+      pos += prefix_lt(bal) << b;
+      total += __popcll(bal) << b;
+    }
+    while (bits) {
+      out[pos++] = k0 + __builtin_ctz(bits);
+      bits &= bits - 1u;
+    }
+    n += total;
   }
-  for (int j = n + lane; j < nk; j += 64) out[j] = -1;
+  // padding: single entries up to a 16-byte boundary, then 16-byte stores
+  int j0 = n;
+  while (j0 < nk && ((uintptr_t)(out + j0) & 15u) != 0) ++j0;  // at most 3 steps
+  if (n + lane < j0) out[n + lane] = -1;
+  const int nq = (nk - j0) >> 2;  // whole 4-entry groups
+  int4* o4 = (int4*)(out + j0);
+  for (int q = lane; q < nq; q += 64) o4[q] = int4{-1, -1, -1, -1};
+  for (int j = j0 + 4 * nq + lane; j < nk; j += 64) out[j] = -1;
   if (lane == 0) num[row] = n;
 }
 

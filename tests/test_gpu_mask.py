@@ -52,6 +52,12 @@ CASES = [
     ("sparse_1000", 8, 33, 1000, 0.01, "01"),
     ("max_nk", 9, 2, 16384, 0.5, "bytes"),
     ("video_like", 10, 18432, 768, 96 / 768, "01"),
+    # around the kernel's 1024-block passes (16 mask bytes per lane)
+    ("pass_1023", 11, 6, 1023, 0.4, "bytes"),
+    ("pass_1024", 12, 6, 1024, 0.6, "01"),
+    ("pass_1025", 13, 6, 1025, 0.5, "bytes"),
+    ("pass_2049_dense", 14, 3, 2049, 0.95, "01"),
+    ("rows_4b_aligned_1000", 15, 9, 1000, 0.3, "bytes"),
 ]
 
 
@@ -64,7 +70,7 @@ def test_mask_to_lut_bit_exact(label, seed, rows, nk, density, values):
 
 def test_mask_to_lut_unaligned_rows_and_base():
     """Row starts that are not 4-byte aligned (odd nk, base offset 1) take
-    the byte-wise path."""
+    the byte-wise path (4- and 16-byte aligned rows take word loads)."""
     m = random_mask(7, 40, 131, 0.4)
     big = torch.zeros(m.numel() + 1, dtype=torch.int8, device="cuda")
     big[1:] = m.reshape(-1).cuda()
