@@ -87,7 +87,13 @@ typedef enum {
                         each key block dequantised as code value times its
                         fp32 scale (rocke "sage_attention.py", module
                         docstring: K/V dequantised per block before the score
-                        and the PV product)                                   */
+                        and the PV product).  Widened inside the kernel.
+                        Equivalent, bit for bit: bsa_codebook_dequant with
+                        kind BSA_CODEBOOK_I8 on the same bytes and the 256
+                        fp8 values as the table (entry l = the value of byte
+                        l ^ 0x80), then BSA_KV_BF16_SCALED with the same
+                        scales; faster on launches of many units, at the
+                        cost of bf16 copies of K and V                        */
   BSA_KV_BF16_SCALED = 2 /* K and V are bf16 values [B, H, S, D] times their
                         per-block fp32 scale: the form the codebook modes of
                         the same page take after bsa_codebook_dequant (value
