@@ -158,16 +158,14 @@ def codebook_recode(w, kind: str):
     return w
 
 
-FP8_ROUTE = "auto"  # set from --fp8-route
-
-
-def launch(w, d, out, lse, kernel_events=None):
+def launch(w, d, out, lse, kernel_events=None, fp8_route="auto"):
     """One forward pass; lse=None is the inference route (no LSE store).
     Codebook-coded K/V are dequantised inside the call.  The LUT form first
     computes its launch order on the GPU (heaviest units first, part of the
     step) when the launch has more units than run at once, in either form.
     kernel_events=(start, end): recorded around the forward call alone
-    (after the order pass)."""
+    (after the order pass).  fp8_route: how fp8 K/V are widened (the
+    binding's ``fp8_route``)."""
     cb = dict(k_codebook=d.get("k_codebook"), v_codebook=d.get("v_codebook"))
     order = None
     if bsa.api.launch_order_pays(w.B, w.H, w.NQ):
@@ -188,14 +186,14 @@ def launch(w, d, out, lse, kernel_events=None):
                         k_scale=d["k_scale"], v_scale=d["v_scale"], **cb,
                         meta_strides=w.meta_strides, out=out, lse=lse,
                         need_lse=lse is not None, balance=False,
-                        qblock_order=order, fp8_route=FP8_ROUTE)
+                        qblock_order=order, fp8_route=fp8_route)
     else:
         bsa.bsa_fwd_bitmap(d["q"], d["k"], d["v"], d["mask"], d["vbs"],
                            block=w.block, sm_scale=w.sm_scale,
                            k_scale=d["k_scale"], v_scale=d["v_scale"], **cb,
                            mask_strides=w.mask_strides, out=out, lse=lse,
                            need_lse=lse is not None, balance=False,
-                           qblock_order=order, fp8_route=FP8_ROUTE)
+                           qblock_order=order, fp8_route=fp8_route)
     if kernel_events is not None:
         kernel_events[1].record()
 
@@ -477,8 +475,6 @@ def main() -> int:
                          "runs from PMC_DIR and store the workload's HBM "
                          "bytes per launch")
     args = ap.parse_args()
-    global FP8_ROUTE
-    FP8_ROUTE = args.fp8_route
 
     if args.record_traffic:
         return record_traffic(args.record_traffic, args.workload)
@@ -524,7 +520,7 @@ def main() -> int:
 
     progress(f"warmup {args.warmup} steps on {w.name}")
     for _ in range(args.warmup):
-        launch(w, d, out, lse)
+        launch(w, d, out, lse, fp8_route=args.fp8_route)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -542,7 +538,7 @@ def main() -> int:
         for i in range(args.steps):
             scrub.fill_(float(i))
             pairs_ev[i][0].record(stream)
-            launch(w, d, out, lse)
+            launch(w, d, out, lse, fp8_route=args.fp8_route)
             pairs_ev[i][1].record(stream)
         torch.cuda.synchronize()
         ms = sum(a.elapsed_time(b) for a, b in pairs_ev) / args.steps
@@ -555,7 +551,7 @@ def main() -> int:
                for _ in range(args.steps)]
         ev0.record(stream)
         for i in range(args.steps):
-            launch(w, d, out, lse, kernel_events=kev[i])
+            launch(w, d, out, lse, kernel_events=kev[i], fp8_route=args.fp8_route)
         ev1.record(stream)
         torch.cuda.synchronize()
         ms = ev0.elapsed_time(ev1) / args.steps
