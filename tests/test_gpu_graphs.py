@@ -1,7 +1,8 @@
 """HIP graph capture of the library's calls.
 
 The forward pass (LUT form in a key-split launch and in an ordered launch
-of more units than run at once, bitmap form), the backward pass with a
+of more units than run at once, bitmap form, fp8 K/V widened by the
+binding), the backward pass with a
 caller-owned workspace and the allocation-free backward are each captured
 once into a torch CUDA graph (a hipGraph on ROCm) and replayed several
 times, with eager library work, output resets and synchronisations between
@@ -68,6 +69,10 @@ FWD = [
                            vbs_mode="edges"), True),
     ("bitmap128", dict(seed=503, B=1, H=6, S=2048, block=128, form="bitmap",
                        density=0.4, vbs_mode="partial"), False),
+    # fp8 K/V past one launch of units: the binding widens them to bf16
+    # (a pass and a torch allocation inside the captured call)
+    ("fp8_widened", dict(seed=504, B=1, H=20, S=4096, block=64, kv="fp8",
+                         density=0.3, vbs_mode="partial"), True),
 ]
 
 
@@ -86,16 +91,17 @@ def test_forward_graph_replays_match_eager(label, kw, ordered):
                                        meta_strides=w.meta_strides)
 
     def call(out, lse):
+        sc = dict(k_scale=d["k_scale"], v_scale=d["v_scale"])
         if w.form == "lut":
             bsa.bsa_fwd_lut(d["q"], d["k"], d["v"], d["q2k_idx"], d["q2k_num"],
                             d["vbs"], block=w.block, sm_scale=w.sm_scale,
                             meta_strides=w.meta_strides, out=out, lse=lse,
-                            balance=False, qblock_order=order)
+                            balance=False, qblock_order=order, **sc)
         else:
             bsa.bsa_fwd_bitmap(d["q"], d["k"], d["v"], d["mask"], d["vbs"],
                                block=w.block, sm_scale=w.sm_scale,
                                mask_strides=w.mask_strides, out=out, lse=lse,
-                               balance=False)
+                               balance=False, **sc)
 
     def buffers():
         return (torch.empty(tuple(w.q.shape), dtype=torch.bfloat16, device="cuda"),
