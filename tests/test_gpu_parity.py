@@ -208,42 +208,6 @@ def test_tiny_named_workload_full_parity():
     check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, w.name)
 
 
-def _unit_key_counts(w):
-    """Attended keys per work unit from the metadata (numpy; set semantics
-    per row: in-range entries below the clamped count, each block once)."""
-    NK, blk = w.NK, w.block
-    vbs = np.full(NK, blk) if w.vbs is None else np.clip(w.vbs.numpy(), 0, blk)
-    units = np.arange(w.n_units)
-    qb, h, b = units % w.NQ, (units // w.NQ) % w.H, units // (w.NQ * w.H)
-    if w.form == "lut":
-        sb, sh = w.meta_strides
-        rows = b * sb + h * sh + qb
-        idx = w.q2k_idx.numpy()[rows]
-        n = np.clip(w.q2k_num.numpy()[rows], 0, idx.shape[1])
-        ok = (np.arange(idx.shape[1])[None, :] < n[:, None]) & (idx >= 0) & (idx < NK)
-        sel = np.zeros((w.n_units, NK), dtype=bool)
-        r, c = np.nonzero(ok)
-        sel[r, idx[r, c]] = True
-    else:
-        sb, sh = w.mask_strides
-        sel = w.mask.numpy()[b * sb + h * sh + qb] != 0
-    return sel.astype(np.int64) @ vbs.astype(np.int64)
-
-
-def _sample_units(w, n=1536, seed=0):
-    """n random units plus the 32 heaviest and 32 lightest units and every
-    unit with no attended key."""
-    g = np.random.default_rng(seed)
-    keys = _unit_key_counts(w)
-    order = np.argsort(-keys, kind="stable")
-    units = set([0, w.n_units - 1, w.n_units // 2])
-    units.update(g.choice(w.n_units, size=min(n, w.n_units), replace=False).tolist())
-    units.update(order[:32].tolist())
-    units.update(order[-32:].tolist())
-    units.update(np.nonzero(keys == 0)[0].tolist())
-    return sorted(int(u) for u in units)
-
-
 _FULL_SIZE = {}
 
 
@@ -270,10 +234,10 @@ def _compare_units(w, out, lse, units, label):
     check(o_gpu, l_gpu, o_ref, l_ref, label)
 
 
-# (config, chunk, chunks): the Jenga and fp8 workloads element by element,
-# in chunks of work units; the video and 128-block workloads on samples
-FULL_SIZE = [(1, 0, 1), (4, 0, 4), (4, 1, 4), (4, 2, 4), (4, 3, 4),
-             (2, None, None), (3, None, None)]
+# (config, chunk, chunks): every workload element by element, in chunks of
+# work units (each chunk a few seconds of the oracle on the host's cores)
+FULL_SIZE = ([(1, 0, 1)] + [(4, k, 4) for k in range(4)] +
+             [(2, k, 8) for k in range(8)] + [(3, k, 4) for k in range(4)])
 
 
 @pytest.mark.parametrize("cfg,chunk,chunks", FULL_SIZE,
@@ -281,19 +245,15 @@ FULL_SIZE = [(1, 0, 1), (4, 0, 4), (4, 1, 4), (4, 2, 4), (4, 3, 4),
                               for c, k, n in FULL_SIZE])
 def test_named_workload_parity(cfg, chunk, chunks):
     """Full-size named workloads, launched exactly as the benchmark launches
-    them.  The Jenga (1 024 units) and fp8 (6 144 units) workloads are
-    compared with the oracle on every element; the video (18 432 units) and
-    128-block (10 240 units) workloads on about 1 600 units each: a random
-    sample, the 32 heaviest and 32 lightest units and every empty unit."""
+    them, compared with the oracle on every element: Jenga (1 024 units),
+    fp8 (6 144), video (18 432, in eight chunks) and block 128 (10 240, in
+    four), the heaviest, the lightest and the empty units among them."""
     w, out, lse = _full_size_gpu(cfg)
-    if chunk is None:
-        units = _sample_units(w, seed=cfg)
-        log(f"  oracle on {len(units)} sampled units")
-    else:
-        per = (w.n_units + chunks - 1) // chunks
-        units = list(range(chunk * per, min(w.n_units, (chunk + 1) * per)))
-        log(f"  oracle on units {units[0]}..{units[-1]} of {w.n_units}")
+    per = (w.n_units + chunks - 1) // chunks
+    units = list(range(chunk * per, min(w.n_units, (chunk + 1) * per)))
+    log(f"  oracle on units {units[0]}..{units[-1]} of {w.n_units}")
     _compare_units(w, out, lse, units, f"{w.name}[{len(units)} units]")
+
 
 
 def test_need_lse_false_gives_same_output_and_leaves_lse_alone():
