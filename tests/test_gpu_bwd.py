@@ -153,3 +153,49 @@ def test_backward_is_deterministic():
     b = gpu_bwd(w, dout)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_backward_full_size_jenga():
+    """The Jenga workload at full size (1 024 units, the bitmap form), every
+    gradient element against the oracle."""
+    w = workloads.make_config(1)
+    log(f"[bwd] {w.name}: {w.n_units} units")
+    dout = dout_of(w, 401)
+    check_grads(gpu_bwd(w, dout), oracle_bwd(w, dout), w.name)
+
+
+def _query_slice(w, h, qb0, qb1):
+    """Query blocks [qb0, qb1) of head h of a one-batch LUT workload as a
+    workload of its own (the whole key sequence of K/V head h kept): the dq
+    rows of those blocks depend on nothing else, so they equal the full
+    launch's (dk and dv do not: other query blocks add to them)."""
+    sb, sh = w.meta_strides
+    rows = h * sh + torch.arange(qb0, qb1)
+    r0, r1 = qb0 * w.block, qb1 * w.block
+    n = qb1 - qb0
+    return workloads.Workload(
+        name=f"{w.name}[head {h}, q-blocks {qb0}..{qb1 - 1}]", B=1, H=1,
+        S=r1 - r0, D=w.D, block=w.block, form="lut",
+        q=w.q[:, h:h + 1, r0:r1].contiguous(), k=w.k[:, h:h + 1].contiguous(),
+        v=w.v[:, h:h + 1].contiguous(), q2k_idx=w.q2k_idx[rows].contiguous(),
+        q2k_num=w.q2k_num[rows].contiguous(), meta_strides=(n, n),
+        vbs=w.vbs, sm_scale=w.sm_scale)
+
+
+def test_backward_full_size_video_dq():
+    """The video workload at full size (18 432 units, the benchmark's launch
+    with its dq and dk/dv launch orders): dq of the first 32 query blocks of
+    the first head and of the last 32 of the last head, every element,
+    against the oracle run on those query blocks alone (the oracle's
+    backward runs one K/V head per thread, so a whole video head would take
+    minutes; dk and dv are checked at full size on Jenga above)."""
+    w = workloads.make_config(2)
+    assert w.B == 1 and w.Hk == w.H and w.form == "lut"
+    log(f"[bwd] {w.name}: {w.n_units} units")
+    dout = dout_of(w, 402)
+    dq = gpu_bwd(w, dout)[0]
+    for h, qb0, qb1 in ((0, 0, 32), (w.H - 1, w.NQ - 32, w.NQ)):
+        ws = _query_slice(w, h, qb0, qb1)
+        r0, r1 = qb0 * w.block, qb1 * w.block
+        ref = oracle_bwd(ws, dout[:, h:h + 1, r0:r1].contiguous())[0]
+        check_grads([dq[:, h:h + 1, r0:r1]], [ref], ws.name)
